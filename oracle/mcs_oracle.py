@@ -1,0 +1,221 @@
+"""CPU oracle for Meta-Cached Sparse Attention (MC-Sparse).
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package smoke check and
+the CPU-baseline leg of the benchmark may import or run this module.  The GPU
+library never calls it and shares no code with it.
+
+It is a plain, slow, obviously-correct statement of what the method computes,
+in float64 with numpy, one (head, query-group) unit at a time.  Sources (page
+titles as given by the pages):
+
+* [ABS]  "MC-Sparse: Deconstructing and Closing the Dense-Sparse Attention Gap
+  in Diffusion Transformers", arXiv abstract: individual KV tokens are chosen
+  with exact attention probabilities; similar queries are organised into
+  tile-aligned groups; the cached metadata is the query groups, the KV
+  indices and the residual between dense and sparse outputs, reused on later
+  denoising steps.
+* [BLOG] "The quality cliff nobody admits to", section "MC-Sparse: three
+  failure modes, one fix" (same three cached items, computed once and reused)
+  and section "What Trips People Up" (renormalising over the kept tokens moves
+  probability mass; the residual is the correction).
+* [NARROW] "MC-Sparse Narrows the Dense-Sparse Attention Gap in Diffusion
+  Transformers", the list of three design choices (individual KV selection,
+  hardware-aware query organisation, metadata and residual reuse).
+
+The pages give no formula, so the readings taken where they are silent are:
+
+* grouping: an 8-bit sign hash of the queries against 8 random projections,
+  a stable sort of the tokens by that key, then consecutive runs of G sorted
+  tokens form the groups (the last group may be short);
+* a group's score for key j is the sum over the group's queries of the exact
+  softmax probability P_ij (the probability mass the group keeps on j);
+* top-k by that score, ties to the lower key index, indices stored ascending;
+  the comparison is made on the scores rounded to float32, the precision in
+  which the GPU kernel decides;
+* sparse attention is softmax attention restricted to the kept keys
+  (renormalised over them); the residual O_dense - O_sparse is kept per query
+  (in sorted order) and added back unchanged on every reuse step.
+
+Parity pins for every function live in tests/test_oracle_pins.py.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+HASH_BITS = 8
+
+
+# ---------------------------------------------------------------------------
+# Query grouping ([ABS]: "organizing similar queries into tile-aligned groups";
+# [NARROW]: "Hardware-aware query organization").
+# ---------------------------------------------------------------------------
+
+def hash_keys(q: np.ndarray, proj: np.ndarray) -> np.ndarray:
+    """8-bit sign hash of every query row.
+
+    key_i = sum_b [q_i . r_b > 0] * 2^b.  The dot product is accumulated in
+    float64 in the order c = 0..d-1; every product of a float32 (or bf16)
+    value with a float32 projection is exact in float64, so the sum is one
+    well-defined float64 value per (i, b).  A dot product of exactly zero
+    gives bit 0.
+    """
+    q64 = np.asarray(q, dtype=np.float64)
+    r64 = np.asarray(proj, dtype=np.float64)
+    n, d = q64.shape
+    nb = r64.shape[0]
+    acc = np.zeros((n, nb), dtype=np.float64)
+    for c in range(d):
+        acc = acc + q64[:, c:c + 1] * r64[None, :, c]
+    keys = np.zeros(n, dtype=np.int64)
+    for b in range(nb):
+        keys |= (acc[:, b] > 0.0).astype(np.int64) << b
+    return keys.astype(np.uint8)
+
+
+def group_permutation(keys: np.ndarray) -> np.ndarray:
+    """perm[p] = original token at sorted position p (stable sort by key)."""
+    return np.argsort(np.asarray(keys, dtype=np.int64), kind="stable").astype(np.int32)
+
+
+def group_ranges(n: int, group: int):
+    """Sorted-position ranges [start, end) of the ceil(n/group) query groups."""
+    return [(s, min(n, s + group)) for s in range(0, n, group)]
+
+
+# ---------------------------------------------------------------------------
+# Exact attention ([ABS]: "exact attention probabilities").
+# ---------------------------------------------------------------------------
+
+def softmax_rows(s: np.ndarray):
+    """Row softmax of float64 logits: returns (P, row max m, row sum l)."""
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return e / l, m[:, 0], l[:, 0]
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
+    """Softmax attention of rows q over keys k / values v (all float64).
+
+    Returns (O, P) with S = scale * q k^T, P = row softmax of S, O = P v.
+    """
+    q64 = np.asarray(q, dtype=np.float64)
+    k64 = np.asarray(k, dtype=np.float64)
+    v64 = np.asarray(v, dtype=np.float64)
+    s = scale * (q64 @ k64.T)
+    p, _, _ = softmax_rows(s)
+    return p @ v64, p
+
+
+def dense_attention(q, k, v, scale):
+    """Dense output O[N, d] of one head (float64)."""
+    o, _ = attention(q, k, v, scale)
+    return o
+
+
+# ---------------------------------------------------------------------------
+# Selection ([ABS] / [NARROW]: "individual KV selection" from exact
+# probabilities; [BLOG]: "selects individual KV tokens using exact attention
+# probabilities").
+# ---------------------------------------------------------------------------
+
+def group_scores(p_rows: np.ndarray) -> np.ndarray:
+    """c(j) = sum over the group's query rows i of P_ij (float64 [N])."""
+    return np.asarray(p_rows, dtype=np.float64).sum(axis=0)
+
+
+def topk_select(c: np.ndarray, k: int):
+    """Top-k keys of a group's scores.
+
+    The scores are compared as float32 values; order is score descending,
+    then key index ascending.  Returns (idx ascending int32 [k], gap) where
+    gap = c_(k) - c_(k+1) in the float32 scores (inf when k == N).
+    """
+    c32 = np.asarray(c, dtype=np.float64).astype(np.float32).astype(np.float64)
+    n = c32.shape[0]
+    if not 1 <= k <= n:
+        raise ValueError(f"keep {k} outside [1, {n}]")
+    order = np.lexsort((np.arange(n), -c32))
+    idx = np.sort(order[:k]).astype(np.int32)
+    gap = math.inf if k == n else float(c32[order[k - 1]] - c32[order[k]])
+    return idx, gap
+
+
+def sparse_attention(q, k, v, idx, scale):
+    """Attention of rows q over the kept keys idx only (renormalised)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    o, _ = attention(q, np.asarray(k)[idx], np.asarray(v)[idx], scale)
+    return o
+
+
+@dataclass
+class GroupSelection:
+    rows: np.ndarray        # original token ids of the group's queries (sorted order)
+    scores: np.ndarray      # c(j), float64 [N]
+    idx: np.ndarray         # kept keys, ascending int32 [k]
+    gap: float              # float32-score gap between the k-th and (k+1)-th key
+    o_dense: np.ndarray     # float64 [|g|, d]
+    o_sparse: np.ndarray    # float64 [|g|, d]
+    residual: np.ndarray    # o_dense - o_sparse, float64 [|g|, d]
+
+
+def select_group(q, k, v, rows, keep, scale) -> GroupSelection:
+    """Selection step for one query group ([ABS], [BLOG] "MC-Sparse: three
+    failure modes, one fix"): exact dense rows, group scores, top-k, sparse
+    rows over the kept keys and the residual between the two."""
+    rows = np.asarray(rows, dtype=np.int64)
+    qg = np.asarray(q)[rows]
+    o_d, p = attention(qg, k, v, scale)
+    c = group_scores(p)
+    idx, gap = topk_select(c, keep)
+    o_s = sparse_attention(qg, k, v, idx, scale)
+    return GroupSelection(rows.astype(np.int32), c, idx, gap, o_d, o_s, o_d - o_s)
+
+
+def reuse_group(q_t, k_t, v_t, rows, idx, residual, scale):
+    """Reuse step for one group: sparse attention over the cached keys on the
+    step-t inputs plus the cached residual ([ABS]: metadata "reuses them
+    across subsequent denoising steps"; [BLOG] "What Trips People Up": the
+    residual restores what renormalisation loses)."""
+    qg = np.asarray(q_t)[np.asarray(rows, dtype=np.int64)]
+    return sparse_attention(qg, k_t, v_t, idx, scale) + residual
+
+
+# ---------------------------------------------------------------------------
+# Whole-head drivers (loops over the units above).
+# ---------------------------------------------------------------------------
+
+@dataclass
+class HeadMeta:
+    perm: np.ndarray                 # int32 [N]
+    keys: np.ndarray                 # uint8 [N]
+    groups: list                     # GroupSelection per group
+
+
+def select_head(q, k, v, proj, group, keep, scale, groups=None) -> HeadMeta:
+    """Selection for one head; `groups` restricts the work to a subset of
+    group ids (the permutation always covers the whole head)."""
+    keys = hash_keys(q, proj)
+    perm = group_permutation(keys)
+    ranges = group_ranges(q.shape[0], group)
+    gids = range(len(ranges)) if groups is None else groups
+    sel = {g: select_group(q, k, v, perm[ranges[g][0]:ranges[g][1]], keep, scale) for g in gids}
+    return HeadMeta(perm, keys, sel)
+
+
+def reuse_head(q_t, k_t, v_t, meta: HeadMeta, scale, residuals=None, idxs=None):
+    """Reuse output in original token order for the selected groups of one
+    head (rows of groups not in meta stay NaN).  `residuals`/`idxs` override
+    the cached residual / kept keys per group (to evaluate another side's
+    metadata)."""
+    n, d = q_t.shape
+    out = np.full((n, np.asarray(v_t).shape[1]), np.nan)
+    for g, s in meta.groups.items():
+        r = s.residual if residuals is None else residuals[g]
+        ix = s.idx if idxs is None else idxs[g]
+        out[s.rows] = reuse_group(q_t, k_t, v_t, s.rows, ix, r, scale)
+    return out

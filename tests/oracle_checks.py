@@ -1,0 +1,262 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each check takes an object exposing the oracle's functions, so the same
+checks run against the real oracle (tests/test_oracle_pins.py) and against
+deliberately broken copies of it (tests/test_oracle_mutants.py), which must
+fail at least one of them.
+
+What the checks compare against:
+* hand-derived values in tests/golden/*.json (each with its derivation);
+* exact rational arithmetic (fractions.Fraction) for the hash signs;
+* torch.nn.functional.scaled_dot_product_attention in float64 on the CPU
+  (a library routine) for dense and masked (sparse) attention;
+* brute-force enumeration of every k-subset of keys on tiny inputs for the
+  top-k selection (the kept set must maximise the group's retained
+  probability mass, computed from torch.softmax, not from the oracle);
+* invariants the method fixes: keeping every key reproduces dense attention
+  and a zero residual; reuse on unchanged inputs reproduces dense; a group of
+  one query is per-query top-k attention.
+"""
+
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    """Library attention in float64 on the CPU; mask: bool [n_q, n_k] (True = keep)."""
+    qt = torch.tensor(np.asarray(q, dtype=np.float64))[None, None]
+    kt = torch.tensor(np.asarray(k, dtype=np.float64))[None, None]
+    vt = torch.tensor(np.asarray(v, dtype=np.float64))[None, None]
+    am = None if mask is None else torch.tensor(mask)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=am, scale=scale)
+    return o[0, 0].numpy()
+
+
+def _lib_probs(q, k, scale):
+    s = torch.tensor(np.asarray(q, np.float64)) @ torch.tensor(np.asarray(k, np.float64)).T
+    return torch.softmax(scale * s, dim=-1).numpy()
+
+
+# --------------------------------------------------------------------- hash
+
+def check_hash_golden(impl):
+    g = load_golden("hash_small.json")
+    keys = impl.hash_keys(np.array(g["q"], np.float32), np.array(g["proj"], np.float32))
+    assert keys.tolist() == g["keys"], (keys.tolist(), g["keys"])
+    perm = impl.group_permutation(keys)
+    assert perm.tolist() == g["perm"], (perm.tolist(), g["perm"])
+
+
+def check_hash_exact_rational(impl, seed=3, n=40, d=16):
+    """Every hash bit equals the sign of the exact rational dot product."""
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((n, d)).astype(np.float32)
+    proj = r.standard_normal((8, d)).astype(np.float32)
+    keys = impl.hash_keys(q, proj)
+    for i in range(n):
+        want = 0
+        for b in range(8):
+            exact = sum(Fraction(float(q[i, c])) * Fraction(float(proj[b, c])) for c in range(d))
+            want |= int(exact > 0) << b
+        assert int(keys[i]) == want, (i, int(keys[i]), want)
+
+
+def check_perm_stable_sort(impl, seed=4, n=500):
+    """perm is a bijection, keys are non-decreasing along it and equal keys
+    keep ascending token order: together these fix a stable sort."""
+    r = np.random.default_rng(seed)
+    keys = r.integers(0, 7, size=n).astype(np.uint8)
+    perm = impl.group_permutation(keys)
+    assert sorted(perm.tolist()) == list(range(n))
+    ks = keys[perm].astype(int)
+    assert np.all(np.diff(ks) >= 0)
+    same = np.diff(ks) == 0
+    assert np.all(np.diff(perm.astype(int))[same] > 0)
+
+
+# -------------------------------------------------------------- attention
+
+def check_dense_vs_sdpa(impl, seed=5):
+    r = np.random.default_rng(seed)
+    for (n, m, d) in [(7, 11, 4), (33, 64, 16), (5, 130, 8)]:
+        q = r.standard_normal((n, d)) * 2
+        k = r.standard_normal((m, d)) * 2
+        v = r.standard_normal((m, d))
+        scale = 1.0 / math.sqrt(d)
+        o, p = impl.attention(q, k, v, scale)
+        ref = _sdpa(q, k, v, scale)
+        assert np.max(np.abs(o - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref))), np.max(np.abs(o - ref))
+        assert np.allclose(p.sum(axis=1), 1.0, atol=1e-13)
+        assert np.allclose(p, _lib_probs(q, k, scale), atol=1e-14)
+
+
+def check_two_token_golden(impl):
+    g = load_golden("two_token.json")
+    o, p = impl.attention(np.array(g["q"]), np.array(g["k"]), np.array(g["v"]), g["scale"])
+    assert np.allclose(p[0], g["p"], atol=1e-14)
+    assert abs(o[0, 0] - g["o_dense"]) < 1e-13
+    sel = impl.select_group(np.array(g["q"]), np.array(g["k"]), np.array(g["v"]), [0], 1, g["scale"])
+    assert sel.idx.tolist() == g["idx_k1"]
+    assert abs(sel.o_sparse[0, 0] - g["o_sparse_k1"]) < 1e-13
+    assert abs(sel.residual[0, 0] - g["residual_k1"]) < 1e-13
+    sel2 = impl.select_group(np.array(g["q"]), np.array(g["k"]), np.array(g["v"]), [0], 2, g["scale"])
+    assert np.all(sel2.residual == 0.0)
+
+
+def check_closed_forms(impl, seed=6):
+    r = np.random.default_rng(seed)
+    n, d = 9, 8
+    v = r.standard_normal((n, d))
+    # all keys equal -> uniform weights -> mean of V, whatever q is
+    k = np.tile(r.standard_normal((1, d)), (n, 1))
+    q = r.standard_normal((3, d)) * 5
+    o, _ = impl.attention(q, k, v, 0.3)
+    assert np.allclose(o, v.mean(axis=0)[None, :], atol=1e-13)
+    # one key far ahead of the others -> output is its value row
+    k2 = r.standard_normal((n, d))
+    k2[4] = 0.0
+    q2 = np.zeros((1, d))
+    q2[0, 0] = 1.0
+    k2[4, 0] = 1e4
+    o2, _ = impl.attention(q2, k2, v, 1.0)
+    assert np.allclose(o2[0], v[4], atol=1e-12)
+
+
+# -------------------------------------------------------------- selection
+
+def check_uniform_golden(impl):
+    g = load_golden("uniform_attention.json")
+    q, k, v = (np.array(g[x], np.float64) for x in ("q", "k", "v"))
+    for rows in ([0, 1, 2], [3, 4, 5]):
+        sel = impl.select_group(q, k, v, rows, g["keep"], g["scale"])
+        assert np.allclose(sel.scores, g["scores"], atol=1e-14)
+        assert sel.idx.tolist() == g["idx"]
+        assert np.allclose(sel.o_dense, g["o_dense"], atol=1e-13)
+        assert np.allclose(sel.o_sparse, g["o_sparse"], atol=1e-13)
+        assert np.allclose(sel.residual, g["residual"], atol=1e-13)
+        re = impl.reuse_group(q, k, v, rows, sel.idx, sel.residual, g["scale"])
+        assert np.allclose(re, g["o_dense"], atol=1e-13)
+
+
+def check_scores_mass(impl, seed=7):
+    """Each query's probabilities sum to one, so a group's scores sum to |g|;
+    a group of one query scores keys by its own probability row."""
+    r = np.random.default_rng(seed)
+    n, d = 50, 8
+    q, k, v = r.standard_normal((n, d)), r.standard_normal((n, d)), r.standard_normal((n, d))
+    for rows in ([0], [3, 9, 11], list(range(20, 37))):
+        sel = impl.select_group(q, k, v, rows, 5, 0.7)
+        assert abs(sel.scores.sum() - len(rows)) < 1e-12
+        lib = _lib_probs(q[rows], k, 0.7).sum(axis=0)
+        assert np.allclose(sel.scores, lib, atol=1e-13)
+
+
+def check_topk_bruteforce(impl, seed=8):
+    """The kept set maximises the group's retained probability mass over all
+    k-subsets (enumerated), the mass being computed from library softmax."""
+    r = np.random.default_rng(seed)
+    for trial in range(12):
+        n = int(r.integers(4, 11))
+        d = 3
+        gsize = int(r.integers(1, 5))
+        k = int(r.integers(1, min(5, n) + 1))
+        q = r.standard_normal((gsize, d)) * 1.5
+        kk = r.standard_normal((n, d)) * 1.5
+        v = r.standard_normal((n, d))
+        p = _lib_probs(q, kk, 1.0)
+        best, best_set = -1.0, None
+        for sub in itertools.combinations(range(n), k):
+            mass = sum(p[i, j] for i in range(gsize) for j in sub)
+            if mass > best + 1e-12:
+                best, best_set = mass, sub
+        sel = impl.select_group(q, kk, v, list(range(gsize)), k, 1.0)
+        got = sum(p[i, j] for i in range(gsize) for j in sel.idx)
+        assert abs(got - best) < 1e-9, (trial, got, best, sel.idx, best_set)
+        assert list(sel.idx) == sorted(sel.idx) and len(set(sel.idx.tolist())) == k
+
+
+def check_topk_ties_lower_index(impl):
+    c = np.array([0.2, 0.5, 0.2, 0.5, 0.1, 0.2])
+    idx, gap = impl.topk_select(c, 3)
+    assert idx.tolist() == [0, 1, 3] and gap == 0.0
+    idx, gap = impl.topk_select(c, 4)
+    assert idx.tolist() == [0, 1, 2, 3] and gap == 0.0
+    idx, gap = impl.topk_select(c, 5)
+    assert idx.tolist() == [0, 1, 2, 3, 5]
+    assert abs(gap - (np.float32(0.2) - np.float32(0.1))) < 1e-9
+    idx, gap = impl.topk_select(c, 6)
+    assert idx.tolist() == list(range(6)) and gap == math.inf
+
+
+def check_single_query_topk(impl, seed=9):
+    """G = 1 reduces to per-query top-k attention (torch.topk on the row)."""
+    r = np.random.default_rng(seed)
+    n, d, k = 40, 8, 6
+    q, kk, v = r.standard_normal((1, d)) * 2, r.standard_normal((n, d)) * 2, r.standard_normal((n, d))
+    p = _lib_probs(q, kk, 0.5)[0]
+    top = torch.topk(torch.tensor(p), k).indices.sort().values.numpy()
+    sel = impl.select_group(q, kk, v, [0], k, 0.5)
+    assert sel.idx.tolist() == top.tolist()
+
+
+# ----------------------------------------------------- sparse and residual
+
+def check_sparse_vs_masked_sdpa(impl, seed=10):
+    r = np.random.default_rng(seed)
+    n, d = 30, 8
+    q, kk, v = r.standard_normal((5, d)), r.standard_normal((n, d)), r.standard_normal((n, d))
+    idx = np.sort(r.choice(n, size=7, replace=False))
+    mask = np.zeros((5, n), dtype=bool)
+    mask[:, idx] = True
+    o = impl.sparse_attention(q, kk, v, idx, 0.4)
+    assert np.allclose(o, _sdpa(q, kk, v, 0.4, mask), atol=1e-13)
+
+
+def check_keep_one_and_all(impl, seed=11):
+    r = np.random.default_rng(seed)
+    n, d = 25, 4
+    q, kk, v = r.standard_normal((n, d)), r.standard_normal((n, d)), r.standard_normal((n, d))
+    rows = [2, 5, 7, 11]
+    one = impl.select_group(q, kk, v, rows, 1, 0.5)
+    j = int(np.argmax(_lib_probs(q[rows], kk, 0.5).sum(axis=0)))
+    assert one.idx.tolist() == [j]
+    assert np.allclose(one.o_sparse, np.tile(v[j], (len(rows), 1)), atol=1e-14)
+    full = impl.select_group(q, kk, v, rows, n, 0.5)
+    assert full.idx.tolist() == list(range(n))
+    assert np.all(full.residual == 0.0)
+    assert np.allclose(full.o_dense, _sdpa(q[rows], kk, v, 0.5), atol=1e-13)
+
+
+def check_reuse_identity(impl, seed=12):
+    """Reuse on the selection step's own inputs reproduces dense attention."""
+    r = np.random.default_rng(seed)
+    n, d = 64, 8
+    q, kk, v = r.standard_normal((n, d)) * 2, r.standard_normal((n, d)) * 2, r.standard_normal((n, d))
+    rows = list(range(0, 64, 3))
+    sel = impl.select_group(q, kk, v, rows, 9, 0.35)
+    re = impl.reuse_group(q, kk, v, rows, sel.idx, sel.residual, 0.35)
+    assert np.max(np.abs(re - _sdpa(q[rows], kk, v, 0.35))) < 1e-12
+
+
+ALL_CHECKS = [
+    check_hash_golden, check_hash_exact_rational, check_perm_stable_sort,
+    check_dense_vs_sdpa, check_two_token_golden, check_closed_forms,
+    check_uniform_golden, check_scores_mass, check_topk_bruteforce,
+    check_topk_ties_lower_index, check_single_query_topk,
+    check_sparse_vs_masked_sdpa, check_keep_one_and_all, check_reuse_identity,
+]

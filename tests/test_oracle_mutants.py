@@ -1,0 +1,100 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the
+pins catch every one of them."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.mcs_oracle as orc
+from oracle_checks import ALL_CHECKS
+
+
+def _hash_ge(q, proj):
+    acc = np.asarray(q, np.float64) @ np.asarray(proj, np.float64).T
+    return sum(((acc[:, b] >= 0).astype(np.int64) << b) for b in range(acc.shape[1])).astype(np.uint8)
+
+
+def _hash_msb_first(q, proj):
+    acc = np.asarray(q, np.float64) @ np.asarray(proj, np.float64).T
+    nb = acc.shape[1]
+    return sum(((acc[:, b] > 0).astype(np.int64) << (nb - 1 - b)) for b in range(nb)).astype(np.uint8)
+
+
+def _perm_unstable(keys):
+    n = len(keys)
+    return np.lexsort((-np.arange(n), np.asarray(keys, np.int64))).astype(np.int32)
+
+
+def _attention_noscale(q, k, v, scale):
+    return orc.softmax_rows(np.asarray(q, np.float64) @ np.asarray(k, np.float64).T)[0] @ np.asarray(v, np.float64), \
+        orc.softmax_rows(np.asarray(q, np.float64) @ np.asarray(k, np.float64).T)[0]
+
+
+def _attention_vlogits(q, k, v, scale):
+    p = orc.softmax_rows(scale * (np.asarray(q, np.float64) @ np.asarray(v, np.float64).T))[0]
+    return p @ np.asarray(v, np.float64), p
+
+
+def _scores_max(p_rows):
+    return np.asarray(p_rows, np.float64).max(axis=0)
+
+
+def _topk_ties_high(c, k):
+    c32 = np.asarray(c, np.float64).astype(np.float32).astype(np.float64)
+    n = len(c32)
+    order = np.lexsort((-np.arange(n), -c32))
+    gap = math.inf if k == n else float(c32[order[k - 1]] - c32[order[k]])
+    return np.sort(order[:k]).astype(np.int32), gap
+
+
+def _topk_smallest(c, k):
+    order = np.argsort(np.asarray(c), kind="stable")
+    return np.sort(order[:k]).astype(np.int32), 0.0
+
+
+def _sparse_unnormalised(q, k, v, idx, scale):
+    _, p = orc.attention(q, k, v, scale)
+    idx = np.asarray(idx, np.int64)
+    return p[:, idx] @ np.asarray(v, np.float64)[idx]
+
+
+def _select_residual_flipped(q, k, v, rows, keep, scale):
+    s = orig_select(q, k, v, rows, keep, scale)
+    s.residual = -s.residual
+    return s
+
+
+def _reuse_no_residual(q_t, k_t, v_t, rows, idx, residual, scale):
+    qg = np.asarray(q_t)[np.asarray(rows, np.int64)]
+    return orc.sparse_attention(qg, k_t, v_t, idx, scale)
+
+
+orig_select = orc.select_group
+
+MUTANTS = {
+    "hash >= 0": ("hash_keys", _hash_ge),
+    "hash bit order": ("hash_keys", _hash_msb_first),
+    "unstable sort": ("group_permutation", _perm_unstable),
+    "scale dropped": ("attention", _attention_noscale),
+    "logits against V": ("attention", _attention_vlogits),
+    "group score = max": ("group_scores", _scores_max),
+    "ties to higher index": ("topk_select", _topk_ties_high),
+    "keeps smallest scores": ("topk_select", _topk_smallest),
+    "no renormalisation": ("sparse_attention", _sparse_unnormalised),
+    "residual sign": ("select_group", _select_residual_flipped),
+    "reuse drops residual": ("reuse_group", _reuse_no_residual),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check(orc)
+        except (AssertionError, ValueError, IndexError):
+            failed.append(check.__name__)
+    assert failed, f"mutant '{name}' passed every pin"

@@ -1,0 +1,209 @@
+/*
+ * mcs.h — C ABI of libmcs: Meta-Cached Sparse Attention (MC-Sparse) on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (abstract of "MC-Sparse: Deconstructing and Closing the
+ * Dense-Sparse Attention Gap in Diffusion Transformers"; the section
+ * "MC-Sparse: three failure modes, one fix" of "The quality cliff nobody
+ * admits to"; the three design choices listed in "MC-Sparse Narrows the
+ * Dense-Sparse Attention Gap in Diffusion Transformers") has two stages:
+ *
+ *   selection  exact dense attention; queries are organised into groups of
+ *              similar queries that fill whole GPU tiles; each group keeps the
+ *              individual KV tokens that carry the most exact attention
+ *              probability; the query groups, the kept KV indices and the
+ *              residual between dense and sparse outputs are cached;
+ *   reuse      on later denoising steps, attention of each group over only its
+ *              cached KV tokens, plus the cached residual.
+ *
+ * Readings where the pages give no formula: the grouping key is an 8-bit sign
+ * hash of each query against 8 caller-supplied projections (bit b set iff the
+ * float64 dot product q . r_b, accumulated in dimension order, is > 0); the
+ * tokens are stably sorted by key and cut into groups of G consecutive sorted
+ * tokens (the last group may be shorter); a group scores key j by the sum of
+ * its queries' exact probabilities P_ij; it keeps the k_h best keys (ties to
+ * the lower index, compared as float32), stored in ascending order; the sparse
+ * softmax is renormalised over the kept keys; the residual O_dense - O_sparse
+ * is kept in float32 and added back unchanged on every reuse step.
+ *
+ * Conventions for every call:
+ *  - Tensors Q, K, V, O are [H][N][d] row-major (d contiguous) in the
+ *    descriptor's dtype, in device memory, 16-byte aligned.  Batch is folded
+ *    into H.
+ *  - All calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Results are valid once the stream reaches the call.  No call
+ *    synchronises the device.
+ *  - The caller owns every device buffer.  The library allocates no device
+ *    memory and keeps no global state apart from a per-thread last HIP error.
+ *  - Every argument is validated before anything is launched; a call that
+ *    returns an error status has not written any output.
+ *  - H == 0 or N == 0 is a valid empty problem: the call validates, fills any
+ *    host-side output struct and returns MCS_SUCCESS without launching.
+ *  - The functions are re-entrant; calls that share output buffers on
+ *    different streams race.
+ */
+#ifndef MCS_H_
+#define MCS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MCS_VERSION 1
+#define MCS_META_VERSION 1
+#define MCS_HASH_BITS 8
+#define MCS_MAX_SEQ_LEN (1 << 24)
+
+typedef enum mcs_status {
+  MCS_SUCCESS = 0,
+  MCS_ERROR_INVALID_VALUE = 1,    /* null pointer, negative size, keep outside [1, N] */
+  MCS_ERROR_UNSUPPORTED_SHAPE = 2,/* head_dim not 64/128, group not 64/128, dtype unknown, N too large */
+  MCS_ERROR_MISALIGNED = 3,       /* a device pointer is not 16-byte (tensors) / 256-byte (meta, workspace) aligned */
+  MCS_ERROR_BUFFER_TOO_SMALL = 4, /* meta buffer or workspace smaller than required */
+  MCS_ERROR_META_MISMATCH = 5,    /* metadata built for another shape, dtype or layout version */
+  MCS_ERROR_HIP = 6               /* a HIP runtime call or launch failed; see mcs_last_hip_error() */
+} mcs_status;
+
+typedef enum mcs_dtype {
+  MCS_DTYPE_FP32 = 0,  /* float32 in and out; float32 arithmetic */
+  MCS_DTYPE_BF16 = 1   /* bfloat16 in and out; bf16 matrix products with float32 accumulation */
+} mcs_dtype;
+
+/* Shape of one attention layer. */
+typedef struct mcs_attn_desc {
+  int32_t num_heads;     /* H >= 0 */
+  int32_t seq_len;       /* N, 0 <= N <= MCS_MAX_SEQ_LEN */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t dtype;         /* mcs_dtype */
+  float softmax_scale;   /* logits are scale * q.k; a value <= 0 selects 1/sqrt(d) */
+} mcs_attn_desc;
+
+/*
+ * Cached metadata of one selection step: a value struct describing regions of
+ * a caller-owned device buffer (`base`).  The layout is public so that it can
+ * be saved, restored or filled by other code.  All offsets are in bytes from
+ * `base` and 256-byte aligned.
+ *
+ *   perm      int32 [H][N]     perm[h][p] = original token at sorted position p;
+ *                              group g of head h is positions [g*G, min(N,(g+1)*G))
+ *   keep      int32 [H]        k_h, kept keys per group of head h, 1 <= k_h <= N
+ *   idx_start int64 [H]        element offset of head h's indices in `idx`
+ *   sched     int32 [H]        heads by decreasing k_h (ties: lower head first);
+ *                              reuse launches the costliest heads first
+ *   idx       int32 [total_idx] head h, group g: k_h kept key indices, ascending,
+ *                              at idx[idx_start[h] + g*k_h ...]
+ *   residual  float32 [H][N][d] O_dense - O_sparse of the selection step, row p
+ *                              = sorted position p (not the original token)
+ */
+typedef struct mcs_meta {
+  int32_t version;         /* MCS_META_VERSION */
+  int32_t num_heads;
+  int32_t seq_len;
+  int32_t head_dim;
+  int32_t dtype;
+  int32_t group_size;      /* G */
+  int32_t num_groups;      /* ceil(N / G) */
+  int32_t max_keep;        /* max_h k_h */
+  int64_t total_idx;       /* sum_h num_groups * k_h */
+  void* base;              /* device pointer to the metadata buffer (NULL from mcs_meta_layout) */
+  uint64_t bytes;          /* bytes the layout occupies from base */
+  uint64_t off_perm;
+  uint64_t off_keep;
+  uint64_t off_idx_start;
+  uint64_t off_sched;
+  uint64_t off_idx;
+  uint64_t off_residual;
+} mcs_meta;
+
+/* Library version (MCS_VERSION). */
+int mcs_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* mcs_status_string(mcs_status status);
+
+/* The hipError_t of the last MCS_ERROR_HIP returned on this thread (0 if none). */
+int mcs_last_hip_error(void);
+
+/*
+ * Exact dense attention, the method's selection-time computation and the
+ * speed baseline every sparse speedup is measured against ("Relative to dense
+ * attention", abstract of "MC-Sparse: Deconstructing and Closing the
+ * Dense-Sparse Attention Gap in Diffusion Transformers").
+ *   o[h][i] = sum_j softmax_j(scale * q[h][i] . k[h][j]) v[h][j]
+ * q, k, v: [H][N][d] inputs; o: [H][N][d] output (must not alias the inputs).
+ */
+mcs_status mcs_dense_attn(const mcs_attn_desc* desc, const void* q, const void* k, const void* v,
+                          void* o, void* stream);
+
+/*
+ * Host-only: computes the metadata layout for group size G and per-head keep
+ * budgets keep_host[H] (read during the call).  Fills *layout with base = NULL.
+ */
+mcs_status mcs_meta_layout(const mcs_attn_desc* desc, int32_t group_size, const int32_t* keep_host,
+                           mcs_meta* layout);
+
+/* Bytes of metadata buffer that mcs_select needs (0 if the arguments are invalid). */
+size_t mcs_meta_bytes(const mcs_attn_desc* desc, int32_t group_size, const int32_t* keep_host);
+
+/*
+ * Bytes of workspace mcs_select needs to process `heads_per_chunk` heads at a
+ * time (clamped to [1, H]; 0 if the arguments are invalid).  The bulk is the
+ * per-group key scores, float32 [heads_per_chunk][ceil(N/G)][N rounded up to 64].
+ */
+size_t mcs_select_workspace_bytes(const mcs_attn_desc* desc, int32_t group_size, int32_t heads_per_chunk);
+
+/*
+ * Lays out metadata in meta_buf (device, 256-byte aligned, meta_bytes long)
+ * and writes its keep, idx_start and sched regions; perm, idx and residual
+ * are left for the caller to fill (to restore saved metadata or to supply
+ * metadata built elsewhere).  *meta_out receives the descriptor.
+ */
+mcs_status mcs_meta_init(const mcs_attn_desc* desc, int32_t group_size, const int32_t* keep_host,
+                         void* meta_buf, size_t meta_bytes, mcs_meta* meta_out, void* stream);
+
+/*
+ * Selection step ("selects individual key-value (KV) tokens while organizing
+ * similar queries into tile-aligned groups ... caches metadata comprising query
+ * groups, KV indices selected using exact attention probabilities, and
+ * residuals between dense and sparse attention outputs", abstract of
+ * "MC-Sparse: Deconstructing and Closing the Dense-Sparse Attention Gap in
+ * Diffusion Transformers").
+ *   q, k, v        [H][N][d] step inputs (device)
+ *   group_size     G, 64 or 128 (query rows per group = one GPU tile)
+ *   keep_host      int32 [H] host array, k_h in [1, N], read during the call
+ *   hash_proj_host float32 [MCS_HASH_BITS][d] host array of projection
+ *                  directions, read during the call
+ *   meta_buf       device buffer of meta_bytes >= mcs_meta_bytes(...), 256-aligned
+ *   workspace      device buffer of ws_bytes >= mcs_select_workspace_bytes(desc, G, 1),
+ *                  256-aligned; more space lets more heads run per chunk
+ *   o_dense_out    optional [H][N][d] output (NULL to skip): the exact dense
+ *                  output of this step in the original token order
+ *   meta_out       host struct receiving the metadata descriptor
+ * On success the metadata is complete once the stream reaches the call.
+ */
+mcs_status mcs_select(const mcs_attn_desc* desc, const void* q, const void* k, const void* v,
+                      int32_t group_size, const int32_t* keep_host, const float* hash_proj_host,
+                      void* meta_buf, size_t meta_bytes, void* workspace, size_t ws_bytes,
+                      void* o_dense_out, mcs_meta* meta_out, void* stream);
+
+/*
+ * Reuse step ("reuses them across subsequent denoising steps", same abstract;
+ * the residual restores the attention contribution that renormalising over
+ * the kept tokens loses, section "What Trips People Up" of "The quality cliff
+ * nobody admits to"):
+ *   o[h][perm[p]] = sum_{j in S_g} softmax_{j in S_g}(scale q.k_j) v_j + residual[h][p]
+ * for every sorted position p of group g, S_g = the group's cached keys.
+ * q, k, v: [H][N][d] inputs of this step; meta: from mcs_select or
+ * mcs_meta_init with the same H, N, d and dtype; o: [H][N][d] output.
+ */
+mcs_status mcs_sparse_attn(const mcs_attn_desc* desc, const void* q, const void* k, const void* v,
+                           const mcs_meta* meta, void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MCS_H_ */

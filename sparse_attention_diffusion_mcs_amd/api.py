@@ -1,0 +1,208 @@
+"""Python binding of libmcs: marshals torch tensors (device memory and the
+current HIP stream) into the C ABI.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback path."""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return L.MCS_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return L.MCS_DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check_qkv(q, k, v):
+    for t in (q, k, v):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3:
+            raise ValueError("q, k, v must be [H, N, d] tensors")
+        if not t.is_cuda:
+            raise ValueError("q, k, v must be device tensors")
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+
+
+def desc_for(q: torch.Tensor, scale: float | None = None) -> L.AttnDesc:
+    H, N, d = q.shape
+    return L.AttnDesc(H, N, d, _dtype_code(q), float(scale) if scale else 0.0)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _keep_array(keep, H) -> np.ndarray:
+    arr = np.ascontiguousarray(np.broadcast_to(np.asarray(keep, dtype=np.int32), (H,)), dtype=np.int32)
+    return arr
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class MetaCache:
+    """Cached selection metadata: a device buffer plus its mcs_meta descriptor.
+
+    Region views (all on the device): perm int32 [H, N], keep int32 [H],
+    idx_start int64 [H], sched int32 [H], idx int32 [total_idx] and residual
+    float32 [H, N, d] (rows in group order)."""
+
+    def __init__(self, meta: L.Meta, buffer: torch.Tensor):
+        self.meta = meta
+        self.buffer = buffer
+
+    def _region(self, off, count, dtype, shape):
+        nbytes = count * torch.empty((), dtype=dtype).element_size()
+        return self.buffer[off:off + nbytes].view(dtype).view(*shape)
+
+    @property
+    def num_heads(self):
+        return self.meta.num_heads
+
+    @property
+    def seq_len(self):
+        return self.meta.seq_len
+
+    @property
+    def group_size(self):
+        return self.meta.group_size
+
+    @property
+    def num_groups(self):
+        return self.meta.num_groups
+
+    @property
+    def perm(self):
+        m = self.meta
+        return self._region(m.off_perm, m.num_heads * m.seq_len, torch.int32, (m.num_heads, m.seq_len))
+
+    @property
+    def keep(self):
+        m = self.meta
+        return self._region(m.off_keep, m.num_heads, torch.int32, (m.num_heads,))
+
+    @property
+    def idx_start(self):
+        m = self.meta
+        return self._region(m.off_idx_start, m.num_heads, torch.int64, (m.num_heads,))
+
+    @property
+    def sched(self):
+        m = self.meta
+        return self._region(m.off_sched, m.num_heads, torch.int32, (m.num_heads,))
+
+    @property
+    def idx(self):
+        m = self.meta
+        return self._region(m.off_idx, m.total_idx, torch.int32, (m.total_idx,))
+
+    @property
+    def residual(self):
+        m = self.meta
+        return self._region(m.off_residual, m.num_heads * m.seq_len * m.head_dim, torch.float32,
+                            (m.num_heads, m.seq_len, m.head_dim))
+
+    def head_idx(self, h: int, keep_h: int) -> torch.Tensor:
+        """Kept key indices of head h as [num_groups, keep_h]."""
+        start = int(self.idx_start[h].item())
+        return self.idx[start:start + self.num_groups * keep_h].view(self.num_groups, keep_h)
+
+    @property
+    def nbytes(self) -> int:
+        return int(self.meta.bytes)
+
+
+def dense_attn(q, k, v, out=None, scale=None, stream=None):
+    """Dense attention O = softmax(scale q k^T) v per head (mcs_dense_attn)."""
+    _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    desc = desc_for(q, scale)
+    L.check(L.lib().mcs_dense_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream(stream)),
+            "mcs_dense_attn")
+    return out
+
+
+def meta_layout(H, N, d, dtype_code, group_size, keep) -> L.Meta:
+    desc = L.AttnDesc(H, N, d, dtype_code, 0.0)
+    ka = _keep_array(keep, H)
+    m = L.Meta()
+    L.check(L.lib().mcs_meta_layout(ctypes.byref(desc), group_size, _i32p(ka), ctypes.byref(m)), "mcs_meta_layout")
+    return m
+
+
+def workspace_bytes(q, group_size, heads_per_chunk=None) -> int:
+    desc = desc_for(q)
+    hc = q.shape[0] if heads_per_chunk is None else heads_per_chunk
+    return int(L.lib().mcs_select_workspace_bytes(ctypes.byref(desc), group_size, hc))
+
+
+def meta_init(q, group_size, keep, meta_buf=None, stream=None) -> MetaCache:
+    """Lays out an empty metadata buffer (keep/idx_start/sched written;
+    perm/idx/residual to be filled by the caller) (mcs_meta_init)."""
+    desc = desc_for(q)
+    H = q.shape[0]
+    ka = _keep_array(keep, H)
+    nbytes = int(L.lib().mcs_meta_bytes(ctypes.byref(desc), group_size, _i32p(ka)))
+    if nbytes == 0:
+        raise L.McsError(L.MCS_ERROR_INVALID_VALUE, "mcs_meta_bytes")
+    if meta_buf is None:
+        meta_buf = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    m = L.Meta()
+    L.check(L.lib().mcs_meta_init(ctypes.byref(desc), group_size, _i32p(ka), _ptr(meta_buf), meta_buf.numel(),
+                                  ctypes.byref(m), _stream(stream)), "mcs_meta_init")
+    return MetaCache(m, meta_buf)
+
+
+def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace=None, heads_per_chunk=None,
+           return_dense=False, stream=None):
+    """Selection step (mcs_select).  Returns (MetaCache, dense output or None)."""
+    _check_qkv(q, k, v)
+    H, N, d = q.shape
+    desc = desc_for(q, scale)
+    ka = _keep_array(keep, H)
+    pj = np.ascontiguousarray(np.asarray(proj, dtype=np.float32))
+    if pj.shape != (L.MCS_HASH_BITS, d):
+        raise ValueError(f"proj must be [{L.MCS_HASH_BITS}, {d}]")
+    nbytes = int(L.lib().mcs_meta_bytes(ctypes.byref(desc), group_size, _i32p(ka)))
+    if nbytes == 0 and H * N > 0:
+        raise L.McsError(L.MCS_ERROR_INVALID_VALUE, "mcs_meta_bytes")
+    if meta_buf is None:
+        meta_buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(q, group_size, heads_per_chunk), 256), dtype=torch.uint8,
+                                device=q.device)
+    o_dense = torch.empty_like(q) if return_dense else None
+    m = L.Meta()
+    L.check(L.lib().mcs_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka),
+                               pj.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(meta_buf),
+                               meta_buf.numel(), _ptr(workspace), workspace.numel(), _ptr(o_dense),
+                               ctypes.byref(m), _stream(stream)), "mcs_select")
+    return MetaCache(m, meta_buf), o_dense
+
+
+def sparse_attn(q, k, v, meta: MetaCache, out=None, scale=None, stream=None):
+    """Reuse step (mcs_sparse_attn): attention over each group's cached keys
+    plus the cached residual, output in original token order."""
+    _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    desc = desc_for(q, scale)
+    L.check(L.lib().mcs_sparse_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(meta.meta),
+                                    _ptr(out), _stream(stream)), "mcs_sparse_attn")
+    return out

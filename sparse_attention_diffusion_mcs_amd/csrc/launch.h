@@ -1,0 +1,51 @@
+// Internal host-side launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mcs {
+
+enum AttnMode : int {
+  MODE_PLAIN = 0,    // dense, natural row order, O out
+  MODE_SELECT = 1,   // dense over group-sorted rows: O_dense (float32, sorted rows) + per-group key scores
+  MODE_REUSE = 2,    // sparse over cached keys + residual, O out in original order
+  MODE_RESINIT = 3   // sparse over cached keys at selection: residual -= O_sparse
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;                   // PLAIN/REUSE: output; SELECT: optional dense output (original order)
+  float* residual;           // [H][N][d], sorted-position rows
+  float* colsum;             // SELECT: [nheads][ng][ldc] key scores of the launched heads
+  const int32_t* perm;       // [H][N]
+  const int32_t* keep;       // [H]
+  const int64_t* idx_start;  // [H]
+  const int32_t* sched;      // [H] (REUSE)
+  const int32_t* idx;        // kept keys
+  int H, N, D, G, ng, ldc;
+  long long total_idx;       // entries in idx (sparse modes; bounds every gather)
+  int head0;                 // first head of the launch (PLAIN/SELECT/RESINIT)
+  int nheads;                // heads in the launch
+  float scale;               // softmax scale
+  int run;                   // XCD run length (logical blocks per XCD per round)
+};
+
+// bf16 MFMA kernels (attn_bf16.hip)
+hipError_t launch_attn_bf16(int mode, const AttnArgs& a, hipStream_t s);
+// float32 VALU kernels (attn_f32.hip)
+hipError_t launch_attn_f32(int mode, const AttnArgs& a, hipStream_t s);
+
+// selection helpers (select.hip)
+hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, uint8_t* keys, int H, int N, int D,
+                            hipStream_t s);
+hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hipStream_t s);
+hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, const int32_t* keep,
+                             const int64_t* idx_start, int head0, int nheads, int ng, int N, hipStream_t s);
+// Writes `nbytes` bytes from host memory to device memory through kernel
+// arguments (asynchronous on s, safe for pageable and stack host memory).
+hipError_t launch_fill_bytes(void* dst, const void* src, size_t nbytes, hipStream_t s);
+
+}  // namespace mcs

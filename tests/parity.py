@@ -1,0 +1,126 @@
+"""Shared helpers of the GPU parity tests: build seeded problems from the
+input generator, run the library through its Python binding (which calls the
+C ABI), and compare against the CPU oracle.
+
+Acceptance rules:
+* perm: bit-exact;
+* kept keys per group: same size, distinct, ascending, in range; every key
+  whose oracle score (float32) exceeds the (k+1)-th score by more than 1e-6 is
+  kept; every kept key scores at least the k-th score minus 1e-6 (so the set
+  is bit-exact whenever the oracle's k-th/(k+1)-th gap is 1e-6 or more);
+* outputs: bf16 max-abs <= 2e-2 and relative L2 <= 5e-3; float32 max-abs
+  <= 2e-4 and relative L2 <= 1e-4 (float32 logits of magnitude ~50 carry an
+  absolute error of order sqrt(d) * 2^-24 * 50 ~ 3e-5 at d = 128, which moves
+  every probability by that relative amount); the residual's relative L2 is measured
+  against the dense output's norm.  Residual and reuse outputs are compared
+  with the oracle evaluated on the GPU's own kept keys, so a legitimate
+  near-tie swap cannot mask an arithmetic error.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle.mcs_oracle as orc
+from mcs_inputs import hash_projections, head_base, head_step, position_embedding
+
+GAP = 1e-6
+TOL = {"bf16": (2e-2, 5e-3), "fp32": (2e-4, 1e-4)}
+
+
+def scale_for(d: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+@dataclass
+class Problem:
+    grid: tuple
+    H: int
+    d: int
+    dtype: str
+    G: int
+    keeps: np.ndarray
+    drift: float
+    steps: list                  # reuse steps that were generated (>= 1)
+    seed: int = 0
+    wid: int = 100
+    heads_np: dict = field(default_factory=dict)   # (head, step) -> (q, k, v) float32
+    dev: dict = field(default_factory=dict)        # step -> (q, k, v) device tensors
+
+    @property
+    def N(self):
+        return int(np.prod(self.grid))
+
+    @property
+    def ng(self):
+        return -(-self.N // self.G)
+
+    @property
+    def tdtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def proj(self):
+        return hash_projections(self.seed, self.wid, self.d)
+
+
+def build_problem(grid, H, d, dtype, G, keeps, drift, steps, seed=0, wid=100, keep_heads=None) -> Problem:
+    """Generates step 0 and the listed reuse steps for every head, uploads
+    them, and keeps the float32 host copies of the heads in keep_heads (all
+    heads if None) for the oracle."""
+    p = Problem(tuple(grid), H, d, dtype, G, np.asarray(keeps, np.int32), drift, list(steps), seed, wid)
+    pos = position_embedding(grid, d)
+    bf = dtype == "bf16"
+    all_steps = [0] + p.steps
+    host = {t: [np.empty((H, p.N, d), np.float32) for _ in range(3)] for t in all_steps}
+    for h in range(H):
+        base = head_base(seed, wid, h, grid, d, pos)
+        for t in all_steps:
+            xs = head_step(base, seed, wid, h, t, drift, bf)
+            for i in range(3):
+                host[t][i][h] = xs[i]
+            if keep_heads is None or h in keep_heads:
+                p.heads_np[(h, t)] = xs
+    for t in all_steps:
+        p.dev[t] = tuple(torch.from_numpy(x).to("cuda").to(p.tdtype).contiguous() for x in host[t])
+    return p
+
+
+def rel_l2(x, ref, ref_norm=None):
+    den = np.linalg.norm(ref) if ref_norm is None else ref_norm
+    return float(np.linalg.norm(np.asarray(x, np.float64) - ref) / max(den, 1e-300))
+
+
+def assert_close(x, ref, dtype, what, ref_norm=None):
+    max_abs, rl2 = TOL[dtype]
+    x = np.asarray(x, np.float64)
+    err = float(np.max(np.abs(x - ref))) if x.size else 0.0
+    r = rel_l2(x, ref, ref_norm)
+    assert err <= max_abs and r <= rl2, f"{what}: max-abs {err:.3e} (tol {max_abs}), rel-L2 {r:.3e} (tol {rl2})"
+    return err, r
+
+
+def check_idx(gpu_idx, scores, k, n, what):
+    """Returns True when the GPU set equals the oracle's, asserts the rule."""
+    gi = np.asarray(gpu_idx, np.int64)
+    assert gi.shape == (k,), f"{what}: {gi.shape} != ({k},)"
+    assert np.all(np.diff(gi) > 0), f"{what}: not strictly ascending"
+    assert gi[0] >= 0 and gi[-1] < n, f"{what}: index out of range"
+    c32 = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    srt = np.sort(c32)[::-1]
+    ck = srt[k - 1]
+    ck1 = srt[k] if k < n else -np.inf
+    must = np.nonzero(c32 > ck1 + GAP)[0]
+    missing = np.setdiff1d(must, gi)
+    assert missing.size == 0, f"{what}: clearly-in keys missing {missing[:8]} (scores {c32[missing[:8]]})"
+    low = gi[c32[gi] < ck - GAP]
+    assert low.size == 0, f"{what}: clearly-out keys kept {low[:8]} (scores {c32[low[:8]]}, k-th {ck})"
+    oidx, _ = orc.topk_select(scores, k)
+    return bool(np.array_equal(oidx, gi))
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy()

@@ -1,0 +1,173 @@
+"""GPU parity on small problems that span several tiles and ragged tails:
+every group of every head is compared with the CPU oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.mcs_oracle as orc
+from mcs_inputs import WORKLOADS
+from parity import assert_close, build_problem, check_idx, scale_for, to_np
+
+pytestmark = pytest.mark.gpu
+
+mcs = pytest.importorskip("sparse_attention_diffusion_mcs_amd")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+W1 = WORKLOADS[1]
+CASES = {
+    # name: (grid, H, d, dtype, G, keeps, drift, steps, wid)
+    "w1_fp32_tiny": (W1.grid, 1, 64, "fp32", 64, [128], 0.02, [1, 2, 3], 1),
+    "bf16_d128_g64_ragged": ((5, 8, 25), 2, 128, "bf16", 64, [128, 100], 0.02, [1, 4], 101),
+    "bf16_d64_g128_k1_kN": ((4, 10, 30), 3, 64, "bf16", 128, [64, 1200, 1], 0.02, [2], 102),
+    "bf16_d128_g128_ragged": ((3, 17, 21), 2, 128, "bf16", 128, [333, 1071], 0.01, [1], 103),
+    "bf16_d64_g64_small": ((2, 4, 9), 2, 64, "bf16", 64, [7, 72], 0.02, [1], 104),
+    "fp32_d128_g128": ((4, 4, 20), 2, 128, "fp32", 128, [50, 320], 0.02, [1], 105),
+    "fp32_d64_g64_ragged": ((3, 5, 7), 1, 64, "fp32", 64, [17], 0.02, [1, 2], 106),
+}
+
+
+def run_case(name):
+    grid, H, d, dtype, G, keeps, drift, steps, wid = CASES[name]
+    print(f"[case] {name} grid={grid} H={H} d={d} {dtype} G={G} keeps={keeps}", flush=True)
+    p = build_problem(grid, H, d, dtype, G, keeps, drift, steps, wid=wid)
+    sc = scale_for(d)
+    q0, k0, v0 = p.dev[0]
+    meta, od = mcs.select(q0, k0, v0, G, p.keeps, p.proj(), scale=sc, return_dense=True)
+    outs = {t: mcs.sparse_attn(*p.dev[t], meta, scale=sc) for t in steps}
+    dense_plain = mcs.dense_attn(q0, k0, v0, scale=sc)
+    torch.cuda.synchronize()
+    return p, sc, meta, od, outs, dense_plain
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_select_and_reuse_parity(name):
+    _need_gpu()
+    p, sc, meta, od, outs, dense_plain = run_case(name)
+    perm_g = to_np(meta.perm).astype(np.int64) if meta.perm.dtype != torch.int32 else meta.perm.cpu().numpy()
+    resid_g = to_np(meta.residual)
+    od_g, plain_g = to_np(od), to_np(dense_plain)
+    outs_g = {t: to_np(o) for t, o in outs.items()}
+    exact_sets = 0
+    for h in range(p.H):
+        q, k, v = p.heads_np[(h, 0)]
+        keys = orc.hash_keys(q, p.proj())
+        perm_o = orc.group_permutation(keys)
+        assert np.array_equal(perm_g[h], perm_o), f"head {h}: perm differs"
+        dense_o = orc.dense_attention(q, k, v, sc)
+        assert_close(od_g[h], dense_o, p.dtype, f"head {h} dense output of select")
+        assert_close(plain_g[h], dense_o, p.dtype, f"head {h} dense_attn")
+        kh = int(p.keeps[h])
+        gidx_all = meta.head_idx(h, kh).cpu().numpy()
+        dnorm = np.linalg.norm(dense_o)
+        for g, (s, e) in enumerate(orc.group_ranges(p.N, p.G)):
+            rows = perm_o[s:e]
+            sel = orc.select_group(q, k, v, rows, kh, sc)
+            exact_sets += check_idx(gidx_all[g], sel.scores, kh, p.N, f"head {h} group {g}")
+            res_c = sel.o_dense - orc.sparse_attention(q[rows], k, v, gidx_all[g], sc)
+            assert_close(resid_g[h, s:e], res_c, p.dtype, f"head {h} group {g} residual",
+                         ref_norm=np.linalg.norm(sel.o_dense))
+            for t in p.steps:
+                qt, kt, vt = p.heads_np[(h, t)]
+                ref = orc.reuse_group(qt, kt, vt, rows, gidx_all[g], res_c, sc)
+                assert_close(outs_g[t][h, rows], ref, p.dtype, f"head {h} group {g} reuse step {t}")
+        # whole-head reuse output against the oracle (for the fidelity record)
+        for t in p.steps:
+            assert np.all(np.isfinite(outs_g[t][h]))
+    print(f"[case] exact kept-key sets: {exact_sets} of {p.H * p.ng}", flush=True)
+
+
+def test_reuse_with_oracle_metadata():
+    """The reuse kernel on metadata built entirely by the oracle."""
+    _need_gpu()
+    grid, H, d, G, keeps = (4, 6, 25), 2, 128, 64, [96, 200]
+    p = build_problem(grid, H, d, "bf16", G, keeps, 0.02, [3], wid=107)
+    sc = scale_for(d)
+    q0 = p.dev[0][0]
+    meta = mcs.meta_init(q0, G, p.keeps)
+    perm_all = np.zeros((H, p.N), np.int32)
+    resid_all = np.zeros((H, p.N, d), np.float32)
+    refs = np.zeros((H, p.N, d))
+    idx_flat = []
+    for h in range(H):
+        q, k, v = p.heads_np[(h, 0)]
+        hm = orc.select_head(q, k, v, p.proj(), G, int(p.keeps[h]), sc)
+        perm_all[h] = hm.perm
+        for g, (s, e) in enumerate(orc.group_ranges(p.N, G)):
+            resid_all[h, s:e] = hm.groups[g].residual
+            idx_flat.append(hm.groups[g].idx)
+        refs[h] = orc.reuse_head(*p.heads_np[(h, 3)], hm, sc,
+                                 residuals={g: resid_all[h, s:e].astype(np.float64)
+                                            for g, (s, e) in enumerate(orc.group_ranges(p.N, G))})
+    meta.perm.copy_(torch.from_numpy(perm_all))
+    meta.idx.copy_(torch.from_numpy(np.concatenate(idx_flat).astype(np.int32)))
+    meta.residual.copy_(torch.from_numpy(resid_all))
+    out = to_np(mcs.sparse_attn(*p.dev[3], meta, scale=sc))
+    for h in range(H):
+        assert_close(out[h], refs[h], "bf16", f"head {h} reuse on oracle metadata")
+
+
+@pytest.mark.parametrize("dtype,G", [("bf16", 64), ("bf16", 128), ("fp32", 64)])
+def test_keep_all_gives_zero_residual_and_dense(dtype, G):
+    """Keeping every key makes the sparse pass the dense pass: the residual
+    vanishes and reuse on the selection inputs returns the dense output."""
+    _need_gpu()
+    grid, H, d = (3, 8, 27), 2, 128
+    n = int(np.prod(grid))
+    p = build_problem(grid, H, d, dtype, G, [n, n], 0.0, [1], wid=108)
+    sc = scale_for(d)
+    meta, od = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc, return_dense=True)
+    out = mcs.sparse_attn(*p.dev[0], meta, scale=sc)
+    torch.cuda.synchronize()
+    r = to_np(meta.residual)
+    assert np.max(np.abs(r)) <= 1e-5 * max(1.0, np.max(np.abs(to_np(od))))
+    assert_close(to_np(out), to_np(od).astype(np.float64), dtype, "reuse vs dense at keep = N")
+
+
+def test_reuse_on_selection_inputs_reproduces_dense():
+    _need_gpu()
+    grid, H, d, G = (4, 8, 20), 2, 128, 64
+    p = build_problem(grid, H, d, "bf16", G, [128, 64], 0.0, [1], wid=109)
+    sc = scale_for(d)
+    meta, od = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc, return_dense=True)
+    out = mcs.sparse_attn(*p.dev[0], meta, scale=sc)
+    torch.cuda.synchronize()
+    a, b = to_np(out), to_np(od)
+    # O_sparse + (O_dense - O_sparse) equals O_dense up to float32 rounding,
+    # then both are rounded to bf16: at most one bf16 step apart
+    assert np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-3)) <= 2 ** -7
+    for h in range(H):
+        q, k, v = p.heads_np[(h, 0)]
+        assert_close(a[h], orc.dense_attention(q, k, v, sc), "bf16", f"head {h}")
+
+
+def test_deterministic():
+    _need_gpu()
+    grid, H, d, G = (4, 8, 20), 2, 64, 128
+    p = build_problem(grid, H, d, "bf16", G, [100, 300], 0.02, [1], wid=110)
+    sc = scale_for(d)
+    res = []
+    for _ in range(2):
+        meta, od = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc, return_dense=True)
+        out = mcs.sparse_attn(*p.dev[1], meta, scale=sc)
+        torch.cuda.synchronize()
+        res.append([meta.perm.clone(), meta.keep.clone(), meta.idx_start.clone(), meta.sched.clone(),
+                    meta.idx.clone(), meta.residual.clone(), od.clone(), out.clone()])
+    for a, b in zip(*res):
+        assert torch.equal(a.contiguous().view(-1).view(torch.uint8), b.contiguous().view(-1).view(torch.uint8))
+
+
+def test_empty_problems():
+    _need_gpu()
+    for shape in [(0, 64, 64), (2, 0, 64)]:
+        q = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+        o = mcs.dense_attn(q, q, q)
+        assert o.shape == shape
+        meta, _ = mcs.select(q, q, q, 64, [1] * shape[0], np.zeros((8, 64), np.float32))
+        out = mcs.sparse_attn(q, q, q, meta)
+        assert out.shape == shape

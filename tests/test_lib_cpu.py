@@ -1,0 +1,170 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects invalid arguments before touching the device."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mcs.h")
+
+L = pytest.importorskip("sparse_attention_diffusion_mcs_amd._lib")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mcs_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libmcs.so not built")
+    return L.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert set(names) == set(L.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mcs_version() == 1
+    assert lib.mcs_status_string(0) == b"MCS_SUCCESS"
+    assert lib.mcs_status_string(6) == b"MCS_ERROR_HIP"
+    assert lib.mcs_status_string(99) == b"MCS_UNKNOWN_STATUS"
+    assert lib.mcs_last_hip_error() == 0
+
+
+def _desc(H=2, N=100, d=64, dt=1, scale=0.0):
+    return L.AttnDesc(H, N, d, dt, scale)
+
+
+def _i32(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+FAKE = ctypes.c_void_p(0x7f0000000000)        # 256-aligned, never dereferenced: validation fails first
+FAKE_MIS = ctypes.c_void_p(0x7f0000000008)
+NULL = ctypes.c_void_p(0)
+
+
+def test_dense_validation(lib):
+    f = lib.mcs_dense_attn
+    assert f(None, FAKE, FAKE, FAKE, FAKE, NULL) == L.MCS_ERROR_INVALID_VALUE
+    assert f(ctypes.byref(_desc(d=96)), FAKE, FAKE, FAKE, FAKE, NULL) == L.MCS_ERROR_UNSUPPORTED_SHAPE
+    assert f(ctypes.byref(_desc(dt=7)), FAKE, FAKE, FAKE, FAKE, NULL) == L.MCS_ERROR_UNSUPPORTED_SHAPE
+    assert f(ctypes.byref(_desc(H=-1)), FAKE, FAKE, FAKE, FAKE, NULL) == L.MCS_ERROR_INVALID_VALUE
+    assert f(ctypes.byref(_desc(N=(1 << 24) + 1)), FAKE, FAKE, FAKE, FAKE, NULL) == L.MCS_ERROR_UNSUPPORTED_SHAPE
+    assert f(ctypes.byref(_desc(scale=float("nan"))), FAKE, FAKE, FAKE, FAKE, NULL) == L.MCS_ERROR_INVALID_VALUE
+    assert f(ctypes.byref(_desc()), NULL, FAKE, FAKE, FAKE, NULL) == L.MCS_ERROR_INVALID_VALUE
+    assert f(ctypes.byref(_desc()), FAKE, FAKE, FAKE_MIS, FAKE, NULL) == L.MCS_ERROR_MISALIGNED
+    # empty problems are valid no-ops, whatever the pointers
+    assert f(ctypes.byref(_desc(H=0)), NULL, NULL, NULL, NULL, NULL) == L.MCS_SUCCESS
+    assert f(ctypes.byref(_desc(N=0)), NULL, NULL, NULL, NULL, NULL) == L.MCS_SUCCESS
+
+
+def test_meta_layout(lib):
+    H, N, d, G = 3, 1000, 128, 64
+    keep, kp = _i32([64, 100, 1000])
+    m = L.Meta()
+    assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), G, kp, ctypes.byref(m)) == L.MCS_SUCCESS
+    ng = -(-N // G)
+    assert (m.version, m.num_heads, m.seq_len, m.head_dim, m.group_size, m.num_groups) == (1, H, N, d, G, ng)
+    assert m.total_idx == ng * keep.sum() and m.max_keep == 1000 and m.base is None
+    offs = [m.off_perm, m.off_keep, m.off_idx_start, m.off_sched, m.off_idx, m.off_residual]
+    sizes = [H * N * 4, H * 4, H * 8, H * 4, m.total_idx * 4, H * N * d * 4]
+    assert all(o % 256 == 0 for o in offs)
+    for (o, s), o2 in zip(zip(offs, sizes), offs[1:] + [m.bytes]):
+        assert o + s <= o2
+    assert lib.mcs_meta_bytes(ctypes.byref(_desc(H, N, d)), G, kp) == m.bytes
+    # invalid keep / group
+    bad, bp = _i32([64, 0, 5])
+    assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), G, bp, ctypes.byref(m)) == L.MCS_ERROR_INVALID_VALUE
+    bad, bp = _i32([64, 1001, 5])
+    assert lib.mcs_meta_bytes(ctypes.byref(_desc(H, N, d)), G, bp) == 0
+    assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), 32, kp, ctypes.byref(m)) == L.MCS_ERROR_UNSUPPORTED_SHAPE
+    assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), G, None, ctypes.byref(m)) == L.MCS_ERROR_INVALID_VALUE
+
+
+def test_workspace_bytes(lib):
+    d = _desc(4, 1000, 64)
+    one = lib.mcs_select_workspace_bytes(ctypes.byref(d), 64, 1)
+    two = lib.mcs_select_workspace_bytes(ctypes.byref(d), 64, 2)
+    per = 16 * 1024 * 4      # 16 groups x N rounded up to 64 x float32
+    assert two - one == per
+    assert lib.mcs_select_workspace_bytes(ctypes.byref(d), 64, 99) == lib.mcs_select_workspace_bytes(
+        ctypes.byref(d), 64, 4)
+    assert lib.mcs_select_workspace_bytes(ctypes.byref(d), 48, 1) == 0
+
+
+def test_select_validation(lib):
+    H, N, d = 2, 100, 64
+    keep, kp = _i32([10, 20])
+    proj = np.zeros((8, d), np.float32)
+    pp = proj.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    m = L.Meta()
+    D = ctypes.byref(_desc(H, N, d))
+    mb = lib.mcs_meta_bytes(D, 64, kp)
+    wb = lib.mcs_select_workspace_bytes(D, 64, 1)
+    sel = lib.mcs_select
+    args = lambda **kw: [kw.get("desc", D), FAKE, FAKE, FAKE, kw.get("G", 64), kw.get("keep", kp),
+                         kw.get("proj", pp), kw.get("meta", FAKE), kw.get("mb", mb), kw.get("ws", FAKE),
+                         kw.get("wb", wb), kw.get("od", NULL), kw.get("out", ctypes.byref(m)), NULL]
+    assert sel(*args(G=96)) == L.MCS_ERROR_UNSUPPORTED_SHAPE
+    assert sel(*args(proj=None)) == L.MCS_ERROR_INVALID_VALUE
+    assert sel(*args(meta=NULL)) == L.MCS_ERROR_INVALID_VALUE
+    assert sel(*args(meta=FAKE_MIS)) == L.MCS_ERROR_MISALIGNED
+    assert sel(*args(ws=FAKE_MIS)) == L.MCS_ERROR_MISALIGNED
+    assert sel(*args(od=FAKE_MIS)) == L.MCS_ERROR_MISALIGNED
+    assert sel(*args(mb=mb - 1)) == L.MCS_ERROR_BUFFER_TOO_SMALL
+    assert sel(*args(wb=wb - 1)) == L.MCS_ERROR_BUFFER_TOO_SMALL
+    assert sel(*args(out=None)) == L.MCS_ERROR_INVALID_VALUE
+    bad, bp = _i32([0, 20])
+    assert sel(*args(keep=bp)) == L.MCS_ERROR_INVALID_VALUE
+    # empty problem: validates, fills the descriptor, launches nothing
+    m0 = L.Meta()
+    D0 = ctypes.byref(_desc(0, N, d))
+    assert sel(D0, NULL, NULL, NULL, 64, kp, pp, NULL, 0, NULL, 0, NULL, ctypes.byref(m0), NULL) == L.MCS_SUCCESS
+    assert m0.version == 1 and m0.num_heads == 0 and m0.bytes == 0
+
+
+def test_sparse_validation(lib):
+    H, N, d = 2, 100, 64
+    keep, kp = _i32([10, 20])
+    m = L.Meta()
+    assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), 64, kp, ctypes.byref(m)) == L.MCS_SUCCESS
+    m.base = FAKE.value
+    f = lib.mcs_sparse_attn
+    for bad in (_desc(H + 1, N, d), _desc(H, N + 1, d), _desc(H, N, 128), _desc(H, N, d, dt=0)):
+        assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, ctypes.byref(m), FAKE, NULL) == L.MCS_ERROR_META_MISMATCH
+    m2 = L.Meta.from_buffer_copy(m)
+    m2.version = 2
+    assert f(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, ctypes.byref(m2), FAKE, NULL) == L.MCS_ERROR_META_MISMATCH
+    assert f(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, None, FAKE, NULL) == L.MCS_ERROR_INVALID_VALUE
+    assert f(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, ctypes.byref(m), NULL, NULL) == L.MCS_ERROR_INVALID_VALUE
+    m3 = L.Meta.from_buffer_copy(m)
+    m3.base = FAKE_MIS.value
+    assert f(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, ctypes.byref(m3), FAKE, NULL) == L.MCS_ERROR_MISALIGNED
+    m4 = L.Meta.from_buffer_copy(m)
+    m4.base = None
+    assert f(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, ctypes.byref(m4), FAKE, NULL) == L.MCS_ERROR_INVALID_VALUE
+
+
+def test_meta_init_validation(lib):
+    H, N, d = 2, 100, 64
+    keep, kp = _i32([10, 20])
+    m = L.Meta()
+    D = ctypes.byref(_desc(H, N, d))
+    mb = lib.mcs_meta_bytes(D, 64, kp)
+    assert lib.mcs_meta_init(D, 64, kp, NULL, mb, ctypes.byref(m), NULL) == L.MCS_ERROR_INVALID_VALUE
+    assert lib.mcs_meta_init(D, 64, kp, FAKE_MIS, mb, ctypes.byref(m), NULL) == L.MCS_ERROR_MISALIGNED
+    assert lib.mcs_meta_init(D, 64, kp, FAKE, mb - 4, ctypes.byref(m), NULL) == L.MCS_ERROR_BUFFER_TOO_SMALL
+    assert lib.mcs_meta_init(D, 64, kp, FAKE, mb, None, NULL) == L.MCS_ERROR_INVALID_VALUE

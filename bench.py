@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""MC-Sparse benchmark on one MI355X.
+
+One timed step is one denoising segment of the workload: the selection step
+(hash and group permutation, exact dense attention with per-group key scores,
+per-group top-k, selection-time sparse pass and residual) on the step-0
+inputs, followed by every reuse step on that step's drifted inputs.  All
+inputs are generated (seeded, synthetic) and resident in device memory before
+the timed region.  The library's own dense attention is timed on the same
+inputs as the speedup baseline.
+
+Prints one JSON line: `value` is the mean reuse-step time in ms (lower is
+better), with the speedup over dense, the selection time, the amortised time
+per denoising step, the roofline of the reuse kernel measured with HIP events
+on the launch stream, and the CPU oracle timed on a bounded sample of the same
+workload on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mcs_inputs import WORKLOADS, hash_projections, head_base, head_step, position_embedding  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "reuse-step sparse attn ms + speedup vs dense; % bf16 MFMA peak (1 GPU)"
+ATTN_SRC = os.path.join(ROOT, "sparse_attention_diffusion_mcs_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_reuse_workload2.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5, help="timed denoising segments")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--keep", type=float, default=None, help="override the keep fraction")
+    ap.add_argument("--group", type=int, default=None, help="override the group size")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-groups", type=int, default=96, help="oracle groups sampled per sampled head")
+    ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 8))
+    return ap.parse_args()
+
+
+def workload_of(args):
+    w = WORKLOADS[args.workload]
+    if args.keep is not None:
+        w = w.with_(keep_frac=(args.keep,))
+    if args.group is not None:
+        w = w.with_(group=args.group)
+    return w
+
+
+def describe(w, keeps):
+    ks = sorted(set(int(k) for k in keeps))
+    kdesc = str(ks[0]) if len(ks) == 1 else "/".join(map(str, ks))
+    T, Y, X = w.grid
+    return (f"{w.name}: H={w.heads}, N={w.seq_len} ({T}x{Y}x{X}), d={w.head_dim}, {w.dtype}, G={w.group}, "
+            f"k={kdesc} per group, select once + {w.reuse_steps} reuse steps, drift {w.drift}*t")
+
+
+def generate(w, steps, threads, seed=0):
+    """Device tensors per step: {t: (q, k, v)} in [H, N, d] bf16."""
+    import torch
+    pos = position_embedding(w.grid, w.head_dim)
+    H, N, d = w.heads, w.seq_len, w.head_dim
+    bases = [None] * H
+
+    def mk_base(h):
+        bases[h] = head_base(seed, w.wid, h, w.grid, d, pos)
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(mk_base, range(H)))
+    out = {}
+    for t in steps:
+        host = [np.empty((H, N, d), np.float32) for _ in range(3)]
+
+        def mk(h):
+            xs = head_step(bases[h], seed, w.wid, h, t, w.drift, True)
+            for i in range(3):
+                host[i][h] = xs[i]
+
+        with cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(mk, range(H)))
+        out[t] = tuple(torch.from_numpy(x).to("cuda").to(torch.bfloat16) for x in host)
+        del host
+    return out
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(w, keeps, T, scale, n_groups, seed=0):
+    """Times the oracle on sampled (head, group) units of the workload and
+    extrapolates to the whole layer."""
+    import threadpoolctl
+
+    import oracle.mcs_oracle as orc
+
+    H, N, d, G = w.heads, w.seq_len, w.head_dim, w.group
+    ng = w.num_groups
+    heads = sorted({0, H - 1})
+    rng = np.random.default_rng(1234)
+    fixed = [0, 1, ng // 2, ng - 1]
+    extra = rng.choice(np.arange(2, ng - 1), size=max(0, min(n_groups, ng) - len(set(fixed))), replace=False)
+    groups = sorted(set(fixed) | set(int(x) for x in extra))
+    tsteps = sorted({1, max(1, T // 2), T})
+    pos = position_embedding(w.grid, d)
+    proj = hash_projections(seed, w.wid, d)
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    t_hash, t_sel, t_reuse = [], [], []
+    for h in heads:
+        base = head_base(seed, w.wid, h, w.grid, d, pos)
+        q, k, v = head_step(base, seed, w.wid, h, 0, w.drift, True)
+        later = {t: head_step(base, seed, w.wid, h, t, w.drift, True) for t in tsteps}
+        t0 = time.perf_counter()
+        perm = orc.group_permutation(orc.hash_keys(q, proj))
+        t_hash.append(time.perf_counter() - t0)
+        ranges = orc.group_ranges(N, G)
+        for g in groups:
+            rows = perm[ranges[g][0]:ranges[g][1]]
+            t0 = time.perf_counter()
+            sel = orc.select_group(q, k, v, rows, int(keeps[h]), scale)
+            t_sel.append(time.perf_counter() - t0)
+            for t in tsteps:
+                t0 = time.perf_counter()
+                orc.reuse_group(*later[t], rows, sel.idx, sel.residual, scale)
+                t_reuse.append(time.perf_counter() - t0)
+    units = H * ng
+    sel_ms = 1e3 * (np.mean(t_hash) * H + np.mean(t_sel) * units)
+    reuse_ms = 1e3 * np.mean(t_reuse) * units
+    work_s = sum(t_hash) + sum(t_sel) + sum(t_reuse)
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": round(float(reuse_ms), 3), "unit": "ms", "cores": int(cores), "kind": "oracle",
+        "sample": (f"float64 numpy oracle on heads {heads} x {len(groups)} of {ng} query groups "
+                   f"(reuse steps {tsteps}); per-unit mean times x {units} units = extrapolated full-layer "
+                   f"reuse-step ms; {work_s:.1f} s of CPU work; {cpu_model}"),
+        "select_ms_extrapolated": round(float(sel_ms), 1),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sparse_attention_diffusion_mcs_amd as mcs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mcs.lib()  # fail loudly if the library is missing
+
+    w = workload_of(args)
+    keeps = w.keeps()
+    H, N, d, G, T = w.heads, w.seq_len, w.head_dim, w.group, w.reuse_steps
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    log(f"workload {args.workload}: {describe(w, keeps)}")
+    t0 = time.time()
+    X = generate(w, range(0, T + 1), args.threads)
+    torch.cuda.synchronize()
+    log(f"inputs generated and resident ({time.time() - t0:.1f} s)")
+
+    proj = hash_projections(0, w.wid, d)
+    q0 = X[0][0]
+    ws = torch.empty(mcs.workspace_bytes(q0, G), dtype=torch.uint8, device="cuda")
+    meta_probe = mcs.meta_layout(H, N, d, 1, G, keeps)
+    meta_buf = torch.empty(int(meta_probe.bytes), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q0)
+    stream = torch.cuda.current_stream()
+
+    def segment(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        meta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=meta_buf, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        for t in range(1, T + 1):
+            if ev is not None:
+                ev[2 * t].record(stream)
+            mcs.sparse_attn(*X[t], meta, out=out, scale=scale)
+            if ev is not None:
+                ev[2 * t + 1].record(stream)
+        return meta
+
+    for _ in range(args.warmup):
+        segment()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * T + 2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        meta = segment(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    reuse_ms = [e[2 * t].elapsed_time(e[2 * t + 1]) for e in evs for t in range(1, T + 1)]
+    log(f"segments: wall {1e3 * wall / args.steps:.3f} ms/segment; select {np.median(sel_ms):.3f} ms; "
+        f"reuse mean {np.mean(reuse_ms):.4f} ms")
+
+    # dense baseline on the same inputs
+    dense_out = torch.empty_like(q0)
+    for _ in range(args.warmup):
+        mcs.dense_attn(*X[0], out=dense_out, scale=scale)
+    dev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for k in range(args.steps):
+        dev[k][0].record(stream)
+        mcs.dense_attn(*X[1 + k % T], out=dense_out, scale=scale)
+        dev[k][1].record(stream)
+    torch.cuda.synchronize()
+    dense_ms = [a.elapsed_time(b) for a, b in dev]
+
+    # fidelity of reuse steps against dense attention on the same step
+    fid = {}
+    for t in sorted({1, max(1, T // 2), T}):
+        o_s = mcs.sparse_attn(*X[t], meta, scale=scale).float()
+        o_d = mcs.dense_attn(*X[t], scale=scale).float()
+        fid[str(t)] = round(float(torch.linalg.vector_norm(o_s - o_d) / torch.linalg.vector_norm(o_d)), 6)
+    torch.cuda.synchronize()
+
+    reuse_mean = float(np.mean(reuse_ms))
+    sel_med = float(np.median(sel_ms))
+    dense_med = float(np.median(dense_ms))
+    flops_reuse = 4.0 * N * float(np.sum(keeps)) * d  # sum over heads of 4 N k_h d
+    flops_dense = 4.0 * N * N * d * H
+    flops_select = 1.5 * flops_dense + flops_reuse
+    achieved = flops_reuse / (reuse_mean * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            with open(TRAFFIC_FILE) as f:
+                tr = json.load(f)
+            if tr.get("source_sha") == src_hash(ATTN_SRC) and tr.get("workload") == args.workload:
+                traffic = tr.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    result = {
+        "metric": METRIC,
+        "value": round(reuse_mean, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / args.steps, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded DiT-shaped generator; no model weights)",
+        "config": {"workload": describe(w, keeps), "heads": H, "seq_len": N, "head_dim": d, "group": G,
+                   "keep": [int(x) for x in sorted(set(keeps.tolist()))], "reuse_steps": T},
+        "reuse_ms_median": round(float(np.median(reuse_ms)), 4),
+        "dense_ms": round(dense_med, 4),
+        "speedup_vs_dense": round(dense_med / reuse_mean, 3),
+        "select_ms": round(sel_med, 3),
+        "amortised_ms_per_denoising_step": round((sel_med + T * reuse_mean) / (T + 1), 4),
+        "amortised_speedup_vs_dense": round(dense_med * (T + 1) / (sel_med + T * reuse_mean), 3),
+        "pct_bf16_peak_reuse": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
+        "pct_bf16_peak_dense": round(100.0 * flops_dense / (dense_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "select_tflops": round(flops_select / (sel_med * 1e-3) / 1e12, 1),
+        "fidelity_rel_l2_vs_dense": fid,
+        "roofline": {"kernel": f"attn_bf16_kernel<{d},{G // 32},REUSE> (reuse step)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "flops_per_launch": flops_reuse},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w, keeps, T, scale, args.cpu_groups)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,7 +19,9 @@ Acceptance rules:
 
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -28,6 +30,7 @@ import torch
 import oracle.mcs_oracle as orc
 from mcs_inputs import hash_projections, head_base, head_step, position_embedding
 
+THREADS = min(16, os.cpu_count() or 8)
 GAP = 1e-6
 TOL = {"bf16": (2e-2, 5e-3), "fp32": (2e-4, 1e-4)}
 
@@ -74,18 +77,27 @@ def build_problem(grid, H, d, dtype, G, keeps, drift, steps, seed=0, wid=100, ke
     p = Problem(tuple(grid), H, d, dtype, G, np.asarray(keeps, np.int32), drift, list(steps), seed, wid)
     pos = position_embedding(grid, d)
     bf = dtype == "bf16"
-    all_steps = [0] + p.steps
-    host = {t: [np.empty((H, p.N, d), np.float32) for _ in range(3)] for t in all_steps}
-    for h in range(H):
-        base = head_base(seed, wid, h, grid, d, pos)
-        for t in all_steps:
-            xs = head_step(base, seed, wid, h, t, drift, bf)
+    bases = [None] * H
+
+    def mk_base(h):
+        bases[h] = head_base(seed, wid, h, grid, d, pos)
+
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(mk_base, range(H)))
+    for t in [0] + p.steps:
+        host = [np.empty((H, p.N, d), np.float32) for _ in range(3)]
+
+        def mk(h, t=t, host=host):
+            xs = head_step(bases[h], seed, wid, h, t, drift, bf)
             for i in range(3):
-                host[t][i][h] = xs[i]
+                host[i][h] = xs[i]
             if keep_heads is None or h in keep_heads:
                 p.heads_np[(h, t)] = xs
-    for t in all_steps:
-        p.dev[t] = tuple(torch.from_numpy(x).to("cuda").to(p.tdtype).contiguous() for x in host[t])
+
+        with cf.ThreadPoolExecutor(THREADS) as ex:
+            list(ex.map(mk, range(H)))
+        p.dev[t] = tuple(torch.from_numpy(x).to("cuda").to(p.tdtype).contiguous() for x in host)
+        del host
     return p
 
 
@@ -124,3 +136,47 @@ def check_idx(gpu_idx, scores, k, n, what):
 
 def to_np(t):
     return t.detach().float().cpu().numpy()
+
+
+def sample_groups(ng, extra=4, seed=0):
+    """Groups {0, 1, ng/2, last} plus `extra` seeded random ones."""
+    base = {0, min(1, ng - 1), ng // 2, ng - 1}
+    pool = np.setdiff1d(np.arange(ng), list(base))
+    r = np.random.default_rng(seed)
+    pick = r.choice(pool, size=min(extra, pool.size), replace=False) if pool.size else []
+    return sorted(base | {int(x) for x in pick})
+
+
+def check_units(p: Problem, meta, od, outs, sc, heads, groups, label=""):
+    """Compares the sampled (head, group) units of a GPU run with the oracle:
+    perm of the whole head, kept keys, dense rows, residual and the reuse
+    outputs of every generated step.  Returns the number of kept-key sets
+    equal to the oracle's and the number checked."""
+    exact = total = 0
+    for h in heads:
+        q, k, v = p.heads_np[(h, 0)]
+        perm_o = orc.group_permutation(orc.hash_keys(q, p.proj()))
+        perm_g = meta.perm[h].cpu().numpy()
+        assert np.array_equal(perm_g, perm_o), f"{label} head {h}: perm differs"
+        kh = int(p.keeps[h])
+        gidx = meta.head_idx(h, kh)
+        ranges = orc.group_ranges(p.N, p.G)
+        for g in groups:
+            s, e = ranges[g]
+            rows = perm_o[s:e]
+            rows_t = torch.from_numpy(rows.astype(np.int64)).to("cuda")
+            sel = orc.select_group(q, k, v, rows, kh, sc)
+            gi = gidx[g].cpu().numpy()
+            exact += check_idx(gi, sel.scores, kh, p.N, f"{label} head {h} group {g}")
+            total += 1
+            if od is not None:
+                assert_close(to_np(od[h].index_select(0, rows_t)), sel.o_dense, p.dtype,
+                             f"{label} head {h} group {g} dense rows")
+            res_c = sel.o_dense - orc.sparse_attention(q[rows], k, v, gi, sc)
+            assert_close(to_np(meta.residual[h, s:e]), res_c, p.dtype, f"{label} head {h} group {g} residual",
+                         ref_norm=np.linalg.norm(sel.o_dense))
+            for t, o in outs.items():
+                ref = orc.reuse_group(*p.heads_np[(h, t)], rows, gi, res_c, sc)
+                assert_close(to_np(o[h].index_select(0, rows_t)), ref, p.dtype,
+                             f"{label} head {h} group {g} reuse step {t}")
+    return exact, total

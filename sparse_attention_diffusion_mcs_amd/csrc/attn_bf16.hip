@@ -9,50 +9,70 @@
 // Trips People Up" of "The quality cliff nobody admits to" (the sparse
 // softmax is renormalised over the kept tokens; the residual corrects it).
 //
-// Work decomposition.  One workgroup owns a tile of query rows: 32 rows per
-// wave (two 16-row MFMA blocks).  For the sparse modes the tile is exactly one
-// query group (G = 64 -> 2 waves, G = 128 -> 4 waves), so every wave shares
-// the group's gathered KV tile.  The loop walks KV tiles of 64 tokens: the
-// workgroup gathers K rows (row-major, padded) and V rows (transposed, two
-// tokens packed per 32-bit word) into LDS; each wave computes S^T = K Q^T so
-// that every lane ends up holding scores of a single query row; the online
-// softmax then needs one in-lane pass plus two cross-lane steps, and the
-// probabilities are already laid out as the B operand of O^T += V^T P^T.
+// Work decomposition.  A workgroup owns a tile of query rows, 32 rows per wave
+// (two 16-row MFMA blocks).  In the sparse modes the tile is exactly one query
+// group (G = 64 -> 2 waves, G = 128 -> 4 waves), so all waves share the
+// group's gathered KV tiles; in the dense modes it is 128 rows (4 waves).
+//
+// KV tiles of 32 tokens are gathered straight from global memory into LDS
+// with global_load_lds_dwordx4 (no staging registers), double-buffered with
+// one barrier per tile.  Rows are stored with an XOR swizzle of their 16-byte
+// chunks chosen so that both LDS read patterns are free of bank conflicts: the
+// K operand (16-byte reads, 16 rows per quarter-wave) and the V operand, read
+// transposed with ds_read_b64_tr_b16 (8 rows x 2 chunks per half-wave).
+//
+// Each wave computes S^T = K Q^T, so every lane holds scores of one query row;
+// the row max needs one in-lane pass and two cross-lane steps, and the
+// probabilities are already in the B-operand layout of O^T += V^T P^T.  The
+// running max is only moved (and O, l rescaled) when a row's tile max exceeds
+// it by more than 2^8; otherwise probabilities up to 2^8 are accumulated
+// against the stale max, which leaves O / l unchanged.
 #include "device.h"
 #include "launch.h"
 
 namespace mcs {
 namespace {
 
-constexpr int BKV = 64;  // KV tokens per tile
+constexpr int BKV = 32;             // KV tokens per tile
+constexpr float kRescaleSlack = 8.0f;  // log2 units
 
-// Position of token t (0..63) of a KV tile inside a transposed V row.  The S^T
-// accumulator gives lane-quad q the tokens {16h + 4q + i} of each 32-token
-// chunk (h = 0, 1; i = 0..3); this order makes those 8 tokens contiguous so
-// that the V^T operand of the PV product is a single 16-byte LDS read.
-__device__ __forceinline__ int vpos(int t) {
-  return (t & ~31) | ((t & 12) << 1) | ((t & 16) >> 2) | (t & 3);
-}
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+template <int D>
+struct Geo {
+  static constexpr int ROWB = D * 2;           // bytes per K/V row
+  static constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;         // rows per wave-wide 1 KB load
+  static constexpr int NI = BKV / RPI;         // 1 KB loads per tensor per tile
+  static constexpr int TILE = BKV * ROWB;      // bytes per tensor per tile
+  // Stored position of 16-byte chunk c of tile row t is c ^ swz(t).
+  __device__ static __forceinline__ int swz(int t) {
+    if constexpr (D == 128)
+      return ((t & 7) << 1) | ((t >> 3) & 1);
+    else
+      return (((t >> 1) & 3) << 1) | ((t >> 3) & 1);
+  }
+};
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-template <int D, int NW, int MODE>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int BM = NW * 32;
-  constexpr int KK = D / 32;          // 32-wide k-steps of QK^T
-  constexpr int DB = D / 16;          // 16-wide output column blocks
-  constexpr int KS = D + 8;           // K tile row stride (elements), 16 B pad
-  constexpr int VS = BKV + 8;         // V^T tile row stride (elements), 16 B pad
-  constexpr int CH = D / 8;           // 16-byte chunks per row
-  constexpr int UK = BKV * CH / NT;   // K chunks per thread per tile
-  constexpr int UV = (BKV / 2) * CH / NT;  // V token-pair chunks per thread per tile
-  constexpr bool SPARSE = (MODE == MODE_REUSE || MODE == MODE_RESINIT);
-  static_assert(UK * NT == BKV * CH && UV * NT == (BKV / 2) * CH, "tile/thread mismatch");
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-  __shared__ __attribute__((aligned(16))) __bf16 ks[BKV * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 vt[D * VS];
-  __shared__ float red[MODE == MODE_SELECT ? NW : 1][BKV];
+template <int D, int NW, int MODE>
+__global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
+  using GE = Geo<D>;
+  constexpr int BM = NW * 32;
+  constexpr int KK = D / 32;                 // k-steps of QK^T
+  constexpr int DB = D / 16;                 // output column blocks
+  constexpr int UPW = GE::NI / NW;           // loads per tensor per tile per wave
+  constexpr bool SPARSE = (MODE == MODE_REUSE || MODE == MODE_RESINIT);
+  constexpr int STAGE = 2 * GE::TILE;        // K tile + V tile
+  static_assert(UPW * NW == GE::NI, "tile loads must split evenly over the waves");
+
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  __shared__ float red[MODE == MODE_SELECT ? 2 : 1][NW][BKV];
   __shared__ float lse_s[MODE == MODE_SELECT ? BM : 1];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
@@ -97,55 +117,57 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  // ---- KV tile staging --------------------------------------------------
-  uint4 kreg[UK];
-  uint4 vreg[UV][2];
-  auto gload = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < UK; ++i) {
-      const int u = tid + NT * i, t = u / CH, c = u % CH, tk = j * BKV + t;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (tk < nkv) {
-        const int row = SPARSE ? clamp_index(kvidx[tk], N) : tk;
-        x = *reinterpret_cast<const uint4*>(kh + (size_t)row * D + 8 * c);
-      }
-      kreg[i] = x;
-    }
-#pragma unroll
-    for (int i = 0; i < UV; ++i) {
-      const int u = tid + NT * i, pp = u % (BKV / 2), c = u / (BKV / 2);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int tk = j * BKV + 2 * pp + e;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (tk < nkv) {
-          const int row = SPARSE ? clamp_index(kvidx[tk], N) : tk;
-          x = *reinterpret_cast<const uint4*>(vh + (size_t)row * D + 8 * c);
-        }
-        vreg[i][e] = x;
-      }
+  // ---- tile loads -------------------------------------------------------
+  // Load u of this wave covers tile rows ii*RPI .. +RPI-1 (ii = w + NW u); lane
+  // `lane` fills stored chunk (lane % CPR) of row ii*RPI + lane / CPR.
+  auto tile_row_of = [&](int u) { return (w + NW * u) * GE::RPI + lane / GE::CPR; };
+  auto source_row = [&](int j, int u) -> int {
+    const int tk = j * BKV + tile_row_of(u);
+    if constexpr (SPARSE) {
+      return clamp_index(kvidx[tk < nkv ? tk : nkv - 1], N);
+    } else {
+      return tk < N ? tk : N - 1;
     }
   };
-  auto lstore = [&]() {
+  int rows_next[UPW];
+  auto issue = [&](int j, int stage, bool with_v) {
+    char* kt = lds + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < UK; ++i) {
-      const int u = tid + NT * i, t = u / CH, c = u % CH;
-      *reinterpret_cast<uint4*>(ks + t * KS + 8 * c) = kreg[i];
+    for (int u = 0; u < UPW; ++u) {
+      const int t = tile_row_of(u);
+      const int c = (lane % GE::CPR) ^ GE::swz(t);
+      const size_t off = (size_t)rows_next[u] * D + 8 * c;
+      const int ii = w + NW * u;
+      __builtin_amdgcn_global_load_lds(kh + off, (lds_void*)(kt + ii * 1024), 16, 0, 0);
+      if (with_v) __builtin_amdgcn_global_load_lds(vh + off, (lds_void*)(kt + GE::TILE + ii * 1024), 16, 0, 0);
     }
+    (void)j;
+  };
+  auto fetch_rows = [&](int j) {
+    if (j < nt) {
 #pragma unroll
-    for (int i = 0; i < UV; ++i) {
-      const int u = tid + NT * i, pp = u % (BKV / 2), c = u / (BKV / 2);
-      const int pos = vpos(2 * pp);
-      const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-      const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = __builtin_amdgcn_perm(x1[e], x0[e], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(x1[e], x0[e], 0x07060302u);
-        *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e) * VS + pos) = lo;
-        *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e + 1) * VS + pos) = hi;
-      }
+      for (int u = 0; u < UPW; ++u) rows_next[u] = source_row(j, u);
     }
+  };
+
+  // K operand (A of S^T, or B of S): tile row 16 tb + lr, chunk lq + 4 kk
+  auto kfrag = [&](const char* kt, int tb, int kk) -> bf16x8 {
+    const int t = 16 * tb + lr;
+    const int c = (lq + 4 * kk) ^ GE::swz(t);
+    return *reinterpret_cast<const bf16x8*>(kt + t * GE::ROWB + 16 * c);
+  };
+  // V^T operand for output column block db: two transposed 8-byte reads of
+  // tokens 4 lq + lr/4 (+16), dims 16 db + 4 (lr % 4) ..
+  auto vfrag = [&](const char* vt, int db) -> bf16x8 {
+    uint2 x[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int t = 16 * hh + 4 * lq + (lr >> 2);
+      const int c = (2 * db + ((lr & 3) >> 1)) ^ GE::swz(t);
+      const char* p = vt + t * GE::ROWB + 16 * c + 8 * (lr & 1);
+      x[hh] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p));
+    }
+    return as_bf16x8(make_uint4(x[0].x, x[0].y, x[1].x, x[1].y));
   };
 
   // ---- pass 1: online-softmax attention over the KV tiles ---------------
@@ -157,23 +179,30 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  lstore();
-  __syncthreads();
+  fetch_rows(0);
+  issue(0, 0, true);
+  fetch_rows(1);
   for (int j = 0; j < nt; ++j) {
-    if (j + 1 < nt) gload(j + 1);
+    wait_vm();
+    __syncthreads();
+    if (j + 1 < nt) {
+      issue(j + 1, (j + 1) & 1, true);
+      fetch_rows(j + 2);
+    }
+    const char* kt = lds + (j & 1) * STAGE;
+    const char* vt = kt + GE::TILE;
 
     // S^T[token][row]: lane holds tokens 16 tb + 4 lq + i of row 16 rb + lr
-    f32x4 s[4][2];
+    f32x4 s[2][2];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) s[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (16 * tb + lr) * KS + 8 * lq + 32 * kk);
+      for (int tb = 0; tb < 2; ++tb) {
+        const bf16x8 kf = kfrag(kt, tb, kk);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           s[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][kk], s[tb][rb], 0, 0, 0);
@@ -182,7 +211,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     const int vcols = nkv - j * BKV;
     if (vcols < BKV) {
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (16 * tb + 4 * lq + i >= vcols) {
@@ -191,57 +220,53 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
           }
     }
 
-    bf16x8 pf[2][2];
+    float mx[2];
+    bool need = false;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float mx = s[0][rb][0];
+      float m = fmaxf(fmaxf(s[0][rb][0], s[0][rb][1]), fmaxf(s[0][rb][2], s[0][rb][3]));
+      m = fmaxf(m, fmaxf(fmaxf(s[1][rb][0], s[1][rb][1]), fmaxf(s[1][rb][2], s[1][rb][3])));
+      m = fmaxf(m, xor_shfl(m, 16));
+      m = fmaxf(m, xor_shfl(m, 32));
+      mx[rb] = m * sl2;
+      need |= mx[rb] > m_run[rb] + kRescaleSlack;
+    }
+    if (__ballot(need) != 0ull) {
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int rb = 0; rb < 2; ++rb) {
+        const float mnew = fmaxf(m_run[rb], mx[rb]);
+        const float alpha = fast_exp2(m_run[rb] - mnew);
+        m_run[rb] = mnew;
+        l_run[rb] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tb][rb][i]);
-      mx = fmaxf(mx, xor_shfl(mx, 16));
-      mx = fmaxf(mx, xor_shfl(mx, 32));
-      const float mnew = fmaxf(m_run[rb], mx * sl2);
-      const float alpha = fast_exp2(m_run[rb] - mnew);
-      m_run[rb] = mnew;
+        for (int db = 0; db < DB; ++db) oacc[db][rb] *= alpha;
+      }
+    }
+    bf16x8 pf[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
       float ls = 0.f;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(fmaf(s[tb][rb][i], sl2, -mnew));
+          const float p = fast_exp2(fmaf(s[tb][rb][i], sl2, -m_run[rb]));
           s[tb][rb][i] = p;
           ls += p;
         }
-      l_run[rb] = l_run[rb] * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db][rb] *= alpha;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        bf16x8 t;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          t[i] = (__bf16)s[2 * kc][rb][i];
-          t[4 + i] = (__bf16)s[2 * kc + 1][rb][i];
-        }
-        pf[kc][rb] = t;
-      }
+      l_run[rb] += ls;
+      pf[rb] = as_bf16x8(make_uint4(pack_bf16x2(s[0][rb][0], s[0][rb][1]), pack_bf16x2(s[0][rb][2], s[0][rb][3]),
+                                    pack_bf16x2(s[1][rb][0], s[1][rb][1]), pack_bf16x2(s[1][rb][2], s[1][rb][3])));
     }
 
     // O^T[dim][row] += V^T P^T
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 vf = vfrag(vt, db);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + (16 * db + lr) * VS + 32 * kc + 8 * lq);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kc][rb], oacc[db][rb], 0, 0, 0);
-      }
+      for (int rb = 0; rb < 2; ++rb)
+        oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], oacc[db][rb], 0, 0, 0);
     }
-    __syncthreads();
-    if (j + 1 < nt) lstore();
-    __syncthreads();
   }
 
   // ---- epilogue ---------------------------------------------------------
@@ -291,33 +316,49 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) nlse[rb][i] = -lse_s[32 * w + 16 * rb + 4 * lq + i];
 
-  constexpr int WPG_MAX = 4;  // waves per group (G / 32)
-  const int wpg = a.G / 32;
+  const int wpg = a.G / 32;   // waves per group
   const int gpt = BM / a.G;   // groups per tile
-  (void)WPG_MAX;
-  gload(0);
-  lstore();
-  __syncthreads();
+  auto flush = [&](int j) {   // cross-wave sums of tile j -> colsum
+    for (int t = tid; t < gpt * BKV; t += NW * 64) {
+      const int gi = t / BKV, col = t % BKV, tok = j * BKV + col;
+      const int g = row0 / a.G + gi;
+      if (tok < N && g < a.ng) {
+        float sum = 0.f;
+        for (int ww = 0; ww < wpg; ++ww) sum += red[j & 1][gi * wpg + ww][col];
+        a.colsum[((size_t)hs * a.ng + g) * a.ldc + tok] = sum;
+      }
+    }
+  };
+  fetch_rows(0);
+  issue(0, 0, false);
+  fetch_rows(1);
   for (int j = 0; j < nt; ++j) {
-    if (j + 1 < nt) gload(j + 1);
+    wait_vm();
+    __syncthreads();
+    if (j + 1 < nt) {
+      issue(j + 1, (j + 1) & 1, false);
+      fetch_rows(j + 2);
+    }
+    if (j > 0) flush(j - 1);
+    const char* kt = lds + (j & 1) * STAGE;
     // S[row][token]: lane holds rows 16 rb + 4 lq + i of token 16 tb + lr
-    f32x4 s[2][4];
+    f32x4 s[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) s[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tb = 0; tb < 2; ++tb) s[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (16 * tb + lr) * KS + 8 * lq + 32 * kk);
+      for (int tb = 0; tb < 2; ++tb) {
+        const bf16x8 kf = kfrag(kt, tb, kk);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           s[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rb][kk], kf, s[rb][tb], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int tb = 0; tb < 2; ++tb) {
       float cs = 0.f;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
@@ -325,21 +366,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i) cs += fast_exp2(fmaf(s[rb][tb][i], sl2, nlse[rb][i]));
       cs += xor_shfl(cs, 16);
       cs += xor_shfl(cs, 32);
-      if (lq == 0) red[w][16 * tb + lr] = cs;
+      if (lq == 0) red[j & 1][w][16 * tb + lr] = cs;
     }
-    __syncthreads();
-    for (int t = tid; t < gpt * BKV; t += NT) {
-      const int gi = t / BKV, col = t % BKV, tok = j * BKV + col;
-      const int g = row0 / a.G + gi;
-      if (tok < N && g < a.ng) {
-        float sum = 0.f;
-        for (int ww = 0; ww < wpg; ++ww) sum += red[gi * wpg + ww][col];
-        a.colsum[((size_t)hs * a.ng + g) * a.ldc + tok] = sum;
-      }
-    }
-    if (j + 1 < nt) lstore();
-    __syncthreads();
   }
+  __syncthreads();
+  if (nt > 0) flush(nt - 1);
 }
 
 template <int D, int NW, int MODE>

@@ -58,35 +58,40 @@ def _lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m sparse_attention_diffusion_mcs_amd.build` (no CPU fallback exists)")
-        lib = ctypes.CDLL(LIB_PATH)
-        P = ctypes.c_void_p
-        DP = ctypes.POINTER(AttnDesc)
-        MP = ctypes.POINTER(Meta)
-        I32P = ctypes.POINTER(ctypes.c_int32)
-        F32P = ctypes.POINTER(ctypes.c_float)
-        lib.mcs_version.restype = ctypes.c_int
-        lib.mcs_version.argtypes = []
-        lib.mcs_status_string.restype = ctypes.c_char_p
-        lib.mcs_status_string.argtypes = [ctypes.c_int]
-        lib.mcs_last_hip_error.restype = ctypes.c_int
-        lib.mcs_last_hip_error.argtypes = []
-        lib.mcs_dense_attn.restype = ctypes.c_int
-        lib.mcs_dense_attn.argtypes = [DP, P, P, P, P, P]
-        lib.mcs_meta_layout.restype = ctypes.c_int
-        lib.mcs_meta_layout.argtypes = [DP, ctypes.c_int32, I32P, MP]
-        lib.mcs_meta_bytes.restype = ctypes.c_size_t
-        lib.mcs_meta_bytes.argtypes = [DP, ctypes.c_int32, I32P]
-        lib.mcs_select_workspace_bytes.restype = ctypes.c_size_t
-        lib.mcs_select_workspace_bytes.argtypes = [DP, ctypes.c_int32, ctypes.c_int32]
-        lib.mcs_meta_init.restype = ctypes.c_int
-        lib.mcs_meta_init.argtypes = [DP, ctypes.c_int32, I32P, P, ctypes.c_size_t, MP, P]
-        lib.mcs_select.restype = ctypes.c_int
-        lib.mcs_select.argtypes = [DP, P, P, P, ctypes.c_int32, I32P, F32P, P, ctypes.c_size_t, P,
-                                   ctypes.c_size_t, P, MP, P]
-        lib.mcs_sparse_attn.restype = ctypes.c_int
-        lib.mcs_sparse_attn.argtypes = [DP, P, P, P, MP, P, P]
-        _LIB = lib
+        _LIB = open_library(LIB_PATH)
     return _LIB
+
+
+def open_library(path):
+    """Loads a libmcs build at `path` and declares its C prototypes."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    DP = ctypes.POINTER(AttnDesc)
+    MP = ctypes.POINTER(Meta)
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    F32P = ctypes.POINTER(ctypes.c_float)
+    lib.mcs_version.restype = ctypes.c_int
+    lib.mcs_version.argtypes = []
+    lib.mcs_status_string.restype = ctypes.c_char_p
+    lib.mcs_status_string.argtypes = [ctypes.c_int]
+    lib.mcs_last_hip_error.restype = ctypes.c_int
+    lib.mcs_last_hip_error.argtypes = []
+    lib.mcs_dense_attn.restype = ctypes.c_int
+    lib.mcs_dense_attn.argtypes = [DP, P, P, P, P, P]
+    lib.mcs_meta_layout.restype = ctypes.c_int
+    lib.mcs_meta_layout.argtypes = [DP, ctypes.c_int32, I32P, MP]
+    lib.mcs_meta_bytes.restype = ctypes.c_size_t
+    lib.mcs_meta_bytes.argtypes = [DP, ctypes.c_int32, I32P]
+    lib.mcs_select_workspace_bytes.restype = ctypes.c_size_t
+    lib.mcs_select_workspace_bytes.argtypes = [DP, ctypes.c_int32, ctypes.c_int32]
+    lib.mcs_meta_init.restype = ctypes.c_int
+    lib.mcs_meta_init.argtypes = [DP, ctypes.c_int32, I32P, P, ctypes.c_size_t, MP, P]
+    lib.mcs_select.restype = ctypes.c_int
+    lib.mcs_select.argtypes = [DP, P, P, P, ctypes.c_int32, I32P, F32P, P, ctypes.c_size_t, P,
+                               ctypes.c_size_t, P, MP, P]
+    lib.mcs_sparse_attn.restype = ctypes.c_int
+    lib.mcs_sparse_attn.argtypes = [DP, P, P, P, MP, P, P]
+    return lib
 
 
 def lib():

@@ -14,15 +14,18 @@
 // group (G = 64 -> 2 waves, G = 128 -> 4 waves), so all waves share the
 // group's gathered KV tiles; in the dense modes it is 128 rows (4 waves).
 //
-// KV tiles of 32 tokens are gathered straight from global memory into LDS
-// with global_load_lds_dwordx4 (no staging registers), double-buffered with
-// one barrier per tile.  Rows are stored with an XOR swizzle of their 16-byte
-// chunks chosen so that both LDS read patterns are free of bank conflicts: the
-// K operand (16-byte reads, 16 rows per quarter-wave) and the V operand, read
-// transposed with ds_read_b64_tr_b16 (8 rows x 2 chunks per half-wave).
+// KV tiles of BK tokens are gathered straight from global memory into LDS with
+// global_load_lds_dwordx4 (no staging registers) through an NST-deep ring of
+// LDS stages, one barrier per tile.  The kept-key indices of a tile are
+// wave-uniform data and are read with scalar loads, so they never queue behind
+// the tile copies on the vector-memory counter.  Rows are stored with an XOR
+// swizzle of their 16-byte chunks chosen so that both LDS read patterns are
+// free of bank conflicts: the K operand (16-byte reads, 16 rows per
+// quarter-wave) and the V operand, read transposed with ds_read_b64_tr_b16
+// (8 rows x 2 chunks per half-wave).
 //
 // Each wave computes S^T = K Q^T, so every lane holds scores of one query row;
-// the row max needs one in-lane pass and two cross-lane steps, and the
+// the row max needs one in-lane pass and two row-swap permutes, and the
 // probabilities are already in the B-operand layout of O^T += V^T P^T.  The
 // running max is only moved (and O, l rescaled) when a row's tile max exceeds
 // it by more than 2^8; otherwise probabilities up to 2^8 are accumulated
@@ -30,23 +33,29 @@
 #include "device.h"
 #include "launch.h"
 
+#ifndef MCS_BK
+#define MCS_BK 32
+#endif
+#ifndef MCS_NST
+#define MCS_NST 2
+#endif
+
 namespace mcs {
 namespace {
 
-constexpr int BKV = 32;             // KV tokens per tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-template <int D>
+template <int D, int BK>
 struct Geo {
   static constexpr int ROWB = D * 2;           // bytes per K/V row
   static constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;         // rows per wave-wide 1 KB load
-  static constexpr int NI = BKV / RPI;         // 1 KB loads per tensor per tile
-  static constexpr int TILE = BKV * ROWB;      // bytes per tensor per tile
+  static constexpr int NI = BK / RPI;          // 1 KB loads per tensor per tile
+  static constexpr int TILE = BK * ROWB;       // bytes per tensor per tile
   // Stored position of 16-byte chunk c of tile row t is c ^ swz(t).
   __device__ static __forceinline__ int swz(int t) {
     if constexpr (D == 128)
@@ -58,24 +67,31 @@ struct Geo {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-template <int D, int NW, int MODE>
+template <int D, int NW, int MODE, int BK, int NST>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
-  using GE = Geo<D>;
+  using GE = Geo<D, BK>;
   constexpr int BM = NW * 32;
   constexpr int KK = D / 32;                 // k-steps of QK^T
   constexpr int DB = D / 16;                 // output column blocks
+  constexpr int TB = BK / 16;                // 16-token blocks per tile
+  constexpr int KC = BK / 32;                // 32-token chunks of the PV product
   constexpr int UPW = GE::NI / NW;           // loads per tensor per tile per wave
   constexpr bool SPARSE = (MODE == MODE_REUSE || MODE == MODE_RESINIT);
   constexpr int STAGE = 2 * GE::TILE;        // K tile + V tile
   static_assert(UPW * NW == GE::NI, "tile loads must split evenly over the waves");
+  static_assert(NST == 2 || NST == 3, "2 or 3 pipeline stages");
 
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
-  __shared__ float red[MODE == MODE_SELECT ? 2 : 1][NW][BKV];
+  __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
+  __shared__ float red[MODE == MODE_SELECT ? 2 : 1][NW][BK];
   __shared__ float lse_s[MODE == MODE_SELECT ? BM : 1];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = a.N;
 
   // ---- work item -------------------------------------------------------
@@ -97,7 +113,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     group_keys(a.keep, a.idx_start, h, tile, N, a.total_idx, &start, &nkv);
     kvidx = a.idx + start;
   }
-  const int nt = (nkv + BKV - 1) / BKV;
+  const int nt = (nkv + BK - 1) / BK;
   const float sl2 = a.scale * kLog2e;
 
   // ---- Q fragments: lane holds row (16 rb + lr) of its wave, dims 8 lq + 32 kk ..
@@ -119,35 +135,49 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 
   // ---- tile loads -------------------------------------------------------
   // Load u of this wave covers tile rows ii*RPI .. +RPI-1 (ii = w + NW u); lane
-  // `lane` fills stored chunk (lane % CPR) of row ii*RPI + lane / CPR.
-  auto tile_row_of = [&](int u) { return (w + NW * u) * GE::RPI + lane / GE::CPR; };
-  auto source_row = [&](int j, int u) -> int {
-    const int tk = j * BKV + tile_row_of(u);
-    if constexpr (SPARSE) {
-      return clamp_index(kvidx[tk < nkv ? tk : nkv - 1], N);
-    } else {
-      return tk < N ? tk : N - 1;
+  // `lane` fills stored chunk (lane % CPR) of row ii*RPI + lane / CPR.  Rows
+  // past the end of the key list repeat its last key (their scores are masked).
+  auto load_rows = [&](int j, int (&rows)[UPW]) {
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+      const int tbase = j * BK + (w + NW * u) * GE::RPI;
+      if constexpr (SPARSE) {
+        int r = 0;
+#pragma unroll
+        for (int rr = 0; rr < GE::RPI; ++rr) {
+          const int v = kvidx[min(tbase + rr, nkv - 1)];   // wave-uniform: scalar load
+          r = (lane / GE::CPR == rr) ? v : r;
+        }
+        rows[u] = clamp_index(r, N);
+      } else {
+        rows[u] = min(tbase + lane / GE::CPR, N - 1);
+      }
     }
   };
-  int rows_next[UPW];
-  auto issue = [&](int j, int stage, bool with_v) {
+  auto issue = [&](int stage, const int (&rows)[UPW], bool with_v) {
     char* kt = lds + stage * STAGE;
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
-      const int t = tile_row_of(u);
-      const int c = (lane % GE::CPR) ^ GE::swz(t);
-      const size_t off = (size_t)rows_next[u] * D + 8 * c;
       const int ii = w + NW * u;
+      const int t = ii * GE::RPI + lane / GE::CPR;
+      const int c = (lane % GE::CPR) ^ GE::swz(t);
+      const size_t off = (size_t)rows[u] * D + 8 * c;
       __builtin_amdgcn_global_load_lds(kh + off, (lds_void*)(kt + ii * 1024), 16, 0, 0);
       if (with_v) __builtin_amdgcn_global_load_lds(vh + off, (lds_void*)(kt + GE::TILE + ii * 1024), 16, 0, 0);
     }
-    (void)j;
   };
-  auto fetch_rows = [&](int j) {
-    if (j < nt) {
-#pragma unroll
-      for (int u = 0; u < UPW; ++u) rows_next[u] = source_row(j, u);
+  // Waits until tile j has landed; the tiles after it may stay in flight.
+  auto wait_tile = [&](int j, bool with_v) {
+    if constexpr (NST == 3) {
+      if (j + 1 < nt) {
+        if (with_v)
+          wait_vm<2 * UPW>();
+        else
+          wait_vm<UPW>();
+        return;
+      }
     }
+    wait_vm<0>();
   };
 
   // K operand (A of S^T, or B of S): tile row 16 tb + lr, chunk lq + 4 kk
@@ -156,13 +186,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     const int c = (lq + 4 * kk) ^ GE::swz(t);
     return *reinterpret_cast<const bf16x8*>(kt + t * GE::ROWB + 16 * c);
   };
-  // V^T operand for output column block db: two transposed 8-byte reads of
-  // tokens 4 lq + lr/4 (+16), dims 16 db + 4 (lr % 4) ..
-  auto vfrag = [&](const char* vt, int db) -> bf16x8 {
+  // V^T operand of 32-token chunk kc for output column block db: two
+  // transposed 8-byte reads of tokens 32 kc + 4 lq + lr/4 (+16), dims
+  // 16 db + 4 (lr % 4) ..
+  auto vfrag = [&](const char* vt, int kc, int db) -> bf16x8 {
     uint2 x[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int t = 16 * hh + 4 * lq + (lr >> 2);
+      const int t = 32 * kc + 16 * hh + 4 * lq + (lr >> 2);
       const int c = (2 * db + ((lr & 3) >> 1)) ^ GE::swz(t);
       const char* p = vt + t * GE::ROWB + 16 * c + 8 * (lr & 1);
       x[hh] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p));
@@ -179,39 +210,44 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  fetch_rows(0);
-  issue(0, 0, true);
-  fetch_rows(1);
-  for (int j = 0; j < nt; ++j) {
-    wait_vm();
-    __syncthreads();
-    if (j + 1 < nt) {
-      issue(j + 1, (j + 1) & 1, true);
-      fetch_rows(j + 2);
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0) {
+    if (s0 < nt) {
+      int rows[UPW];
+      load_rows(s0, rows);
+      issue(s0, rows, true);
     }
-    const char* kt = lds + (j & 1) * STAGE;
+  }
+  for (int j = 0; j < nt; ++j) {
+    const int jn = j + NST - 1;
+    int rows[UPW];
+    if (jn < nt) load_rows(jn, rows);
+    wait_tile(j, true);
+    __syncthreads();
+    if (jn < nt) issue(jn % NST, rows, true);
+    const char* kt = lds + (j % NST) * STAGE;
     const char* vt = kt + GE::TILE;
 
     // S^T[token][row]: lane holds tokens 16 tb + 4 lq + i of row 16 rb + lr
-    f32x4 s[2][2];
+    f32x4 s[TB][2];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) s[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
+      for (int tb = 0; tb < TB; ++tb) {
         const bf16x8 kf = kfrag(kt, tb, kk);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           s[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][kk], s[tb][rb], 0, 0, 0);
       }
     }
-    const int vcols = nkv - j * BKV;
-    if (vcols < BKV) {
+    const int vcols = nkv - j * BK;
+    if (vcols < BK) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (16 * tb + 4 * lq + i >= vcols) {
@@ -224,11 +260,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     bool need = false;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float m = fmaxf(fmaxf(s[0][rb][0], s[0][rb][1]), fmaxf(s[0][rb][2], s[0][rb][3]));
-      m = fmaxf(m, fmaxf(fmaxf(s[1][rb][0], s[1][rb][1]), fmaxf(s[1][rb][2], s[1][rb][3])));
-      m = fmaxf(m, xor_shfl(m, 16));
-      m = fmaxf(m, xor_shfl(m, 32));
-      mx[rb] = m * sl2;
+      float m = s[0][rb][0];
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, s[tb][rb][i]);
+      mx[rb] = quad_rows_max(m) * sl2;
       need |= mx[rb] > m_run[rb] + kRescaleSlack;
     }
     if (__ballot(need) != 0ull) {
@@ -242,12 +279,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int db = 0; db < DB; ++db) oacc[db][rb] *= alpha;
       }
     }
-    bf16x8 pf[2];
+    bf16x8 pf[KC][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float ls = 0.f;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = fast_exp2(fmaf(s[tb][rb][i], sl2, -m_run[rb]));
@@ -255,26 +292,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
           ls += p;
         }
       l_run[rb] += ls;
-      pf[rb] = as_bf16x8(make_uint4(pack_bf16x2(s[0][rb][0], s[0][rb][1]), pack_bf16x2(s[0][rb][2], s[0][rb][3]),
-                                    pack_bf16x2(s[1][rb][0], s[1][rb][1]), pack_bf16x2(s[1][rb][2], s[1][rb][3])));
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        pf[kc][rb] = as_bf16x8(make_uint4(pack_bf16x2(s[2 * kc][rb][0], s[2 * kc][rb][1]),
+                                          pack_bf16x2(s[2 * kc][rb][2], s[2 * kc][rb][3]),
+                                          pack_bf16x2(s[2 * kc + 1][rb][0], s[2 * kc + 1][rb][1]),
+                                          pack_bf16x2(s[2 * kc + 1][rb][2], s[2 * kc + 1][rb][3])));
     }
 
     // O^T[dim][row] += V^T P^T
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const bf16x8 vf = vfrag(vt, db);
+    for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], oacc[db][rb], 0, 0, 0);
-    }
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 vf = vfrag(vt, kc, db);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kc][rb], oacc[db][rb], 0, 0, 0);
+      }
   }
 
   // ---- epilogue ---------------------------------------------------------
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    float l = l_run[rb];
-    l += xor_shfl(l, 16);
-    l += xor_shfl(l, 32);
+    const float l = quad_rows_sum(l_run[rb]);
     const float inv = 1.0f / l;
     const int r = 32 * w + 16 * rb + lr;
     const int p = row0 + r;
@@ -319,8 +360,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   const int wpg = a.G / 32;   // waves per group
   const int gpt = BM / a.G;   // groups per tile
   auto flush = [&](int j) {   // cross-wave sums of tile j -> colsum
-    for (int t = tid; t < gpt * BKV; t += NW * 64) {
-      const int gi = t / BKV, col = t % BKV, tok = j * BKV + col;
+    for (int t = tid; t < gpt * BK; t += NW * 64) {
+      const int gi = t / BK, col = t % BK, tok = j * BK + col;
       const int g = row0 / a.G + gi;
       if (tok < N && g < a.ng) {
         float sum = 0.f;
@@ -329,28 +370,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  fetch_rows(0);
-  issue(0, 0, false);
-  fetch_rows(1);
-  for (int j = 0; j < nt; ++j) {
-    wait_vm();
-    __syncthreads();
-    if (j + 1 < nt) {
-      issue(j + 1, (j + 1) & 1, false);
-      fetch_rows(j + 2);
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0) {
+    if (s0 < nt) {
+      int rows[UPW];
+      load_rows(s0, rows);
+      issue(s0, rows, false);
     }
+  }
+  for (int j = 0; j < nt; ++j) {
+    const int jn = j + NST - 1;
+    int rows[UPW];
+    if (jn < nt) load_rows(jn, rows);
+    wait_tile(j, false);
+    __syncthreads();
+    if (jn < nt) issue(jn % NST, rows, false);
     if (j > 0) flush(j - 1);
-    const char* kt = lds + (j & 1) * STAGE;
+    const char* kt = lds + (j % NST) * STAGE;
     // S[row][token]: lane holds rows 16 rb + 4 lq + i of token 16 tb + lr
-    f32x4 s[2][2];
+    f32x4 s[2][TB];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) s[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tb = 0; tb < TB; ++tb) s[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
+      for (int tb = 0; tb < TB; ++tb) {
         const bf16x8 kf = kfrag(kt, tb, kk);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -358,14 +404,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+    for (int tb = 0; tb < TB; ++tb) {
       float cs = 0.f;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cs += fast_exp2(fmaf(s[rb][tb][i], sl2, nlse[rb][i]));
-      cs += xor_shfl(cs, 16);
-      cs += xor_shfl(cs, 32);
+      cs = quad_rows_sum(cs);
       if (lq == 0) red[j & 1][w][16 * tb + lr] = cs;
     }
   }
@@ -380,7 +425,8 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   const long long nblocks = (long long)a.nheads * tiles;
   if (nblocks == 0) return hipSuccess;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, MODE>), dim3((unsigned)nblocks), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, MODE, MCS_BK, MCS_NST>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
+                     s, a);
   return hipGetLastError();
 }
 

@@ -53,6 +53,22 @@ __device__ __forceinline__ float xor_shfl(float v, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane ^ mask) << 2), __float_as_int(v)));
 }
 
+// Max / sum over the four lanes {l, l^16, l^32, l^48} (the four 16-lane rows
+// of the wave), with the gfx950 row-swap permutes: each swap returns the
+// lane's own value and its partner's, in some order.
+__device__ __forceinline__ float quad_rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 t = {(__bf16)lo, (__bf16)hi};

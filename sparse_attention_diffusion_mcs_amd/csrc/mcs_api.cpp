@@ -17,7 +17,10 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr uint64_t kAlign = 256;
-constexpr int kXcdRun = 16;  // consecutive work items per XCD per round
+#ifndef MCS_XCD_RUN
+#define MCS_XCD_RUN 128
+#endif
+constexpr int kXcdRun = MCS_XCD_RUN;  // consecutive work items per XCD per round
 
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 

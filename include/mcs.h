@@ -55,7 +55,7 @@ extern "C" {
 #define MCS_VERSION 1
 #define MCS_META_VERSION 1
 #define MCS_HASH_BITS 8
-#define MCS_MAX_SEQ_LEN (1 << 24)
+#define MCS_MAX_SEQ_LEN (1 << 22)
 
 typedef enum mcs_status {
   MCS_SUCCESS = 0,

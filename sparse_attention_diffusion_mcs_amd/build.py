@@ -23,6 +23,10 @@ SOURCES = ["attn_bf16.hip", "attn_f32.hip", "select.hip", "mcs_api.cpp"]
 # Packed fp32 VALU instructions are turned off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
+# The bf16 attention kernels never produce NaN (masked scores are -inf), so
+# max/min need no NaN quieting.
+FILE_FLAGS = {"attn_bf16.hip": ["-fno-honor-nans"]}
+
 
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -35,7 +39,7 @@ def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj, "-O3", "-fPIC", "-std=c++17",
            f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-Wno-unused-command-line-argument"] + DEVICE_FLAGS
+           "-Wno-unused-command-line-argument"] + DEVICE_FLAGS + FILE_FLAGS.get(src, [])
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

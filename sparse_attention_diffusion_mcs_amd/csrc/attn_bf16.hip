@@ -15,14 +15,16 @@
 // group's gathered KV tiles; in the dense modes it is 128 rows (4 waves).
 //
 // KV tiles of BK tokens are gathered straight from global memory into LDS with
-// global_load_lds_dwordx4 (no staging registers) through an NST-deep ring of
-// LDS stages, one barrier per tile.  The kept-key indices of a tile are
-// wave-uniform data and are read with scalar loads, so they never queue behind
-// the tile copies on the vector-memory counter.  Rows are stored with an XOR
-// swizzle of their 16-byte chunks chosen so that both LDS read patterns are
-// free of bank conflicts: the K operand (16-byte reads, 16 rows per
+// buffer_load_dwordx4 ... lds (no staging registers, 32-bit row offsets into
+// the head's K and V) into two LDS stages, one barrier per tile.  The two
+// stages are distinct LDS objects and the tile loop is unrolled by two, so the
+// compiler can see that a tile's reads never alias the copy into the other
+// stage and does not wait for that copy before reading.  Rows are stored with
+// an XOR swizzle of their 16-byte chunks chosen so that both LDS read patterns
+// are free of bank conflicts: the K operand (16-byte reads, 16 rows per
 // quarter-wave) and the V operand, read transposed with ds_read_b64_tr_b16
-// (8 rows x 2 chunks per half-wave).
+// (8 rows x 2 chunks per half-wave).  All operand reads of a tile are issued
+// before its first MFMA so that their latency overlaps.
 //
 // Each wave computes S^T = K Q^T, so every lane holds scores of one query row;
 // the row max needs one in-lane pass and two row-swap permutes, and the
@@ -33,17 +35,11 @@
 #include "device.h"
 #include "launch.h"
 
-#ifndef MCS_BK
-#define MCS_BK 32
-#endif
-#ifndef MCS_NST
-#define MCS_NST 2
-#endif
-
 namespace mcs {
 namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -72,7 +68,7 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, int NW, int MODE, int BK, int NST>
+template <int D, int NW, int MODE, int BK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   using GE = Geo<D, BK>;
   constexpr int BM = NW * 32;
@@ -82,11 +78,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KC = BK / 32;                // 32-token chunks of the PV product
   constexpr int UPW = GE::NI / NW;           // loads per tensor per tile per wave
   constexpr bool SPARSE = (MODE == MODE_REUSE || MODE == MODE_RESINIT);
+  // The selection step's outputs (dense output and selection-time sparse
+  // output) feed the cached residual, which every reuse step adds back; they
+  // carry the probabilities into the PV product as bf16 hi + lo parts so that
+  // the residual holds ~16-bit probabilities instead of 8-bit ones.
+  constexpr bool PRECISE_PV = (MODE == MODE_SELECT || MODE == MODE_RESINIT);
   constexpr int STAGE = 2 * GE::TILE;        // K tile + V tile
   static_assert(UPW * NW == GE::NI, "tile loads must split evenly over the waves");
-  static_assert(NST == 2 || NST == 3, "2 or 3 pipeline stages");
 
-  __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
   __shared__ float red[MODE == MODE_SELECT ? 2 : 1][NW][BK];
   __shared__ float lse_s[MODE == MODE_SELECT ? BM : 1];
 
@@ -105,6 +106,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + hoff;
   const uint16_t* vh = static_cast<const uint16_t*>(a.v) + hoff;
   const int32_t* permh = a.perm ? a.perm + (size_t)h * N : nullptr;
+  // Buffer resources over this head's K and V (N rows of ROWB bytes).
+  const int head_bytes = N * GE::ROWB;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, head_bytes, kBufferConfig);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, head_bytes, kBufferConfig);
 
   int nkv = N;
   const int32_t* kvidx = nullptr;
@@ -137,47 +142,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   // Load u of this wave covers tile rows ii*RPI .. +RPI-1 (ii = w + NW u); lane
   // `lane` fills stored chunk (lane % CPR) of row ii*RPI + lane / CPR.  Rows
   // past the end of the key list repeat its last key (their scores are masked).
-  auto load_rows = [&](int j, int (&rows)[UPW]) {
+  // The source row of each load is fetched one tile ahead and only turned into
+  // a byte offset when the copy is issued, so that nothing waits on the fetch
+  // (and, through the in-order memory counter, on the copy issued before it).
+  int src_row[UPW];
+  auto fetch_rows = [&](int j) {
+    if (j < nt) {
 #pragma unroll
-    for (int u = 0; u < UPW; ++u) {
-      const int tbase = j * BK + (w + NW * u) * GE::RPI;
-      if constexpr (SPARSE) {
-        int r = 0;
-#pragma unroll
-        for (int rr = 0; rr < GE::RPI; ++rr) {
-          const int v = kvidx[min(tbase + rr, nkv - 1)];   // wave-uniform: scalar load
-          r = (lane / GE::CPR == rr) ? v : r;
-        }
-        rows[u] = clamp_index(r, N);
-      } else {
-        rows[u] = min(tbase + lane / GE::CPR, N - 1);
+      for (int u = 0; u < UPW; ++u) {
+        const int t = (w + NW * u) * GE::RPI + lane / GE::CPR;
+        const int tk = min(j * BK + t, nkv - 1);
+        src_row[u] = SPARSE ? kvidx[tk] : tk;
       }
     }
   };
-  auto issue = [&](int stage, const int (&rows)[UPW], bool with_v) {
-    char* kt = lds + stage * STAGE;
+  auto issue = [&](char* stage, bool with_v) {
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
       const int ii = w + NW * u;
       const int t = ii * GE::RPI + lane / GE::CPR;
-      const int c = (lane % GE::CPR) ^ GE::swz(t);
-      const size_t off = (size_t)rows[u] * D + 8 * c;
-      __builtin_amdgcn_global_load_lds(kh + off, (lds_void*)(kt + ii * 1024), 16, 0, 0);
-      if (with_v) __builtin_amdgcn_global_load_lds(vh + off, (lds_void*)(kt + GE::TILE + ii * 1024), 16, 0, 0);
+      const int off = clamp_index(src_row[u], N) * GE::ROWB + 16 * ((lane % GE::CPR) ^ GE::swz(t));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + ii * 1024), 16, off, 0, 0, 0);
+      if (with_v)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + GE::TILE + ii * 1024), 16, off, 0, 0, 0);
     }
-  };
-  // Waits until tile j has landed; the tiles after it may stay in flight.
-  auto wait_tile = [&](int j, bool with_v) {
-    if constexpr (NST == 3) {
-      if (j + 1 < nt) {
-        if (with_v)
-          wait_vm<2 * UPW>();
-        else
-          wait_vm<UPW>();
-        return;
-      }
-    }
-    wait_vm<0>();
   };
 
   // K operand (A of S^T, or B of S): tile row 16 tb + lr, chunk lq + 4 kk
@@ -186,19 +174,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     const int c = (lq + 4 * kk) ^ GE::swz(t);
     return *reinterpret_cast<const bf16x8*>(kt + t * GE::ROWB + 16 * c);
   };
-  // V^T operand of 32-token chunk kc for output column block db: two
-  // transposed 8-byte reads of tokens 32 kc + 4 lq + lr/4 (+16), dims
+  // Half of the V^T operand of 32-token chunk kc for output column block db:
+  // a transposed 8-byte read of token 32 kc + 16 hh + 4 lq + lr/4, dims
   // 16 db + 4 (lr % 4) ..
-  auto vfrag = [&](const char* vt, int kc, int db) -> bf16x8 {
-    uint2 x[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int t = 32 * kc + 16 * hh + 4 * lq + (lr >> 2);
-      const int c = (2 * db + ((lr & 3) >> 1)) ^ GE::swz(t);
-      const char* p = vt + t * GE::ROWB + 16 * c + 8 * (lr & 1);
-      x[hh] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p));
-    }
-    return as_bf16x8(make_uint4(x[0].x, x[0].y, x[1].x, x[1].y));
+  auto vhalf = [&](const char* vt, int kc, int db, int hh) -> uint2 {
+    const int t = 32 * kc + 16 * hh + 4 * lq + (lr >> 2);
+    const int c = (2 * db + ((lr & 3) >> 1)) ^ GE::swz(t);
+    const char* p = vt + t * GE::ROWB + 16 * c + 8 * (lr & 1);
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p));
   };
 
   // ---- pass 1: online-softmax attention over the KV tiles ---------------
@@ -210,23 +193,26 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int s0 = 0; s0 < NST - 1; ++s0) {
-    if (s0 < nt) {
-      int rows[UPW];
-      load_rows(s0, rows);
-      issue(s0, rows, true);
-    }
-  }
-  for (int j = 0; j < nt; ++j) {
-    const int jn = j + NST - 1;
-    int rows[UPW];
-    if (jn < nt) load_rows(jn, rows);
-    wait_tile(j, true);
+  auto attend_tile = [&](int j, const char* cur, char* nxt) {
+    wait_vm<0>();
     __syncthreads();
-    if (jn < nt) issue(jn % NST, rows, true);
-    const char* kt = lds + (j % NST) * STAGE;
-    const char* vt = kt + GE::TILE;
+    if (j + 1 < nt) {
+      issue(nxt, true);
+      fetch_rows(j + 2);
+    }
+    const char* vt = cur + GE::TILE;
+    bf16x8 kf[KK][TB];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) kf[kk][tb] = kfrag(cur, tb, kk);
+    uint2 vr[KC][DB][2];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) vr[kc][db][hh] = vhalf(vt, kc, db, hh);
 
     // S^T[token][row]: lane holds tokens 16 tb + 4 lq + i of row 16 rb + lr
     f32x4 s[TB][2];
@@ -235,15 +221,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) s[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        const bf16x8 kf = kfrag(kt, tb, kk);
+      for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
-          s[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][kk], s[tb][rb], 0, 0, 0);
-      }
-    }
+          s[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk][tb], qf[rb][kk], s[tb][rb], 0, 0, 0);
     const int vcols = nkv - j * BK;
     if (vcols < BK) {
 #pragma unroll
@@ -264,14 +247,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, s[tb][rb][i]);
+        for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, s[tb][rb][i]);
       mx[rb] = quad_rows_max(m) * sl2;
       need |= mx[rb] > m_run[rb] + kRescaleSlack;
     }
     if (__ballot(need) != 0ull) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const float mnew = fmaxf(m_run[rb], mx[rb]);
+        const float mnew = __builtin_fmaxf(m_run[rb], mx[rb]);
         const float alpha = fast_exp2(m_run[rb] - mnew);
         m_run[rb] = mnew;
         l_run[rb] *= alpha;
@@ -280,6 +263,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     bf16x8 pf[KC][2];
+    bf16x8 pl[PRECISE_PV ? KC : 1][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float ls = 0.f;
@@ -293,11 +277,26 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
         }
       l_run[rb] += ls;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        pf[kc][rb] = as_bf16x8(make_uint4(pack_bf16x2(s[2 * kc][rb][0], s[2 * kc][rb][1]),
-                                          pack_bf16x2(s[2 * kc][rb][2], s[2 * kc][rb][3]),
-                                          pack_bf16x2(s[2 * kc + 1][rb][0], s[2 * kc + 1][rb][1]),
-                                          pack_bf16x2(s[2 * kc + 1][rb][2], s[2 * kc + 1][rb][3])));
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint4 hi = make_uint4(pack_bf16x2(s[2 * kc][rb][0], s[2 * kc][rb][1]),
+                                    pack_bf16x2(s[2 * kc][rb][2], s[2 * kc][rb][3]),
+                                    pack_bf16x2(s[2 * kc + 1][rb][0], s[2 * kc + 1][rb][1]),
+                                    pack_bf16x2(s[2 * kc + 1][rb][2], s[2 * kc + 1][rb][3]));
+        pf[kc][rb] = as_bf16x8(hi);
+        if constexpr (PRECISE_PV) {
+          // low part p - bf16(p), so that P = hi + lo to ~16 significant bits
+          const uint32_t h4[4] = {hi.x, hi.y, hi.z, hi.w};
+          uint32_t lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x4 src = s[2 * kc + (e >> 1)][rb];
+            const float r0 = src[2 * (e & 1)] - __uint_as_float(h4[e] << 16);
+            const float r1 = src[2 * (e & 1) + 1] - __uint_as_float(h4[e] & 0xffff0000u);
+            lo[e] = pack_bf16x2(r0, r1);
+          }
+          pl[kc][rb] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+        }
+      }
     }
 
     // O^T[dim][row] += V^T P^T
@@ -305,11 +304,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = vfrag(vt, kc, db);
+        const bf16x8 vf = as_bf16x8(
+            make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y));
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb) {
           oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kc][rb], oacc[db][rb], 0, 0, 0);
+          if constexpr (PRECISE_PV)
+            oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[kc][rb], oacc[db][rb], 0, 0, 0);
+        }
       }
+  };
+
+  fetch_rows(0);
+  if (nt > 0) issue(st0, true);
+  fetch_rows(1);
+  for (int j = 0; j < nt; j += 2) {
+    attend_tile(j, st0, st1);
+    if (j + 1 < nt) attend_tile(j + 1, st1, st0);
   }
 
   // ---- epilogue ---------------------------------------------------------
@@ -370,23 +381,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     }
   };
-#pragma unroll
-  for (int s0 = 0; s0 < NST - 1; ++s0) {
-    if (s0 < nt) {
-      int rows[UPW];
-      load_rows(s0, rows);
-      issue(s0, rows, false);
-    }
-  }
-  for (int j = 0; j < nt; ++j) {
-    const int jn = j + NST - 1;
-    int rows[UPW];
-    if (jn < nt) load_rows(jn, rows);
-    wait_tile(j, false);
+  auto score_tile = [&](int j, const char* cur, char* nxt) {
+    wait_vm<0>();
     __syncthreads();
-    if (jn < nt) issue(jn % NST, rows, false);
+    if (j + 1 < nt) {
+      issue(nxt, false);
+      fetch_rows(j + 2);
+    }
     if (j > 0) flush(j - 1);
-    const char* kt = lds + (j % NST) * STAGE;
+    bf16x8 kf[KK][TB];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) kf[kk][tb] = kfrag(cur, tb, kk);
     // S[row][token]: lane holds rows 16 rb + 4 lq + i of token 16 tb + lr
     f32x4 s[2][TB];
 #pragma unroll
@@ -394,15 +401,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) s[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        const bf16x8 kf = kfrag(kt, tb, kk);
+      for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
-          s[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rb][kk], kf, s[rb][tb], 0, 0, 0);
-      }
-    }
+          s[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rb][kk], kf[kk][tb], s[rb][tb], 0, 0, 0);
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       float cs = 0.f;
@@ -413,9 +417,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       cs = quad_rows_sum(cs);
       if (lq == 0) red[j & 1][w][16 * tb + lr] = cs;
     }
+  };
+  fetch_rows(0);
+  if (nt > 0) issue(st0, false);
+  fetch_rows(1);
+  for (int j = 0; j < nt; j += 2) {
+    score_tile(j, st0, st1);
+    if (j + 1 < nt) score_tile(j + 1, st1, st0);
   }
   __syncthreads();
   if (nt > 0) flush(nt - 1);
+}
+
+// KV tile size per workgroup shape: 4-wave tiles amortise each tile over more
+// rows and run best with 64-token tiles; 2-wave groups keep 32-token tiles so
+// that more workgroups fit in LDS.
+template <int NW>
+constexpr int tile_tokens() {
+#ifdef MCS_BK
+  return MCS_BK;
+#else
+  return NW == 4 ? 64 : 32;
+#endif
 }
 
 template <int D, int NW, int MODE>
@@ -425,7 +448,7 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   const long long nblocks = (long long)a.nheads * tiles;
   if (nblocks == 0) return hipSuccess;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, MODE, MCS_BK, MCS_NST>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, MODE, tile_tokens<NW>()>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
                      s, a);
   return hipGetLastError();
 }

@@ -138,9 +138,10 @@ def test_reuse_on_selection_inputs_reproduces_dense():
     out = mcs.sparse_attn(*p.dev[0], meta, scale=sc)
     torch.cuda.synchronize()
     a, b = to_np(out), to_np(od)
-    # O_sparse + (O_dense - O_sparse) equals O_dense up to float32 rounding,
-    # then both are rounded to bf16: at most one bf16 step apart
-    assert np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-3)) <= 2 ** -7
+    # O_sparse + (O_dense - O_sparse) returns the dense output; what remains is
+    # the difference between the reuse kernel's bf16 probabilities and the
+    # selection step's finer ones, within the bf16 output tolerance
+    assert_close(a, b.astype(np.float64), "bf16", "reuse on selection inputs vs selection dense output")
     for h in range(H):
         q, k, v = p.heads_np[(h, 0)]
         assert_close(a[h], orc.dense_attention(q, k, v, sc), "bf16", f"head {h}")

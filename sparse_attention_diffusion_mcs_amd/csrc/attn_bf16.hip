@@ -63,6 +63,11 @@ struct Geo {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -112,11 +117,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, head_bytes, kBufferConfig);
 
   int nkv = N;
-  const int32_t* kvidx = nullptr;
+  __amdgpu_buffer_rsrc_t ridx;  // the group's kept keys; reads past the end return 0 (row 0)
   if constexpr (SPARSE) {
     long long start;
     group_keys(a.keep, a.idx_start, h, tile, N, a.total_idx, &start, &nkv);
-    kvidx = a.idx + start;
+    ridx = __builtin_amdgcn_make_buffer_rsrc((void*)(a.idx + start), (short)0, nkv * 4, kBufferConfig);
   }
   const int nt = (nkv + BK - 1) / BK;
   const float sl2 = a.scale * kLog2e;
@@ -141,18 +146,26 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   // ---- tile loads -------------------------------------------------------
   // Load u of this wave covers tile rows ii*RPI .. +RPI-1 (ii = w + NW u); lane
   // `lane` fills stored chunk (lane % CPR) of row ii*RPI + lane / CPR.  Rows
-  // past the end of the key list repeat its last key (their scores are masked).
+  // past the end of the key list load key 0 (their scores are masked).
   // The source row of each load is fetched one tile ahead and only turned into
   // a byte offset when the copy is issued, so that nothing waits on the fetch
   // (and, through the in-order memory counter, on the copy issued before it).
   int src_row[UPW];
+  int chunk_off[UPW];
+#pragma unroll
+  for (int u = 0; u < UPW; ++u) {
+    const int t = (w + NW * u) * GE::RPI + lane / GE::CPR;
+    chunk_off[u] = 16 * ((lane % GE::CPR) ^ GE::swz(t));
+  }
   auto fetch_rows = [&](int j) {
     if (j < nt) {
 #pragma unroll
       for (int u = 0; u < UPW; ++u) {
         const int t = (w + NW * u) * GE::RPI + lane / GE::CPR;
-        const int tk = min(j * BK + t, nkv - 1);
-        src_row[u] = SPARSE ? kvidx[tk] : tk;
+        if constexpr (SPARSE)
+          src_row[u] = __builtin_amdgcn_raw_buffer_load_b32(ridx, 4 * t, 4 * BK * j, 0);
+        else
+          src_row[u] = j * BK + t;
       }
     }
   };
@@ -160,8 +173,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
       const int ii = w + NW * u;
-      const int t = ii * GE::RPI + lane / GE::CPR;
-      const int off = clamp_index(src_row[u], N) * GE::ROWB + 16 * ((lane % GE::CPR) ^ GE::swz(t));
+      const int row = (int)min((unsigned)src_row[u], (unsigned)(N - 1));
+      const int off = (row * GE::ROWB) | chunk_off[u];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + ii * 1024), 16, off, 0, 0, 0);
       if (with_v)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + GE::TILE + ii * 1024), 16, off, 0, 0, 0);
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto attend_tile = [&](int j, const char* cur, char* nxt) {
+  auto attend_tile = [&](int j, const char* cur, char* nxt, auto masked) {
     wait_vm<0>();
     __syncthreads();
     if (j + 1 < nt) {
@@ -227,8 +240,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           s[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk][tb], qf[rb][kk], s[tb][rb], 0, 0, 0);
-    const int vcols = nkv - j * BK;
-    if (vcols < BK) {
+    if constexpr (decltype(masked)::value) {  // the ragged last tile only
+      const int vcols = nkv - j * BK;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -318,9 +331,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   fetch_rows(0);
   if (nt > 0) issue(st0, true);
   fetch_rows(1);
-  for (int j = 0; j < nt; j += 2) {
-    attend_tile(j, st0, st1);
-    if (j + 1 < nt) attend_tile(j + 1, st1, st0);
+  {
+    const Flag<false> full;
+    const Flag<true> ragged;
+    const int nfull = (nkv % BK) ? nt - 1 : nt;   // tiles that need no masking
+    int j = 0;
+    for (; j + 1 < nfull; j += 2) {
+      attend_tile(j, st0, st1, full);
+      attend_tile(j + 1, st1, st0, full);
+    }
+    if (j < nfull) attend_tile(j++, st0, st1, full);
+    if (j < nt) {
+      if (j & 1)
+        attend_tile(j, st1, st0, ragged);
+      else
+        attend_tile(j, st0, st1, ragged);
+    }
   }
 
   // ---- epilogue ---------------------------------------------------------

@@ -455,15 +455,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   if (nt > 0) flush(nt - 1);
 }
 
-// KV tile size per workgroup shape: 4-wave tiles amortise each tile over more
-// rows and run best with 64-token tiles; 2-wave groups keep 32-token tiles so
-// that more workgroups fit in LDS.
-template <int NW>
+// KV tile size: 32 tokens at d = 128 (the batched K and V operand reads of a
+// 64-token tile would not fit the register budget), 64 tokens at d = 64.
+template <int D>
 constexpr int tile_tokens() {
 #ifdef MCS_BK
   return MCS_BK;
 #else
-  return NW == 4 ? 64 : 32;
+  return D == 128 ? 32 : 64;
 #endif
 }
 
@@ -474,7 +473,7 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   const long long nblocks = (long long)a.nheads * tiles;
   if (nblocks == 0) return hipSuccess;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, MODE, tile_tokens<NW>()>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, MODE, tile_tokens<D>()>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
                      s, a);
   return hipGetLastError();
 }

@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--keep", type=float, default=None, help="override the keep fraction")
     ap.add_argument("--group", type=int, default=None, help="override the group size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 1 GiB device-to-device copy first (a known-size reference for HBM counters)")
     ap.add_argument("--cpu-groups", type=int, default=96, help="oracle groups sampled per sampled head")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 8))
     return ap.parse_args()
@@ -193,6 +195,13 @@ def main():
     t0 = time.time()
     X = generate(w, range(0, T + 1), args.threads)
     torch.cuda.synchronize()
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"inputs generated and resident ({time.time() - t0:.1f} s)")
 
     proj = hash_projections(0, w.wid, d)

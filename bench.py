@@ -15,7 +15,12 @@ per denoising step, the roofline of the reuse kernel measured with HIP events
 on the launch stream, and the CPU oracle timed on a bounded sample of the same
 workload on this host.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+With --sweep (workload 5) the line also carries the denoising-loop sweep:
+for every keep fraction and group size, a 30-step loop with re-selection every
+10 steps, its amortised time against 30 dense steps and the relative L2 error
+of every step's output against dense attention on that step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--sweep]
 """
 
 from __future__ import annotations
@@ -58,8 +63,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (a known-size reference for HBM counters)")
-    ap.add_argument("--cpu-groups", type=int, default=96, help="oracle groups sampled per sampled head")
+    ap.add_argument("--cpu-groups", type=int, default=288, help="oracle groups sampled per sampled head")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 8))
+    ap.add_argument("--sweep", action="store_true",
+                    help="workload 5 only: add the keep x group denoising-loop sweep to the result")
     return ap.parse_args()
 
 
@@ -172,6 +179,81 @@ def cpu_baseline(w, keeps, T, scale, n_groups, seed=0):
     }
 
 
+def rel_l2(a, b):
+    import torch
+    return float(torch.linalg.vector_norm(a.float() - b.float()) / torch.linalg.vector_norm(b.float()))
+
+
+def sweep(w, X, threads, scale):
+    """Denoising-loop sweep: for each (keep, G), steps 0..S-1 with selection on
+    the steps divisible by the re-selection interval and reuse on the others;
+    every step's output is compared with dense attention on that step."""
+    import torch
+
+    import sparse_attention_diffusion_mcs_amd as mcs
+
+    S, R = w.sweep["steps"], w.reselect
+    H, N, d = w.heads, w.seq_len, w.head_dim
+    stream = torch.cuda.current_stream()
+    proj = hash_projections(0, w.wid, d)
+    dense = {}
+    dense_ms = []
+    for t in range(S):  # dense outputs of every step (the fidelity reference), each timed
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dense[t] = mcs.dense_attn(*X[t], scale=scale)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms.append(e0.elapsed_time(e1))
+    dense_med = float(np.median(dense_ms[1:]))
+    points = []
+    for G in w.sweep["group"]:
+        for frac in w.sweep["keep"]:
+            wk = w.with_(keep_frac=(frac,), group=G)
+            keeps = wk.keeps()
+            ws = torch.empty(mcs.workspace_bytes(X[0][0], G), dtype=torch.uint8, device="cuda")
+            mb = torch.empty(int(mcs.meta_layout(H, N, d, 1, G, keeps).bytes), dtype=torch.uint8, device="cuda")
+            out = torch.empty_like(X[0][0])
+            mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws)  # warm-up
+            torch.cuda.synchronize()
+            sel_ms, reuse_ms, err = [], [], []
+            meta = None
+            for t in range(S):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                if t % R == 0:
+                    e0.record(stream)
+                    meta, od = mcs.select(*X[t], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws,
+                                          return_dense=True)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    sel_ms.append(e0.elapsed_time(e1))
+                    err.append(rel_l2(od, dense[t]))
+                else:
+                    e0.record(stream)
+                    mcs.sparse_attn(*X[t], meta, out=out, scale=scale)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    reuse_ms.append(e0.elapsed_time(e1))
+                    err.append(rel_l2(out, dense[t]))
+            total = float(np.sum(sel_ms) + np.sum(reuse_ms))
+            reuse_err = [e for t, e in enumerate(err) if t % R != 0]
+            points.append({
+                "keep_frac": frac, "group": G, "keep": int(keeps[0]),
+                "select_ms": round(float(np.median(sel_ms)), 3),
+                "reuse_ms": round(float(np.mean(reuse_ms)), 4),
+                "amortised_vs_dense": round(total / (S * dense_med), 4),
+                "speedup_vs_dense": round(S * dense_med / total, 3),
+                "rel_l2_mean_all_steps": round(float(np.mean(err)), 6),
+                "rel_l2_mean_reuse_steps": round(float(np.mean(reuse_err)), 6),
+                "rel_l2_final": round(float(err[-1]), 6),
+                "meta_bytes": int(mb.numel()),
+            })
+            log(f"sweep G={G} keep={frac}: {points[-1]}")
+            del ws, mb, out, meta
+            torch.cuda.empty_cache()
+    return {"steps": S, "reselect_every": R, "dense_ms": round(dense_med, 4), "points": points}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -192,8 +274,12 @@ def main():
     H, N, d, G, T = w.heads, w.seq_len, w.head_dim, w.group, w.reuse_steps
     scale = float(np.float32(1.0 / math.sqrt(d)))
     log(f"workload {args.workload}: {describe(w, keeps)}")
+    if args.sweep and not w.sweep:
+        print("--sweep needs a workload with a sweep (workload 5)", file=sys.stderr)
+        sys.exit(2)
     t0 = time.time()
-    X = generate(w, range(0, T + 1), args.threads)
+    n_steps = max(T + 1, w.sweep["steps"] if args.sweep else 0)
+    X = generate(w, range(0, n_steps), args.threads)
     torch.cuda.synchronize()
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -261,6 +347,9 @@ def main():
         fid[str(t)] = round(float(torch.linalg.vector_norm(o_s - o_d) / torch.linalg.vector_norm(o_d)), 6)
     torch.cuda.synchronize()
 
+    sweep_res = sweep(w, X, args.threads, scale) if args.sweep else None
+    peak_mem = int(torch.cuda.max_memory_allocated())
+
     reuse_mean = float(np.mean(reuse_ms))
     sel_med = float(np.median(sel_ms))
     dense_med = float(np.median(dense_ms))
@@ -293,6 +382,8 @@ def main():
         "config": {"workload": describe(w, keeps), "heads": H, "seq_len": N, "head_dim": d, "group": G,
                    "keep": [int(x) for x in sorted(set(keeps.tolist()))], "reuse_steps": T},
         "reuse_ms_median": round(float(np.median(reuse_ms)), 4),
+        "reuse_ms_p10_p90": [round(float(np.percentile(reuse_ms, 10)), 4),
+                             round(float(np.percentile(reuse_ms, 90)), 4)],
         "dense_ms": round(dense_med, 4),
         "speedup_vs_dense": round(dense_med / reuse_mean, 3),
         "select_ms": round(sel_med, 3),
@@ -302,11 +393,19 @@ def main():
         "pct_bf16_peak_dense": round(100.0 * flops_dense / (dense_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "select_tflops": round(flops_select / (sel_med * 1e-3) / 1e12, 1),
         "fidelity_rel_l2_vs_dense": fid,
+        "meta_bytes": int(meta_buf.numel()),
+        "select_workspace_bytes": int(ws.numel()),
+        "peak_device_bytes": peak_mem,
         "roofline": {"kernel": f"attn_bf16_kernel<{d},{G // 32},REUSE> (reuse step)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": flops_reuse},
     }
+    if len(set(keeps.tolist())) > 1:
+        ks, cnt = np.unique(keeps, return_counts=True)
+        result["keep_histogram"] = {str(int(k)): int(c) for k, c in zip(ks, cnt)}
+    if sweep_res is not None:
+        result["sweep"] = sweep_res
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w, keeps, T, scale, args.cpu_groups)

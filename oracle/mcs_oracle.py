@@ -36,6 +36,13 @@ The pages give no formula, so the readings taken where they are silent are:
   (renormalised over them); the residual O_dense - O_sparse is kept per query
   (in sorted order) and added back unchanged on every reuse step.
 
+The ablations of the three failure modes the pages name ([ABS]: constraints
+of token grouping, inaccurate interaction selection, contributions lost with
+the discarded tokens; [BLOG] "MC-Sparse: three failure modes, one fix") swap
+one choice each: raster-order query groups instead of hash groups, whole
+64-token KV blocks ranked by their summed score instead of individual tokens,
+and no residual (the renormalised sparse output alone).
+
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
 
@@ -79,6 +86,11 @@ def hash_keys(q: np.ndarray, proj: np.ndarray) -> np.ndarray:
 def group_permutation(keys: np.ndarray) -> np.ndarray:
     """perm[p] = original token at sorted position p (stable sort by key)."""
     return np.argsort(np.asarray(keys, dtype=np.int64), kind="stable").astype(np.int32)
+
+
+def raster_permutation(n: int) -> np.ndarray:
+    """Ablation of the grouping: groups are runs of G tokens in raster order."""
+    return np.arange(n, dtype=np.int32)
 
 
 def group_ranges(n: int, group: int):
@@ -145,6 +157,28 @@ def topk_select(c: np.ndarray, k: int):
     return idx, gap
 
 
+def block_scores(c: np.ndarray, block: int) -> np.ndarray:
+    """Score of each run of `block` consecutive keys: the sum of the group's
+    key scores over the run (float64 [N / block])."""
+    c = np.asarray(c, dtype=np.float64)
+    if c.shape[0] % block:
+        raise ValueError(f"{c.shape[0]} keys do not split into blocks of {block}")
+    return c.reshape(-1, block).sum(axis=1)
+
+
+def topk_blocks(c: np.ndarray, k: int, block: int):
+    """Ablation of the selection granularity ([BLOG]: dropping whole blocks
+    evicts tokens one wanted to keep): keep the k / block key blocks with the
+    largest block scores (compared as float32, ties to the lower block), and
+    with them every key of those blocks.  Returns (idx ascending int32 [k],
+    gap between the kept and the first dropped block score, kept block ids)."""
+    if k % block:
+        raise ValueError(f"keep {k} is not a multiple of the block size {block}")
+    bidx, gap = topk_select(block_scores(c, block), k // block)
+    idx = (bidx.astype(np.int64)[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    return idx.astype(np.int32), gap, bidx
+
+
 def sparse_attention(q, k, v, idx, scale):
     """Attention of rows q over the kept keys idx only (renormalised)."""
     idx = np.asarray(idx, dtype=np.int64)
@@ -163,17 +197,25 @@ class GroupSelection:
     residual: np.ndarray    # o_dense - o_sparse, float64 [|g|, d]
 
 
-def select_group(q, k, v, rows, keep, scale) -> GroupSelection:
+def select_group(q, k, v, rows, keep, scale, kv_block=1, residual=True) -> GroupSelection:
     """Selection step for one query group ([ABS], [BLOG] "MC-Sparse: three
     failure modes, one fix"): exact dense rows, group scores, top-k, sparse
-    rows over the kept keys and the residual between the two."""
+    rows over the kept keys and the residual between the two.
+
+    Ablations: kv_block > 1 keeps whole key blocks (topk_blocks); residual
+    False caches a zero residual, so reuse returns the renormalised sparse
+    output alone."""
     rows = np.asarray(rows, dtype=np.int64)
     qg = np.asarray(q)[rows]
     o_d, p = attention(qg, k, v, scale)
     c = group_scores(p)
-    idx, gap = topk_select(c, keep)
+    if kv_block == 1:
+        idx, gap = topk_select(c, keep)
+    else:
+        idx, gap, _ = topk_blocks(c, keep, kv_block)
     o_s = sparse_attention(qg, k, v, idx, scale)
-    return GroupSelection(rows.astype(np.int32), c, idx, gap, o_d, o_s, o_d - o_s)
+    res = o_d - o_s if residual else np.zeros_like(o_d)
+    return GroupSelection(rows.astype(np.int32), c, idx, gap, o_d, o_s, res)
 
 
 def reuse_group(q_t, k_t, v_t, rows, idx, residual, scale):
@@ -196,14 +238,24 @@ class HeadMeta:
     groups: list                     # GroupSelection per group
 
 
-def select_head(q, k, v, proj, group, keep, scale, groups=None) -> HeadMeta:
+def select_head(q, k, v, proj, group, keep, scale, groups=None, grouping="hash", kv_block=1,
+                residual=True) -> HeadMeta:
     """Selection for one head; `groups` restricts the work to a subset of
-    group ids (the permutation always covers the whole head)."""
-    keys = hash_keys(q, proj)
-    perm = group_permutation(keys)
-    ranges = group_ranges(q.shape[0], group)
+    group ids (the permutation always covers the whole head).  `grouping`
+    "raster" replaces the hash groups by raster-order runs (keys are then 0)."""
+    n = q.shape[0]
+    if grouping == "hash":
+        keys = hash_keys(q, proj)
+        perm = group_permutation(keys)
+    elif grouping == "raster":
+        keys = np.zeros(n, dtype=np.uint8)
+        perm = raster_permutation(n)
+    else:
+        raise ValueError(f"unknown grouping {grouping!r}")
+    ranges = group_ranges(n, group)
     gids = range(len(ranges)) if groups is None else groups
-    sel = {g: select_group(q, k, v, perm[ranges[g][0]:ranges[g][1]], keep, scale) for g in gids}
+    sel = {g: select_group(q, k, v, perm[ranges[g][0]:ranges[g][1]], keep, scale, kv_block, residual)
+           for g in gids}
     return HeadMeta(perm, keys, sel)
 
 

@@ -15,7 +15,10 @@ What the checks compare against:
   probability mass, computed from torch.softmax, not from the oracle);
 * invariants the method fixes: keeping every key reproduces dense attention
   and a zero residual; reuse on unchanged inputs reproduces dense; a group of
-  one query is per-query top-k attention.
+  one query is per-query top-k attention;
+* for the failure-mode ablations: brute force over every choice of whole key
+  blocks (block selection), the identity order together with a hash whose
+  keys all agree (raster groups), and library masked attention (no residual).
 """
 
 from __future__ import annotations
@@ -253,10 +256,89 @@ def check_reuse_identity(impl, seed=12):
     assert np.max(np.abs(re - _sdpa(q[rows], kk, v, 0.35))) < 1e-12
 
 
+# ------------------------------------------------------------- ablations
+
+def check_block_topk_bruteforce(impl, seed=13):
+    """Block selection keeps the whole key blocks that retain the most group
+    probability mass among every choice of k / B blocks (enumerated; the mass
+    comes from library softmax), stored ascending and as complete blocks."""
+    r = np.random.default_rng(seed)
+    for trial in range(12):
+        b = int(r.choice([2, 3, 4]))
+        nb = int(r.integers(3, 7))
+        n = nb * b
+        kb = int(r.integers(1, nb))
+        gsize = int(r.integers(1, 4))
+        q = r.standard_normal((gsize, 3)) * 1.5
+        kk = r.standard_normal((n, 3)) * 1.5
+        v = r.standard_normal((n, 3))
+        p = _lib_probs(q, kk, 1.0).sum(axis=0)
+        best = max(sum(float(p[x * b:(x + 1) * b].sum()) for x in sub)
+                   for sub in itertools.combinations(range(nb), kb))
+        sel = impl.select_group(q, kk, v, list(range(gsize)), kb * b, 1.0, kv_block=b)
+        got = float(p[sel.idx].sum())
+        assert abs(got - best) < 1e-9, (trial, got, best, sel.idx)
+        ids = sel.idx.tolist()
+        assert ids == sorted(ids) and len(set(ids)) == kb * b
+        blocks = sorted({i // b for i in ids})
+        assert ids == [x * b + t for x in blocks for t in range(b)], (trial, ids)
+    # hand-derived: block 0 holds one strong key (0.5), block 1 three moderate
+    # ones (0.9 in total); the summed score keeps block 1, ties go to the
+    # lower block
+    c = np.array([0.5, 0.0, 0.0, 0.0, 0.3, 0.3, 0.3, 0.0, 0.1, 0.1, 0.1, 0.1])
+    idx, gap, bidx = impl.topk_blocks(c, 4, 4)
+    assert bidx.tolist() == [1] and idx.tolist() == [4, 5, 6, 7]
+    assert abs(gap - (np.float32(0.9) - np.float32(0.5))) < 1e-7
+    idx, _, bidx = impl.topk_blocks(np.array([0.2, 0.2, 0.1, 0.3, 0.2, 0.2]), 2, 2)
+    assert bidx.tolist() == [0] and idx.tolist() == [0, 1]
+
+
+def check_raster_groups(impl, seed=14):
+    """Raster grouping keeps the tokens in raster order.  When every query
+    hashes to the same key, the hash grouping's stable sort is the identity
+    too, so both groupings must give the same permutation and kept keys."""
+    r = np.random.default_rng(seed)
+    n, d, g, k = 48, 8, 16, 5
+    q = r.standard_normal((n, d))
+    q[:, 0] = np.abs(q[:, 0]) + 50.0
+    proj = np.zeros((8, d), np.float32)
+    proj[:, 0] = 1.0
+    proj[:, 1:] = r.standard_normal((8, d - 1)) * 0.01
+    kk, v = r.standard_normal((n, d)), r.standard_normal((n, d))
+    hm = impl.select_head(q, kk, v, proj, g, k, 0.3, grouping="hash")
+    rm = impl.select_head(q, kk, v, proj, g, k, 0.3, grouping="raster")
+    assert hm.keys.tolist() == [255] * n
+    assert hm.perm.tolist() == list(range(n)) and rm.perm.tolist() == list(range(n))
+    for gi in hm.groups:
+        assert hm.groups[gi].idx.tolist() == rm.groups[gi].idx.tolist()
+    q2 = r.standard_normal((n, d))
+    rm2 = impl.select_head(q2, kk, v, r.standard_normal((8, d)), g, k, 0.3, grouping="raster")
+    assert rm2.perm.tolist() == list(range(n))
+    assert rm2.groups[1].rows.tolist() == list(range(16, 32))
+
+
+def check_no_residual(impl, seed=15):
+    """Without the residual the cached correction is zero and reuse returns
+    the sparse output renormalised over the kept keys (library masked
+    attention) -- not dense attention."""
+    r = np.random.default_rng(seed)
+    n, d = 40, 8
+    q, kk, v = r.standard_normal((n, d)) * 2, r.standard_normal((n, d)) * 2, r.standard_normal((n, d))
+    rows = list(range(1, 40, 4))
+    sel = impl.select_group(q, kk, v, rows, 7, 0.35, residual=False)
+    assert np.all(sel.residual == 0.0)
+    mask = np.zeros((len(rows), n), dtype=bool)
+    mask[:, sel.idx] = True
+    re = impl.reuse_group(q, kk, v, rows, sel.idx, sel.residual, 0.35)
+    assert np.allclose(re, _sdpa(q[rows], kk, v, 0.35, mask), atol=1e-13)
+    assert np.max(np.abs(re - _sdpa(q[rows], kk, v, 0.35))) > 1e-6
+
+
 ALL_CHECKS = [
     check_hash_golden, check_hash_exact_rational, check_perm_stable_sort,
     check_dense_vs_sdpa, check_two_token_golden, check_closed_forms,
     check_uniform_golden, check_scores_mass, check_topk_bruteforce,
     check_topk_ties_lower_index, check_single_query_topk,
     check_sparse_vs_masked_sdpa, check_keep_one_and_all, check_reuse_identity,
+    check_block_topk_bruteforce, check_raster_groups, check_no_residual,
 ]

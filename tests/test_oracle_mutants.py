@@ -59,10 +59,29 @@ def _sparse_unnormalised(q, k, v, idx, scale):
     return p[:, idx] @ np.asarray(v, np.float64)[idx]
 
 
-def _select_residual_flipped(q, k, v, rows, keep, scale):
-    s = orig_select(q, k, v, rows, keep, scale)
+def _select_residual_flipped(q, k, v, rows, keep, scale, kv_block=1, residual=True):
+    s = orig_select(q, k, v, rows, keep, scale, kv_block, residual)
     s.residual = -s.residual
     return s
+
+
+def _select_ignores_no_residual(q, k, v, rows, keep, scale, kv_block=1, residual=True):
+    return orig_select(q, k, v, rows, keep, scale, kv_block, True)
+
+
+def _block_scores_max(c, block):
+    return np.asarray(c, np.float64).reshape(-1, block).max(axis=1)
+
+
+def _topk_blocks_first_key(c, k, block):
+    # ranks blocks by their first key only
+    bidx, gap = orc.topk_select(np.asarray(c, np.float64)[::block], k // block)
+    idx = (bidx.astype(np.int64)[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    return idx.astype(np.int32), gap, bidx
+
+
+def _raster_reversed(n):
+    return np.arange(n - 1, -1, -1, dtype=np.int32)
 
 
 def _reuse_no_residual(q_t, k_t, v_t, rows, idx, residual, scale):
@@ -84,6 +103,10 @@ MUTANTS = {
     "no renormalisation": ("sparse_attention", _sparse_unnormalised),
     "residual sign": ("select_group", _select_residual_flipped),
     "reuse drops residual": ("reuse_group", _reuse_no_residual),
+    "no-residual option ignored": ("select_group", _select_ignores_no_residual),
+    "block score = max": ("block_scores", _block_scores_max),
+    "block ranked by first key": ("topk_blocks", _topk_blocks_first_key),
+    "raster order reversed": ("raster_permutation", _raster_reversed),
 }
 
 

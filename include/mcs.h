@@ -151,7 +151,8 @@ size_t mcs_meta_bytes(const mcs_attn_desc* desc, int32_t group_size, const int32
 /*
  * Bytes of workspace mcs_select needs to process `heads_per_chunk` heads at a
  * time (clamped to [1, H]; 0 if the arguments are invalid).  The bulk is the
- * per-group key scores, float32 [heads_per_chunk][ceil(N/G)][N rounded up to 64].
+ * per-group key scores, float32 [heads_per_chunk][ceil(N/G)][N rounded up to 64],
+ * plus 64-key block scores (1/64 of that) for block-granular selection.
  */
 size_t mcs_select_workspace_bytes(const mcs_attn_desc* desc, int32_t group_size, int32_t heads_per_chunk);
 
@@ -188,6 +189,41 @@ mcs_status mcs_select(const mcs_attn_desc* desc, const void* q, const void* k, c
                       int32_t group_size, const int32_t* keep_host, const float* hash_proj_host,
                       void* meta_buf, size_t meta_bytes, void* workspace, size_t ws_bytes,
                       void* o_dense_out, mcs_meta* meta_out, void* stream);
+
+/*
+ * Ablations of the three failure modes the pages trace the dense-sparse gap
+ * to (abstract of "MC-Sparse: Deconstructing and Closing the Dense-Sparse
+ * Attention Gap in Diffusion Transformers": constraints of token grouping,
+ * inaccurate interaction selection, contributions lost with the discarded
+ * tokens; the list in section "MC-Sparse: three failure modes, one fix" of
+ * "The quality cliff nobody admits to").  Each field swaps one of MC-Sparse's
+ * choices for the coarser one; all zero-initialised fields but kv_block and
+ * residual select MC-Sparse itself.
+ */
+typedef enum mcs_grouping {
+  MCS_GROUPING_HASH = 0,    /* 8-bit sign hash + stable sort (MC-Sparse) */
+  MCS_GROUPING_RASTER = 1   /* runs of G tokens in raster order (perm = identity) */
+} mcs_grouping;
+
+typedef struct mcs_select_options {
+  int32_t grouping;  /* mcs_grouping */
+  int32_t kv_block;  /* 1: individual KV tokens (MC-Sparse); 64: whole runs of 64 keys, ranked by the
+                        sum of the group's key scores over the run; needs N and every k_h to be
+                        multiples of 64 (else MCS_ERROR_UNSUPPORTED_SHAPE) */
+  int32_t residual;  /* 1: cache O_dense - O_sparse (MC-Sparse); 0: cache zeros, so reuse returns the
+                        sparse output renormalised over the kept keys alone */
+  int32_t reserved;  /* must be 0 */
+} mcs_select_options;
+
+/*
+ * mcs_select with options (NULL = MC-Sparse: hash groups, single tokens,
+ * residual).  Same arguments, ownership and errors as mcs_select; an option
+ * outside the values above returns MCS_ERROR_INVALID_VALUE.
+ */
+mcs_status mcs_select_ex(const mcs_attn_desc* desc, const void* q, const void* k, const void* v,
+                         int32_t group_size, const int32_t* keep_host, const float* hash_proj_host,
+                         const mcs_select_options* options, void* meta_buf, size_t meta_bytes, void* workspace,
+                         size_t ws_bytes, void* o_dense_out, mcs_meta* meta_out, void* stream);
 
 /*
  * Reuse step ("reuses them across subsequent denoising steps", same abstract;

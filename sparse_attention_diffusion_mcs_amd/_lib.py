@@ -21,8 +21,12 @@ MCS_DTYPE_BF16 = 1
 MCS_META_VERSION = 1
 MCS_HASH_BITS = 8
 
+MCS_GROUPING_HASH = 0
+MCS_GROUPING_RASTER = 1
+
 EXPORTS = ("mcs_version", "mcs_status_string", "mcs_last_hip_error", "mcs_dense_attn", "mcs_meta_layout",
-           "mcs_meta_bytes", "mcs_select_workspace_bytes", "mcs_meta_init", "mcs_select", "mcs_sparse_attn")
+           "mcs_meta_bytes", "mcs_select_workspace_bytes", "mcs_meta_init", "mcs_select", "mcs_select_ex",
+           "mcs_sparse_attn")
 
 
 class AttnDesc(ctypes.Structure):
@@ -37,6 +41,11 @@ class Meta(ctypes.Structure):
                 ("base", ctypes.c_void_p), ("bytes", ctypes.c_uint64), ("off_perm", ctypes.c_uint64),
                 ("off_keep", ctypes.c_uint64), ("off_idx_start", ctypes.c_uint64), ("off_sched", ctypes.c_uint64),
                 ("off_idx", ctypes.c_uint64), ("off_residual", ctypes.c_uint64)]
+
+
+class SelectOptions(ctypes.Structure):
+    _fields_ = [("grouping", ctypes.c_int32), ("kv_block", ctypes.c_int32), ("residual", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class McsError(RuntimeError):
@@ -89,6 +98,9 @@ def open_library(path):
     lib.mcs_select.restype = ctypes.c_int
     lib.mcs_select.argtypes = [DP, P, P, P, ctypes.c_int32, I32P, F32P, P, ctypes.c_size_t, P,
                                ctypes.c_size_t, P, MP, P]
+    lib.mcs_select_ex.restype = ctypes.c_int
+    lib.mcs_select_ex.argtypes = [DP, P, P, P, ctypes.c_int32, I32P, F32P, ctypes.POINTER(SelectOptions), P,
+                                  ctypes.c_size_t, P, ctypes.c_size_t, P, MP, P]
     lib.mcs_sparse_attn.restype = ctypes.c_int
     lib.mcs_sparse_attn.argtypes = [DP, P, P, P, MP, P, P]
     return lib

@@ -170,8 +170,10 @@ def meta_init(q, group_size, keep, meta_buf=None, stream=None) -> MetaCache:
 
 
 def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace=None, heads_per_chunk=None,
-           return_dense=False, stream=None):
-    """Selection step (mcs_select).  Returns (MetaCache, dense output or None)."""
+           return_dense=False, stream=None, grouping="hash", kv_block=1, residual=True):
+    """Selection step (mcs_select; mcs_select_ex for the failure-mode
+    ablations: grouping "raster", kv_block 64, residual False).  Returns
+    (MetaCache, dense output or None)."""
     _check_qkv(q, k, v)
     H, N, d = q.shape
     desc = desc_for(q, scale)
@@ -189,10 +191,20 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
                                 device=q.device)
     o_dense = torch.empty_like(q) if return_dense else None
     m = L.Meta()
-    L.check(L.lib().mcs_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka),
-                               pj.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(meta_buf),
-                               meta_buf.numel(), _ptr(workspace), workspace.numel(), _ptr(o_dense),
-                               ctypes.byref(m), _stream(stream)), "mcs_select")
+    pjp = pj.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    if grouping == "hash" and kv_block == 1 and residual:
+        L.check(L.lib().mcs_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
+                                   _ptr(meta_buf), meta_buf.numel(), _ptr(workspace), workspace.numel(),
+                                   _ptr(o_dense), ctypes.byref(m), _stream(stream)), "mcs_select")
+    else:
+        codes = {"hash": L.MCS_GROUPING_HASH, "raster": L.MCS_GROUPING_RASTER}
+        if grouping not in codes:
+            raise ValueError(f"unknown grouping {grouping!r}")
+        opts = L.SelectOptions(codes[grouping], int(kv_block), 1 if residual else 0, 0)
+        L.check(L.lib().mcs_select_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
+                                      ctypes.byref(opts), _ptr(meta_buf), meta_buf.numel(), _ptr(workspace),
+                                      workspace.numel(), _ptr(o_dense), ctypes.byref(m), _stream(stream)),
+                "mcs_select_ex")
     return MetaCache(m, meta_buf), o_dense
 
 

@@ -43,7 +43,14 @@ hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, uint8_
                             hipStream_t s);
 hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hipStream_t s);
 hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, const int32_t* keep,
-                             const int64_t* idx_start, int head0, int nheads, int ng, int N, hipStream_t s);
+                             const int64_t* idx_start, int head0, int nheads, int ng, int N, int block,
+                             hipStream_t s);
+// ablation helpers: 64-key block scores of score rows, raster-order
+// permutation, zero fill (residual off)
+hipError_t launch_block_scores(const float* colsum, int ldc, float* bs, int ldb, long long rows, int nb,
+                               hipStream_t s);
+hipError_t launch_iota_perm(int32_t* perm, int H, int N, hipStream_t s);
+hipError_t launch_zero_floats(float* p, long long n, hipStream_t s);
 // Writes `nbytes` bytes from host memory to device memory through kernel
 // arguments (asynchronous on s, safe for pageable and stack host memory).
 hipError_t launch_fill_bytes(void* dst, const void* src, size_t nbytes, hipStream_t s);

@@ -99,10 +99,14 @@ void make_layout(const mcs_attn_desc* d, int32_t G, const int32_t* keep, mcs_met
 
 uint64_t colsum_ld(int N) { return align_up((uint64_t)N, 64); }
 
+// Leading dimension of the 64-key block scores of one score row.
+uint64_t block_ld(int N) { return align_up((uint64_t)(N + 63) / 64, 64); }
+
 struct WsLayout {
-  uint64_t off_keys, off_proj, off_colsum, per_head_colsum, fixed;
+  uint64_t off_keys, off_proj, off_colsum, per_head_colsum, per_head_block, fixed;
 };
 
+// keys | projections | key scores [hc][ng][ldc] | block scores [hc][ng][ldb]
 WsLayout ws_layout(const mcs_attn_desc* d, int32_t G) {
   const uint64_t H = (uint64_t)d->num_heads, N = (uint64_t)d->seq_len;
   const uint64_t ng = (N + G - 1) / G;
@@ -111,6 +115,7 @@ WsLayout ws_layout(const mcs_attn_desc* d, int32_t G) {
   w.off_proj = align_up(H * N, kAlign);
   w.off_colsum = align_up(w.off_proj + (uint64_t)MCS_HASH_BITS * d->head_dim * 8, kAlign);
   w.per_head_colsum = ng * colsum_ld((int)N) * 4;
+  w.per_head_block = ng * block_ld((int)N) * 4;
   w.fixed = w.off_colsum;
   return w;
 }
@@ -216,7 +221,7 @@ size_t mcs_select_workspace_bytes(const mcs_attn_desc* d, int32_t G, int32_t hea
   if (G != 64 && G != 128) return 0;
   const WsLayout w = ws_layout(d, G);
   const int64_t hc = std::max<int64_t>(1, std::min<int64_t>(heads_per_chunk, std::max(1, d->num_heads)));
-  return (size_t)(w.fixed + (uint64_t)hc * w.per_head_colsum);
+  return (size_t)(w.fixed + (uint64_t)hc * (w.per_head_colsum + w.per_head_block));
 }
 
 mcs_status mcs_meta_init(const mcs_attn_desc* d, int32_t G, const int32_t* keep, void* meta_buf,
@@ -241,10 +246,28 @@ mcs_status mcs_meta_init(const mcs_attn_desc* d, int32_t G, const int32_t* keep,
 mcs_status mcs_select(const mcs_attn_desc* d, const void* q, const void* k, const void* v, int32_t G,
                       const int32_t* keep, const float* proj, void* meta_buf, size_t meta_bytes, void* ws,
                       size_t ws_bytes, void* o_dense_out, mcs_meta* meta_out, void* stream) {
+  return mcs_select_ex(d, q, k, v, G, keep, proj, nullptr, meta_buf, meta_bytes, ws, ws_bytes, o_dense_out,
+                       meta_out, stream);
+}
+
+mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, const void* v, int32_t G,
+                         const int32_t* keep, const float* proj, const mcs_select_options* opts, void* meta_buf,
+                         size_t meta_bytes, void* ws, size_t ws_bytes, void* o_dense_out, mcs_meta* meta_out,
+                         void* stream) {
   mcs_status st;
   if ((st = check_desc(d)) != MCS_SUCCESS) return st;
   if ((st = check_group_keep(d, G, keep)) != MCS_SUCCESS) return st;
   if (!meta_out) return MCS_ERROR_INVALID_VALUE;
+  mcs_select_options o{MCS_GROUPING_HASH, 1, 1, 0};
+  if (opts) o = *opts;
+  if ((o.grouping != MCS_GROUPING_HASH && o.grouping != MCS_GROUPING_RASTER) || (o.kv_block != 1 && o.kv_block != 64) ||
+      (o.residual != 0 && o.residual != 1) || o.reserved != 0)
+    return MCS_ERROR_INVALID_VALUE;
+  if (o.kv_block > 1) {
+    if (d->seq_len % o.kv_block) return MCS_ERROR_UNSUPPORTED_SHAPE;
+    for (int h = 0; h < d->num_heads; ++h)
+      if (keep[h] % o.kv_block) return MCS_ERROR_UNSUPPORTED_SHAPE;
+  }
   mcs_meta m;
   make_layout(d, G, keep, &m);
   m.base = meta_buf;
@@ -259,9 +282,10 @@ mcs_status mcs_select(const mcs_attn_desc* d, const void* q, const void* k, cons
   if (!aligned(meta_buf, kAlign) || !aligned(ws, kAlign)) return MCS_ERROR_MISALIGNED;
   if (meta_bytes < m.bytes) return MCS_ERROR_BUFFER_TOO_SMALL;
   const WsLayout wl = ws_layout(d, G);
-  if (ws_bytes < wl.fixed + wl.per_head_colsum) return MCS_ERROR_BUFFER_TOO_SMALL;
+  const uint64_t per_head = wl.per_head_colsum + wl.per_head_block;
+  if (ws_bytes < wl.fixed + per_head) return MCS_ERROR_BUFFER_TOO_SMALL;
   const int H = d->num_heads, N = d->seq_len, D = d->head_dim;
-  const int hc = (int)std::min<uint64_t>((uint64_t)H, (ws_bytes - wl.fixed) / wl.per_head_colsum);
+  const int hc = (int)std::min<uint64_t>((uint64_t)H, (ws_bytes - wl.fixed) / per_head);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   if ((st = upload_meta_tables(&m, keep, s)) != MCS_SUCCESS) return st;
@@ -271,10 +295,15 @@ mcs_status mcs_select(const mcs_attn_desc* d, const void* q, const void* k, cons
   double* dproj = at<double>(ws, wl.off_proj);
   uint8_t* keys = at<uint8_t>(ws, wl.off_keys);
   float* colsum = at<float>(ws, wl.off_colsum);
+  float* bscore = at<float>(ws, wl.off_colsum + (uint64_t)hc * wl.per_head_colsum);
   int32_t* perm = at<int32_t>(meta_buf, m.off_perm);
-  if ((e = mcs::launch_fill_bytes(dproj, proj64.data(), proj64.size() * 8, s)) != hipSuccess) return hip_fail(e);
-  if ((e = mcs::launch_hash_keys(q, d->dtype, dproj, keys, H, N, D, s)) != hipSuccess) return hip_fail(e);
-  if ((e = mcs::launch_perm_sort(keys, perm, H, N, s)) != hipSuccess) return hip_fail(e);
+  if (o.grouping == MCS_GROUPING_HASH) {
+    if ((e = mcs::launch_fill_bytes(dproj, proj64.data(), proj64.size() * 8, s)) != hipSuccess) return hip_fail(e);
+    if ((e = mcs::launch_hash_keys(q, d->dtype, dproj, keys, H, N, D, s)) != hipSuccess) return hip_fail(e);
+    if ((e = mcs::launch_perm_sort(keys, perm, H, N, s)) != hipSuccess) return hip_fail(e);
+  } else if ((e = mcs::launch_iota_perm(perm, H, N, s)) != hipSuccess) {
+    return hip_fail(e);
+  }
 
   mcs::AttnArgs a = base_args(d, q, k, v);
   a.residual = at<float>(meta_buf, m.off_residual);
@@ -293,11 +322,23 @@ mcs_status mcs_select(const mcs_attn_desc* d, const void* q, const void* k, cons
     a.nheads = std::min(hc, H - h0);
     a.o = o_dense_out;
     if ((e = launch_attn(d->dtype, mcs::MODE_SELECT, a, s)) != hipSuccess) return hip_fail(e);
-    if ((e = mcs::launch_group_topk(colsum, a.ldc, at<int32_t>(meta_buf, m.off_idx), a.keep, a.idx_start, h0,
-                                    a.nheads, a.ng, N, s)) != hipSuccess)
-      return hip_fail(e);
+    if (o.kv_block == 1) {
+      e = mcs::launch_group_topk(colsum, a.ldc, at<int32_t>(meta_buf, m.off_idx), a.keep, a.idx_start, h0,
+                                 a.nheads, a.ng, N, 1, s);
+    } else {
+      const int nb = N / o.kv_block, ldb = (int)block_ld(N);
+      e = mcs::launch_block_scores(colsum, a.ldc, bscore, ldb, (long long)a.nheads * a.ng, nb, s);
+      if (e == hipSuccess)
+        e = mcs::launch_group_topk(bscore, ldb, at<int32_t>(meta_buf, m.off_idx), a.keep, a.idx_start, h0,
+                                   a.nheads, a.ng, nb, o.kv_block, s);
+    }
+    if (e != hipSuccess) return hip_fail(e);
     a.o = nullptr;
-    if ((e = launch_attn(d->dtype, mcs::MODE_RESINIT, a, s)) != hipSuccess) return hip_fail(e);
+    if (o.residual)
+      e = launch_attn(d->dtype, mcs::MODE_RESINIT, a, s);
+    else
+      e = mcs::launch_zero_floats(a.residual + (size_t)h0 * N * D, (long long)a.nheads * N * D, s);
+    if (e != hipSuccess) return hip_fail(e);
   }
   *meta_out = m;
   return MCS_SUCCESS;

@@ -13,6 +13,8 @@
 // float32 projection is exact in float64, so the key is a well-defined
 // function of the inputs); tokens are stably sorted by key; a group keeps the
 // k keys of largest float32 score, ties to the lower key index, ascending.
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -156,18 +158,22 @@ __device__ __forceinline__ void block_excl_scan2(int a, int b, int* ea, int* eb,
   *tb = tot_b;
 }
 
+// One workgroup per (head, group) row of N scores: the keep[h] / block
+// largest (ties to the lower index), written ascending.  With block > 1 the
+// row holds scores of whole key blocks and every kept block b is written as
+// its keys b*block .. b*block + block - 1.
 __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restrict__ colsum, int ldc,
                                                            int32_t* __restrict__ idx, const int32_t* __restrict__ keep,
                                                            const int64_t* __restrict__ idx_start, int head0, int ng,
-                                                           int N) {
+                                                           int N, int block) {
   __shared__ int hist[2048];
   __shared__ int sh[8];
   __shared__ int found[2];
   const int tid = threadIdx.x;
   const int g = blockIdx.x, hl = blockIdx.y, h = head0 + hl;
   const uint32_t* row = reinterpret_cast<const uint32_t*>(colsum + ((size_t)hl * ng + g) * ldc);
-  const int k = keep[h];
-  int32_t* out = idx + idx_start[h] + (int64_t)g * k;
+  const int k = keep[h] / block;
+  int32_t* out = idx + idx_start[h] + (int64_t)g * keep[h];
 
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
@@ -229,13 +235,48 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
       if (j0 + e >= N) break;
       const bool gt = u[e] > T, eq = u[e] == T;
       const int pos = gt_before + min(eq_before, krem);
-      if ((gt || (eq && eq_before < krem)) && pos < k) out[pos] = j0 + e;
+      if ((gt || (eq && eq_before < krem)) && pos < k) {
+        if (block == 1)
+          out[pos] = j0 + e;
+        else
+          for (int t = 0; t < block; ++t) out[(int64_t)pos * block + t] = (j0 + e) * block + t;
+      }
       gt_before += gt;
       eq_before += eq;
     }
     gt_base += tgt;
     eq_base += teq;
   }
+}
+
+// ------------------------------------------------ ablation helpers ----
+// Score of each run of `block` consecutive keys of a score row (block = 64:
+// sixteen float4 reads of one 256-byte run).
+__global__ void block_scores_kernel(const float* __restrict__ colsum, int ldc, float* __restrict__ bs, int ldb,
+                                    long long rows, int nb) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * nb) return;
+  const long long r = i / nb;
+  const int b = (int)(i % nb);
+  const float4* src = reinterpret_cast<const float4*>(colsum + r * ldc + 64LL * b);
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const float4 x = src[t];
+    sum += (x.x + x.y) + (x.z + x.w);
+  }
+  bs[r * ldb + b] = sum;
+}
+
+// Raster-order groups: perm[h][p] = p.
+__global__ void iota_perm_kernel(int32_t* __restrict__ perm, long long total, int N) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long long)gridDim.x * blockDim.x)
+    perm[i] = (int32_t)(i % N);
+}
+
+__global__ void zero_floats_kernel(float* __restrict__ p, long long n) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    p[i] = 0.f;
 }
 
 // ----------------------------------------------------------- host bytes ----
@@ -280,10 +321,35 @@ hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hi
 }
 
 hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, const int32_t* keep,
-                             const int64_t* idx_start, int head0, int nheads, int ng, int N, hipStream_t s) {
+                             const int64_t* idx_start, int head0, int nheads, int ng, int N, int block,
+                             hipStream_t s) {
   if (nheads == 0 || ng == 0) return hipSuccess;
   hipLaunchKernelGGL(group_topk_kernel, dim3(ng, nheads), dim3(TK_NT), 0, s, colsum, ldc, idx, keep, idx_start,
-                     head0, ng, N);
+                     head0, ng, N, block);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_scores(const float* colsum, int ldc, float* bs, int ldb, long long rows, int nb,
+                               hipStream_t s) {
+  const long long total = rows * nb;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(block_scores_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, colsum, ldc, bs,
+                     ldb, rows, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_iota_perm(int32_t* perm, int H, int N, hipStream_t s) {
+  const long long total = (long long)H * N;
+  if (total == 0) return hipSuccess;
+  const long long blocks = std::min<long long>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(iota_perm_kernel, dim3((unsigned)blocks), dim3(256), 0, s, perm, total, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_floats(float* p, long long n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const long long blocks = std::min<long long>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(zero_floats_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

@@ -180,3 +180,30 @@ def check_units(p: Problem, meta, od, outs, sc, heads, groups, label=""):
                 assert_close(to_np(o[h].index_select(0, rows_t)), ref, p.dtype,
                              f"{label} head {h} group {g} reuse step {t}")
     return exact, total
+
+
+def check_blocks(gpu_idx, scores, k, n, block, what):
+    """Block-granular kept set: whole, ascending runs of `block` keys, k / block
+    of them, chosen by the oracle's block scores under the gap rule (a block
+    score is a float32 sum of 64 float32 key scores on the GPU, so the gap
+    allowance scales with the largest block score).  Returns True when the
+    kept blocks equal the oracle's."""
+    gi = np.asarray(gpu_idx, np.int64)
+    assert gi.shape == (k,), f"{what}: {gi.shape} != ({k},)"
+    runs = gi.reshape(-1, block)
+    assert np.all(runs % block == np.arange(block)[None, :]), f"{what}: not whole blocks"
+    assert np.all(np.diff(runs[:, 0]) > 0), f"{what}: blocks not ascending"
+    assert runs[0, 0] >= 0 and runs[-1, -1] < n, f"{what}: index out of range"
+    bs = orc.block_scores(scores, block).astype(np.float32).astype(np.float64)
+    kb, nb = k // block, n // block
+    gap = GAP + 4e-6 * float(bs.max())
+    srt = np.sort(bs)[::-1]
+    ck = srt[kb - 1]
+    ck1 = srt[kb] if kb < nb else -np.inf
+    kept = runs[:, 0] // block
+    missing = np.setdiff1d(np.nonzero(bs > ck1 + gap)[0], kept)
+    assert missing.size == 0, f"{what}: clearly-in blocks missing {missing[:8]}"
+    low = kept[bs[kept] < ck - gap]
+    assert low.size == 0, f"{what}: clearly-out blocks kept {low[:8]}"
+    _, _, ob = orc.topk_blocks(scores, k, block)
+    return bool(np.array_equal(ob, kept))

@@ -98,7 +98,8 @@ def test_workspace_bytes(lib):
     d = _desc(4, 1000, 64)
     one = lib.mcs_select_workspace_bytes(ctypes.byref(d), 64, 1)
     two = lib.mcs_select_workspace_bytes(ctypes.byref(d), 64, 2)
-    per = 16 * 1024 * 4      # 16 groups x N rounded up to 64 x float32
+    # 16 groups x (N rounded up to 64 key scores + 16 block scores rounded up to 64) x float32
+    per = 16 * (1024 + 64) * 4
     assert two - one == per
     assert lib.mcs_select_workspace_bytes(ctypes.byref(d), 64, 99) == lib.mcs_select_workspace_bytes(
         ctypes.byref(d), 64, 4)
@@ -134,6 +135,35 @@ def test_select_validation(lib):
     D0 = ctypes.byref(_desc(0, N, d))
     assert sel(D0, NULL, NULL, NULL, 64, kp, pp, NULL, 0, NULL, 0, NULL, ctypes.byref(m0), NULL) == L.MCS_SUCCESS
     assert m0.version == 1 and m0.num_heads == 0 and m0.bytes == 0
+
+
+def test_select_ex_options_validation(lib):
+    """Bad ablation options are rejected before anything is launched."""
+    H, N, d = 2, 128, 64
+    keep, kp = _i32([64, 128])
+    proj = np.zeros((8, d), np.float32)
+    pp = proj.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    m = L.Meta()
+    D = ctypes.byref(_desc(H, N, d))
+    mb = lib.mcs_meta_bytes(D, 64, kp)
+    wb = lib.mcs_select_workspace_bytes(D, 64, 1)
+
+    def call(opts, desc=D, keep_p=kp):
+        return lib.mcs_select_ex(desc, FAKE, FAKE, FAKE, 64, keep_p, pp, ctypes.byref(opts), FAKE, mb, FAKE, wb,
+                                 NULL, ctypes.byref(m), NULL)
+
+    O = L.SelectOptions
+    assert call(O(2, 1, 1, 0)) == L.MCS_ERROR_INVALID_VALUE       # unknown grouping
+    assert call(O(0, 32, 1, 0)) == L.MCS_ERROR_INVALID_VALUE      # block size other than 1 / 64
+    assert call(O(0, 1, 2, 0)) == L.MCS_ERROR_INVALID_VALUE       # residual flag not 0 / 1
+    assert call(O(0, 1, 1, 7)) == L.MCS_ERROR_INVALID_VALUE       # reserved field set
+    odd, op = _i32([64, 100])
+    assert call(O(0, 64, 1, 0), keep_p=op) == L.MCS_ERROR_UNSUPPORTED_SHAPE   # keep not whole blocks
+    d2 = ctypes.byref(_desc(H, 130, d))
+    assert call(O(1, 64, 0, 0), desc=d2) == L.MCS_ERROR_UNSUPPORTED_SHAPE     # N not whole blocks
+    # the options do not bypass the ordinary checks
+    zero, zp = _i32([0, 64])
+    assert call(O(1, 1, 0, 0), keep_p=zp) == L.MCS_ERROR_INVALID_VALUE
 
 
 def test_sparse_validation(lib):

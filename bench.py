@@ -15,12 +15,16 @@ per denoising step, the roofline of the reuse kernel measured with HIP events
 on the launch stream, and the CPU oracle timed on a bounded sample of the same
 workload on this host.
 
+With --ablation the line also carries the failure-mode ablations: the same
+segment with raster query groups, whole 64-key KV blocks, no residual, and
+all three together, each with its timings and per-step fidelity.
+
 With --sweep (workload 5) the line also carries the denoising-loop sweep:
 for every keep fraction and group size, a 30-step loop with re-selection every
 10 steps, its amortised time against 30 dense steps and the relative L2 error
 of every step's output against dense attention on that step.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--sweep]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--sweep] [--ablation]
 """
 
 from __future__ import annotations
@@ -65,6 +69,8 @@ def parse():
                     help="run one plain 1 GiB device-to-device copy first (a known-size reference for HBM counters)")
     ap.add_argument("--cpu-groups", type=int, default=288, help="oracle groups sampled per sampled head")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 8))
+    ap.add_argument("--ablation", action="store_true",
+                    help="add the failure-mode ablations (raster groups, 64-key blocks, no residual)")
     ap.add_argument("--sweep", action="store_true",
                     help="workload 5 only: add the keep x group denoising-loop sweep to the result")
     return ap.parse_args()
@@ -254,6 +260,57 @@ def sweep(w, X, threads, scale):
     return {"steps": S, "reselect_every": R, "dense_ms": round(dense_med, 4), "points": points}
 
 
+ABLATIONS = [
+    ("mc-sparse", dict(grouping="hash", kv_block=1, residual=True)),
+    ("no residual", dict(grouping="hash", kv_block=1, residual=False)),
+    ("64-key blocks", dict(grouping="hash", kv_block=64, residual=True)),
+    ("raster groups", dict(grouping="raster", kv_block=1, residual=True)),
+    ("raster groups + 64-key blocks + no residual", dict(grouping="raster", kv_block=64, residual=False)),
+]
+
+
+def ablation(w, X, keeps, scale):
+    """Each failure-mode ablation on the workload's segment (selection on step
+    0, reuse on steps 1..T): timings and the relative L2 of every reuse step
+    against dense attention on that step."""
+    import torch
+
+    import sparse_attention_diffusion_mcs_amd as mcs
+
+    H, N, d, G, T = w.heads, w.seq_len, w.head_dim, w.group, w.reuse_steps
+    stream = torch.cuda.current_stream()
+    proj = hash_projections(0, w.wid, d)
+    dense = {t: mcs.dense_attn(*X[t], scale=scale) for t in range(1, T + 1)}
+    ws = torch.empty(mcs.workspace_bytes(X[0][0], G), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(X[0][0])
+    rows = []
+    for name, opt in ABLATIONS:
+        if opt["kv_block"] > 1 and (N % opt["kv_block"] or np.any(keeps % opt["kv_block"])):
+            rows.append({"variant": name, "skipped": "N or keep not whole 64-key blocks"})
+            continue
+        mb = torch.empty(int(mcs.meta_layout(H, N, d, 1, G, keeps).bytes), dtype=torch.uint8, device="cuda")
+        mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws, **opt)  # warm-up
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * T + 2)]
+        e[0].record(stream)
+        meta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws, **opt)
+        e[1].record(stream)
+        err = []
+        for t in range(1, T + 1):
+            e[2 * t].record(stream)
+            mcs.sparse_attn(*X[t], meta, out=out, scale=scale)
+            e[2 * t + 1].record(stream)
+            err.append(rel_l2(out, dense[t]))
+        torch.cuda.synchronize()
+        reuse = [e[2 * t].elapsed_time(e[2 * t + 1]) for t in range(1, T + 1)]
+        rows.append({"variant": name, **opt, "select_ms": round(e[0].elapsed_time(e[1]), 3),
+                     "reuse_ms": round(float(np.mean(reuse)), 4),
+                     "rel_l2_step1": round(err[0], 6), "rel_l2_mean": round(float(np.mean(err)), 6),
+                     "rel_l2_final": round(err[-1], 6)})
+        log(f"ablation {rows[-1]}")
+        del meta, mb
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -348,6 +405,7 @@ def main():
     torch.cuda.synchronize()
 
     sweep_res = sweep(w, X, args.threads, scale) if args.sweep else None
+    ablation_res = ablation(w, X, keeps, scale) if args.ablation else None
     peak_mem = int(torch.cuda.max_memory_allocated())
 
     reuse_mean = float(np.mean(reuse_ms))
@@ -406,6 +464,8 @@ def main():
         result["keep_histogram"] = {str(int(k)): int(c) for k, c in zip(ks, cnt)}
     if sweep_res is not None:
         result["sweep"] = sweep_res
+    if ablation_res is not None:
+        result["ablation"] = ablation_res
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w, keeps, T, scale, args.cpu_groups)

@@ -41,7 +41,10 @@ of token grouping, inaccurate interaction selection, contributions lost with
 the discarded tokens; [BLOG] "MC-Sparse: three failure modes, one fix") swap
 one choice each: raster-order query groups instead of hash groups, whole
 64-token KV blocks ranked by their summed score instead of individual tokens,
-and no residual (the renormalised sparse output alone).
+and no residual (the renormalised sparse output alone).  A fourth variant
+changes the grouping the other way: the sign hash of the queries centred on
+their per-head mean, so that a component shared by all queries does not fix
+most of the bits.
 
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
@@ -77,6 +80,31 @@ def hash_keys(q: np.ndarray, proj: np.ndarray) -> np.ndarray:
     acc = np.zeros((n, nb), dtype=np.float64)
     for c in range(d):
         acc = acc + q64[:, c:c + 1] * r64[None, :, c]
+    keys = np.zeros(n, dtype=np.int64)
+    for b in range(nb):
+        keys |= (acc[:, b] > 0.0).astype(np.int64) << b
+    return keys.astype(np.uint8)
+
+
+def query_mean(q: np.ndarray) -> np.ndarray:
+    """Per-dimension mean of one head's queries: float64 sums accumulated in
+    token order (i = 0, 1, ..., N-1), then one division by N."""
+    q64 = np.asarray(q, dtype=np.float64)
+    return np.cumsum(q64, axis=0)[-1] / q64.shape[0]
+
+
+def centred_hash_keys(q: np.ndarray, proj: np.ndarray) -> np.ndarray:
+    """Sign hash of the centred queries q_i - mean.  Every step is one
+    rounded float64 operation: the subtraction, then for c = 0..d-1 the
+    product (q_ic - mean_c) * r_bc and its addition to the running sum (no
+    fused multiply-add), so the keys are one well-defined value."""
+    x = np.asarray(q, dtype=np.float64) - query_mean(q)[None, :]
+    r64 = np.asarray(proj, dtype=np.float64)
+    n, d = x.shape
+    nb = r64.shape[0]
+    acc = np.zeros((n, nb), dtype=np.float64)
+    for c in range(d):
+        acc = acc + x[:, c:c + 1] * r64[None, :, c]
     keys = np.zeros(n, dtype=np.int64)
     for b in range(nb):
         keys |= (acc[:, b] > 0.0).astype(np.int64) << b
@@ -242,10 +270,14 @@ def select_head(q, k, v, proj, group, keep, scale, groups=None, grouping="hash",
                 residual=True) -> HeadMeta:
     """Selection for one head; `groups` restricts the work to a subset of
     group ids (the permutation always covers the whole head).  `grouping`
-    "raster" replaces the hash groups by raster-order runs (keys are then 0)."""
+    "raster" replaces the hash groups by raster-order runs (keys are then 0);
+    "centred" hashes the queries centred on their mean."""
     n = q.shape[0]
     if grouping == "hash":
         keys = hash_keys(q, proj)
+        perm = group_permutation(keys)
+    elif grouping == "centred":
+        keys = centred_hash_keys(q, proj)
         perm = group_permutation(keys)
     elif grouping == "raster":
         keys = np.zeros(n, dtype=np.uint8)

@@ -317,6 +317,40 @@ def check_raster_groups(impl, seed=14):
     assert rm2.groups[1].rows.tolist() == list(range(16, 32))
 
 
+def check_centred_hash(impl, seed=16):
+    """Centred hash against exact rational arithmetic.  With small-integer
+    queries and projections and N a power of two, every float64 step of the
+    centred hash is exact, so its bits must be the signs of the exact
+    rational dot products (q_i - mean) . r_b; a hand-derived case pins the
+    mean and the bits; a shift of every query by a constant leaves the keys
+    unchanged."""
+    r = np.random.default_rng(seed)
+    for trial in range(6):
+        n, d = 16, 6
+        q = r.integers(-8, 9, size=(n, d)).astype(np.float32)
+        proj = r.integers(-3, 4, size=(8, d)).astype(np.float32)
+        keys = impl.centred_hash_keys(q, proj)
+        mean = [sum(Fraction(int(q[i, c])) for i in range(n)) / n for c in range(d)]
+        for i in range(n):
+            want = 0
+            for b in range(8):
+                dot = sum((Fraction(int(q[i, c])) - mean[c]) * int(proj[b, c]) for c in range(d))
+                want |= (1 << b) if dot > 0 else 0
+            assert int(keys[i]) == want, (trial, i, int(keys[i]), want)
+        shifted = impl.centred_hash_keys(q + np.float32(5.0), proj)
+        assert shifted.tolist() == keys.tolist()
+    # hand-derived: mean (1, 2); centred rows (-1,-1), (1,1), (1,-1), (-1,1);
+    # r_0 = (1, 0) -> bit 0 = [x > 0]; r_1 = (0, 1) -> bit 1 = [y > 0];
+    # r_2 = (1, 1) -> only the second row is positive, the sums of 0 give 0
+    q = np.array([[0, 1], [2, 3], [2, 1], [0, 3]], np.float32)
+    proj = np.zeros((8, 2), np.float32)
+    proj[0] = [1, 0]
+    proj[1] = [0, 1]
+    proj[2] = [1, 1]
+    assert impl.query_mean(q).tolist() == [1.0, 2.0]
+    assert impl.centred_hash_keys(q, proj).tolist() == [0, 7, 1, 2]
+
+
 def check_no_residual(impl, seed=15):
     """Without the residual the cached correction is zero and reuse returns
     the sparse output renormalised over the kept keys (library masked
@@ -340,5 +374,5 @@ ALL_CHECKS = [
     check_uniform_golden, check_scores_mass, check_topk_bruteforce,
     check_topk_ties_lower_index, check_single_query_topk,
     check_sparse_vs_masked_sdpa, check_keep_one_and_all, check_reuse_identity,
-    check_block_topk_bruteforce, check_raster_groups, check_no_residual,
+    check_block_topk_bruteforce, check_raster_groups, check_no_residual, check_centred_hash,
 ]

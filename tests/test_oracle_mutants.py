@@ -80,6 +80,15 @@ def _topk_blocks_first_key(c, k, block):
     return idx.astype(np.int32), gap, bidx
 
 
+def _centred_hash_uncentred(q, proj):
+    return orc.hash_keys(q, proj)
+
+
+def _mean_first_half(q):
+    q64 = np.asarray(q, np.float64)
+    return q64[: q64.shape[0] // 2].mean(axis=0)
+
+
 def _raster_reversed(n):
     return np.arange(n - 1, -1, -1, dtype=np.int32)
 
@@ -107,6 +116,8 @@ MUTANTS = {
     "block score = max": ("block_scores", _block_scores_max),
     "block ranked by first key": ("topk_blocks", _topk_blocks_first_key),
     "raster order reversed": ("raster_permutation", _raster_reversed),
+    "centred hash not centred": ("centred_hash_keys", _centred_hash_uncentred),
+    "mean over half the queries": ("query_mean", _mean_first_half),
 }
 
 

@@ -16,8 +16,9 @@ on the launch stream, and the CPU oracle timed on a bounded sample of the same
 workload on this host.
 
 With --ablation the line also carries the failure-mode ablations: the same
-segment with raster query groups, whole 64-key KV blocks, no residual, and
-all three together, each with its timings and per-step fidelity.
+segment with raster query groups, centred-hash groups, whole 64-key KV
+blocks, no residual, and the coarse three together, each with its timings
+and per-step fidelity.
 
 With --sweep (workload 5) the line also carries the denoising-loop sweep:
 for every keep fraction and group size, a 30-step loop with re-selection every
@@ -265,6 +266,7 @@ ABLATIONS = [
     ("no residual", dict(grouping="hash", kv_block=1, residual=False)),
     ("64-key blocks", dict(grouping="hash", kv_block=64, residual=True)),
     ("raster groups", dict(grouping="raster", kv_block=1, residual=True)),
+    ("centred-hash groups", dict(grouping="centred", kv_block=1, residual=True)),
     ("raster groups + 64-key blocks + no residual", dict(grouping="raster", kv_block=64, residual=False)),
 ]
 

@@ -201,8 +201,10 @@ mcs_status mcs_select(const mcs_attn_desc* desc, const void* q, const void* k, c
  * residual select MC-Sparse itself.
  */
 typedef enum mcs_grouping {
-  MCS_GROUPING_HASH = 0,    /* 8-bit sign hash + stable sort (MC-Sparse) */
-  MCS_GROUPING_RASTER = 1   /* runs of G tokens in raster order (perm = identity) */
+  MCS_GROUPING_HASH = 0,          /* 8-bit sign hash + stable sort (MC-Sparse) */
+  MCS_GROUPING_RASTER = 1,        /* runs of G tokens in raster order (perm = identity) */
+  MCS_GROUPING_CENTRED_HASH = 2   /* sign hash of q_i - mean_i' q_i' (per head; float64 sums in token
+                                     order, each product and addition rounded separately) + stable sort */
 } mcs_grouping;
 
 typedef struct mcs_select_options {

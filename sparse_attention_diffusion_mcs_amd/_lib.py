@@ -23,6 +23,7 @@ MCS_HASH_BITS = 8
 
 MCS_GROUPING_HASH = 0
 MCS_GROUPING_RASTER = 1
+MCS_GROUPING_CENTRED_HASH = 2
 
 EXPORTS = ("mcs_version", "mcs_status_string", "mcs_last_hip_error", "mcs_dense_attn", "mcs_meta_layout",
            "mcs_meta_bytes", "mcs_select_workspace_bytes", "mcs_meta_init", "mcs_select", "mcs_select_ex",

@@ -172,7 +172,7 @@ def meta_init(q, group_size, keep, meta_buf=None, stream=None) -> MetaCache:
 def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace=None, heads_per_chunk=None,
            return_dense=False, stream=None, grouping="hash", kv_block=1, residual=True):
     """Selection step (mcs_select; mcs_select_ex for the failure-mode
-    ablations: grouping "raster", kv_block 64, residual False).  Returns
+    ablations: grouping "raster" or "centred", kv_block 64, residual False).  Returns
     (MetaCache, dense output or None)."""
     _check_qkv(q, k, v)
     H, N, d = q.shape
@@ -197,7 +197,8 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
                                    _ptr(meta_buf), meta_buf.numel(), _ptr(workspace), workspace.numel(),
                                    _ptr(o_dense), ctypes.byref(m), _stream(stream)), "mcs_select")
     else:
-        codes = {"hash": L.MCS_GROUPING_HASH, "raster": L.MCS_GROUPING_RASTER}
+        codes = {"hash": L.MCS_GROUPING_HASH, "raster": L.MCS_GROUPING_RASTER,
+                 "centred": L.MCS_GROUPING_CENTRED_HASH}
         if grouping not in codes:
             raise ValueError(f"unknown grouping {grouping!r}")
         opts = L.SelectOptions(codes[grouping], int(kv_block), 1 if residual else 0, 0)

@@ -39,8 +39,10 @@ hipError_t launch_attn_bf16(int mode, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(int mode, const AttnArgs& a, hipStream_t s);
 
 // selection helpers (select.hip)
-hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, uint8_t* keys, int H, int N, int D,
-                            hipStream_t s);
+// mean: per-head query means (float64 [H][D]) for the centred hash, or null
+hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, const double* mean, uint8_t* keys, int H,
+                            int N, int D, hipStream_t s);
+hipError_t launch_query_mean(const void* q, int dtype, double* mean, int H, int N, int D, hipStream_t s);
 hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hipStream_t s);
 hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, const int32_t* keep,
                              const int64_t* idx_start, int head0, int nheads, int ng, int N, int block,

@@ -103,17 +103,18 @@ uint64_t colsum_ld(int N) { return align_up((uint64_t)N, 64); }
 uint64_t block_ld(int N) { return align_up((uint64_t)(N + 63) / 64, 64); }
 
 struct WsLayout {
-  uint64_t off_keys, off_proj, off_colsum, per_head_colsum, per_head_block, fixed;
+  uint64_t off_keys, off_proj, off_mean, off_colsum, per_head_colsum, per_head_block, fixed;
 };
 
-// keys | projections | key scores [hc][ng][ldc] | block scores [hc][ng][ldb]
+// keys | projections | query means | key scores [hc][ng][ldc] | block scores [hc][ng][ldb]
 WsLayout ws_layout(const mcs_attn_desc* d, int32_t G) {
   const uint64_t H = (uint64_t)d->num_heads, N = (uint64_t)d->seq_len;
   const uint64_t ng = (N + G - 1) / G;
   WsLayout w;
   w.off_keys = 0;
   w.off_proj = align_up(H * N, kAlign);
-  w.off_colsum = align_up(w.off_proj + (uint64_t)MCS_HASH_BITS * d->head_dim * 8, kAlign);
+  w.off_mean = align_up(w.off_proj + (uint64_t)MCS_HASH_BITS * d->head_dim * 8, kAlign);
+  w.off_colsum = align_up(w.off_mean + H * d->head_dim * 8, kAlign);
   w.per_head_colsum = ng * colsum_ld((int)N) * 4;
   w.per_head_block = ng * block_ld((int)N) * 4;
   w.fixed = w.off_colsum;
@@ -260,7 +261,9 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
   if (!meta_out) return MCS_ERROR_INVALID_VALUE;
   mcs_select_options o{MCS_GROUPING_HASH, 1, 1, 0};
   if (opts) o = *opts;
-  if ((o.grouping != MCS_GROUPING_HASH && o.grouping != MCS_GROUPING_RASTER) || (o.kv_block != 1 && o.kv_block != 64) ||
+  if ((o.grouping != MCS_GROUPING_HASH && o.grouping != MCS_GROUPING_RASTER &&
+       o.grouping != MCS_GROUPING_CENTRED_HASH) ||
+      (o.kv_block != 1 && o.kv_block != 64) ||
       (o.residual != 0 && o.residual != 1) || o.reserved != 0)
     return MCS_ERROR_INVALID_VALUE;
   if (o.kv_block > 1) {
@@ -297,9 +300,14 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
   float* colsum = at<float>(ws, wl.off_colsum);
   float* bscore = at<float>(ws, wl.off_colsum + (uint64_t)hc * wl.per_head_colsum);
   int32_t* perm = at<int32_t>(meta_buf, m.off_perm);
-  if (o.grouping == MCS_GROUPING_HASH) {
+  if (o.grouping == MCS_GROUPING_HASH || o.grouping == MCS_GROUPING_CENTRED_HASH) {
+    double* mean = nullptr;
+    if (o.grouping == MCS_GROUPING_CENTRED_HASH) {
+      mean = at<double>(ws, wl.off_mean);
+      if ((e = mcs::launch_query_mean(q, d->dtype, mean, H, N, D, s)) != hipSuccess) return hip_fail(e);
+    }
     if ((e = mcs::launch_fill_bytes(dproj, proj64.data(), proj64.size() * 8, s)) != hipSuccess) return hip_fail(e);
-    if ((e = mcs::launch_hash_keys(q, d->dtype, dproj, keys, H, N, D, s)) != hipSuccess) return hip_fail(e);
+    if ((e = mcs::launch_hash_keys(q, d->dtype, dproj, mean, keys, H, N, D, s)) != hipSuccess) return hip_fail(e);
     if ((e = mcs::launch_perm_sort(keys, perm, H, N, s)) != hipSuccess) return hip_fail(e);
   } else if ((e = mcs::launch_iota_perm(perm, H, N, s)) != hipSuccess) {
     return hip_fail(e);

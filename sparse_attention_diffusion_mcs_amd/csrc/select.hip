@@ -29,25 +29,58 @@ __device__ __forceinline__ float load_elem<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
-template <typename T, int D>
+// With CENTRED the queries are first centred on their head's mean (`mean`,
+// float64 [H][D]); each product and each addition is then rounded on its own
+// (__dmul_rn, __dadd_rn), because the centred values no longer multiply
+// exactly.  Without it every product of a bf16/float32 value and a float32
+// projection is exact in float64 and one fused multiply-add per term gives
+// the same sum.
+template <typename T, int D, bool CENTRED>
 __global__ __launch_bounds__(256) void hash_keys_kernel(const T* __restrict__ q, const double* __restrict__ proj,
-                                                         uint8_t* __restrict__ keys, long long total) {
+                                                         const double* __restrict__ mean, uint8_t* __restrict__ keys,
+                                                         long long total, int N) {
   __shared__ double r[8][D];
   for (int e = threadIdx.x; e < 8 * D; e += 256) r[e / D][e % D] = proj[e];
   __syncthreads();
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
   const T* row = q + i * D;
+  const double* mu = CENTRED ? mean + (i / N) * D : nullptr;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int c = 0; c < D; ++c) {
     const double x = (double)load_elem<T>(row + c);
+    if constexpr (CENTRED) {
+      const double xc = x - mu[c];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[b] = __fma_rn(x, r[b][c], acc[b]);
+      for (int b = 0; b < 8; ++b) acc[b] = __dadd_rn(acc[b], __dmul_rn(xc, r[b][c]));
+    } else {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) acc[b] = __fma_rn(x, r[b][c], acc[b]);
+    }
   }
   uint32_t key = 0;
 #pragma unroll
   for (int b = 0; b < 8; ++b) key |= (acc[b] > 0.0 ? 1u : 0u) << b;
   keys[i] = (uint8_t)key;
+}
+
+// Per-dimension mean of each head's queries: one thread per (head, dim),
+// float64 sums in token order, one division.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void query_mean_kernel(const T* __restrict__ q, double* __restrict__ mean, int N) {
+  const int h = blockIdx.x, c = threadIdx.x;
+  const T* col = q + (size_t)h * N * D + c;
+  double sum = 0.0;
+  int i = 0;
+  for (; i + 8 <= N; i += 8) {
+    double x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = (double)load_elem<T>(col + (size_t)(i + u) * D);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum = __dadd_rn(sum, x[u]);
+  }
+  for (; i < N; ++i) sum = __dadd_rn(sum, (double)load_elem<T>(col + (size_t)i * D));
+  mean[(size_t)h * D + c] = sum / (double)N;
 }
 
 // ---------------------------------------------------------- stable sort ----
@@ -291,25 +324,54 @@ __global__ void fill_words_kernel(uint32_t* dst, FillPayload p, int n) {
 
 }  // namespace
 
-hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, uint8_t* keys, int H, int N, int D,
-                            hipStream_t s) {
+namespace {
+template <typename T, int D>
+void hash_launch(const void* q, const double* proj, const double* mean, uint8_t* keys, long long total, int N,
+                 hipStream_t s) {
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (mean)
+    hipLaunchKernelGGL((hash_keys_kernel<T, D, true>), grid, dim3(256), 0, s, static_cast<const T*>(q), proj, mean,
+                       keys, total, N);
+  else
+    hipLaunchKernelGGL((hash_keys_kernel<T, D, false>), grid, dim3(256), 0, s, static_cast<const T*>(q), proj,
+                       mean, keys, total, N);
+}
+}  // namespace
+
+hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, const double* mean, uint8_t* keys, int H,
+                            int N, int D, hipStream_t s) {
   const long long total = (long long)H * N;
   if (total == 0) return hipSuccess;
-  const dim3 grid((unsigned)((total + 255) / 256));
   if (dtype == 1) {
     if (D == 64)
-      hipLaunchKernelGGL((hash_keys_kernel<uint16_t, 64>), grid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(q), proj, keys, total);
+      hash_launch<uint16_t, 64>(q, proj, mean, keys, total, N, s);
     else
-      hipLaunchKernelGGL((hash_keys_kernel<uint16_t, 128>), grid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(q), proj, keys, total);
+      hash_launch<uint16_t, 128>(q, proj, mean, keys, total, N, s);
   } else {
     if (D == 64)
-      hipLaunchKernelGGL((hash_keys_kernel<float, 64>), grid, dim3(256), 0, s, static_cast<const float*>(q),
-                         proj, keys, total);
+      hash_launch<float, 64>(q, proj, mean, keys, total, N, s);
     else
-      hipLaunchKernelGGL((hash_keys_kernel<float, 128>), grid, dim3(256), 0, s, static_cast<const float*>(q),
-                         proj, keys, total);
+      hash_launch<float, 128>(q, proj, mean, keys, total, N, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_query_mean(const void* q, int dtype, double* mean, int H, int N, int D, hipStream_t s) {
+  if (H == 0 || N == 0) return hipSuccess;
+  if (dtype == 1) {
+    if (D == 64)
+      hipLaunchKernelGGL((query_mean_kernel<uint16_t, 64>), dim3(H), dim3(64), 0, s, static_cast<const uint16_t*>(q),
+                         mean, N);
+    else
+      hipLaunchKernelGGL((query_mean_kernel<uint16_t, 128>), dim3(H), dim3(128), 0, s,
+                         static_cast<const uint16_t*>(q), mean, N);
+  } else {
+    if (D == 64)
+      hipLaunchKernelGGL((query_mean_kernel<float, 64>), dim3(H), dim3(64), 0, s, static_cast<const float*>(q), mean,
+                         N);
+    else
+      hipLaunchKernelGGL((query_mean_kernel<float, 128>), dim3(H), dim3(128), 0, s, static_cast<const float*>(q),
+                         mean, N);
   }
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 """GPU parity of the failure-mode ablations (mcs_select_ex): raster query
-groups, whole 64-key KV blocks, and no residual, each against the CPU oracle
-run with the same option on every group of every head."""
+groups, centred-hash groups, whole 64-key KV blocks, and no residual, each
+against the CPU oracle run with the same option on every group of every
+head (the permutation bit-exact)."""
 
 import numpy as np
 import pytest
@@ -20,6 +21,8 @@ CASES = {
     "no_residual_bf16_d64_g128": ((4, 10, 30), 2, 64, "bf16", 128, [100, 600], "hash", 1, False, 123),
     "raster_block64_no_residual_bf16": ((2, 16, 16), 2, 128, "bf16", 64, [64, 192], "raster", 64, False, 124),
     "block64_fp32_d64_g128": ((2, 8, 16), 1, 64, "fp32", 128, [128], "hash", 64, True, 125),
+    "centred_bf16_d128_ragged": ((3, 9, 23), 3, 128, "bf16", 64, [96, 160, 300], "centred", 1, True, 127),
+    "centred_fp32_d64_g128": ((2, 10, 20), 2, 64, "fp32", 128, [50, 200], "centred", 1, True, 128),
 }
 
 

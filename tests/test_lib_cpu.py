@@ -153,7 +153,7 @@ def test_select_ex_options_validation(lib):
                                  NULL, ctypes.byref(m), NULL)
 
     O = L.SelectOptions
-    assert call(O(2, 1, 1, 0)) == L.MCS_ERROR_INVALID_VALUE       # unknown grouping
+    assert call(O(3, 1, 1, 0)) == L.MCS_ERROR_INVALID_VALUE       # unknown grouping
     assert call(O(0, 32, 1, 0)) == L.MCS_ERROR_INVALID_VALUE      # block size other than 1 / 64
     assert call(O(0, 1, 2, 0)) == L.MCS_ERROR_INVALID_VALUE       # residual flag not 0 / 1
     assert call(O(0, 1, 1, 7)) == L.MCS_ERROR_INVALID_VALUE       # reserved field set

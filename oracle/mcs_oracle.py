@@ -44,7 +44,10 @@ one choice each: raster-order query groups instead of hash groups, whole
 and no residual (the renormalised sparse output alone).  A fourth variant
 changes the grouping the other way: the sign hash of the queries centred on
 their per-head mean, so that a component shared by all queries does not fix
-most of the bits.
+most of the bits.  A fifth groups the tokens of a (T, Y, X) latent grid in
+Morton (Z-curve) order, so that a group of G = 64 tokens is a 4 x 4 x 4
+block of the grid: spatially compact queries, the similar queries of a
+position-driven DiT.
 
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
@@ -119,6 +122,24 @@ def group_permutation(keys: np.ndarray) -> np.ndarray:
 def raster_permutation(n: int) -> np.ndarray:
     """Ablation of the grouping: groups are runs of G tokens in raster order."""
     return np.arange(n, dtype=np.int32)
+
+
+def morton_code(t: np.ndarray, y: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """Z-curve code of grid cells: bit b of x, y, t goes to bit 3b, 3b + 1,
+    3b + 2 of the code (10 bits per axis)."""
+    code = np.zeros(np.shape(x), dtype=np.int64)
+    for b in range(10):
+        code |= (((np.asarray(x) >> b) & 1) << (3 * b)) | (((np.asarray(y) >> b) & 1) << (3 * b + 1)) | \
+                (((np.asarray(t) >> b) & 1) << (3 * b + 2))
+    return code
+
+
+def morton_permutation(grid) -> np.ndarray:
+    """Tokens of a raster-ordered (T, Y, X) grid (token = (t * Y + y) * X + x)
+    sorted by their Z-curve code."""
+    tt, yy, xx = np.meshgrid(*(np.arange(n) for n in grid), indexing="ij")
+    code = morton_code(tt.ravel(), yy.ravel(), xx.ravel())
+    return np.argsort(code, kind="stable").astype(np.int32)
 
 
 def group_ranges(n: int, group: int):
@@ -267,11 +288,12 @@ class HeadMeta:
 
 
 def select_head(q, k, v, proj, group, keep, scale, groups=None, grouping="hash", kv_block=1,
-                residual=True) -> HeadMeta:
+                residual=True, grid=None) -> HeadMeta:
     """Selection for one head; `groups` restricts the work to a subset of
     group ids (the permutation always covers the whole head).  `grouping`
     "raster" replaces the hash groups by raster-order runs (keys are then 0);
-    "centred" hashes the queries centred on their mean."""
+    "centred" hashes the queries centred on their mean; "morton" orders the
+    tokens of the (T, Y, X) `grid` along the Z-curve."""
     n = q.shape[0]
     if grouping == "hash":
         keys = hash_keys(q, proj)
@@ -282,6 +304,11 @@ def select_head(q, k, v, proj, group, keep, scale, groups=None, grouping="hash",
     elif grouping == "raster":
         keys = np.zeros(n, dtype=np.uint8)
         perm = raster_permutation(n)
+    elif grouping == "morton":
+        if grid is None or int(np.prod(grid)) != n:
+            raise ValueError("morton grouping needs the (T, Y, X) grid of the tokens")
+        keys = np.zeros(n, dtype=np.uint8)
+        perm = morton_permutation(grid)
     else:
         raise ValueError(f"unknown grouping {grouping!r}")
     ranges = group_ranges(n, group)

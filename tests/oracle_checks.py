@@ -351,6 +351,36 @@ def check_centred_hash(impl, seed=16):
     assert impl.centred_hash_keys(q, proj).tolist() == [0, 7, 1, 2]
 
 
+def check_morton_groups(impl):
+    """Z-curve order: a hand-derived order on a 1 x 2 x 4 grid; on a 4 x 4 x 8
+    grid every run of 8 tokens is a 2 x 2 x 2 cube and every run of 64 a
+    4 x 4 x 4 cube; on a 3 x 5 x 6 grid (no power of two) the order is a
+    bijection that visits each 2 x 2 x 2 cell of the curve before the next."""
+    # (y, x) codes: (0,0)=0 (0,1)=1 (1,0)=2 (1,1)=3 (0,2)=8 (0,3)=9 (1,2)=10 (1,3)=11
+    assert impl.morton_permutation((1, 2, 4)).tolist() == [0, 1, 4, 5, 2, 3, 6, 7]
+    assert impl.morton_permutation((2, 2, 2)).tolist() == list(range(8))
+    T, Y, X = 4, 4, 8
+    perm = impl.morton_permutation((T, Y, X))
+    t, rem = np.divmod(perm, Y * X)
+    y, x = np.divmod(rem, X)
+    for size, side in ((8, 2), (64, 4)):
+        for s in range(0, T * Y * X, size):
+            for a in (t[s:s + size], y[s:s + size], x[s:s + size]):
+                assert a.max() - a.min() == side - 1 and a.min() % side == 0, (size, s)
+            assert len({(int(i), int(j), int(k)) for i, j, k in zip(t[s:s + size], y[s:s + size], x[s:s + size])}) == size
+    perm = impl.morton_permutation((3, 5, 6))
+    assert sorted(perm.tolist()) == list(range(90))
+    t, rem = np.divmod(perm, 30)
+    y, x = np.divmod(rem, 6)
+    cell = (t // 2) * 100 + (y // 2) * 10 + (x // 2)
+    first = {}
+    for i, c in enumerate(cell.tolist()):
+        first.setdefault(c, i)
+    last = {c: i for i, c in enumerate(cell.tolist())}
+    for c in first:
+        assert last[c] - first[c] + 1 == int(np.sum(cell == c)), "a 2x2x2 cell is split"
+
+
 def check_no_residual(impl, seed=15):
     """Without the residual the cached correction is zero and reuse returns
     the sparse output renormalised over the kept keys (library masked
@@ -375,4 +405,5 @@ ALL_CHECKS = [
     check_topk_ties_lower_index, check_single_query_topk,
     check_sparse_vs_masked_sdpa, check_keep_one_and_all, check_reuse_identity,
     check_block_topk_bruteforce, check_raster_groups, check_no_residual, check_centred_hash,
+    check_morton_groups,
 ]

@@ -89,6 +89,16 @@ def _mean_first_half(q):
     return q64[: q64.shape[0] // 2].mean(axis=0)
 
 
+def _morton_xy_swapped(grid):
+    tt, yy, xx = np.meshgrid(*(np.arange(n) for n in grid), indexing="ij")
+    code = orc.morton_code(tt.ravel(), xx.ravel(), yy.ravel())
+    return np.argsort(code, kind="stable").astype(np.int32)
+
+
+def _morton_code_t_low(t, y, x):
+    return orig_morton_code(y, x, t)
+
+
 def _raster_reversed(n):
     return np.arange(n - 1, -1, -1, dtype=np.int32)
 
@@ -99,6 +109,7 @@ def _reuse_no_residual(q_t, k_t, v_t, rows, idx, residual, scale):
 
 
 orig_select = orc.select_group
+orig_morton_code = orc.morton_code
 
 MUTANTS = {
     "hash >= 0": ("hash_keys", _hash_ge),
@@ -118,6 +129,8 @@ MUTANTS = {
     "raster order reversed": ("raster_permutation", _raster_reversed),
     "centred hash not centred": ("centred_hash_keys", _centred_hash_uncentred),
     "mean over half the queries": ("query_mean", _mean_first_half),
+    "morton x and y swapped": ("morton_permutation", _morton_xy_swapped),
+    "morton t in the low bit": ("morton_code", _morton_code_t_low),
 }
 
 

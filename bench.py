@@ -70,6 +70,8 @@ def parse():
                     help="run one plain 1 GiB device-to-device copy first (a known-size reference for HBM counters)")
     ap.add_argument("--cpu-groups", type=int, default=288, help="oracle groups sampled per sampled head")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 8))
+    ap.add_argument("--grouping", default="morton", choices=["morton", "hash", "raster", "centred"],
+                    help="query grouping: Z-curve over the latent grid (default), sign hash, raster, centred hash")
     ap.add_argument("--ablation", action="store_true",
                     help="add the failure-mode ablations (raster groups, 64-key blocks, no residual)")
     ap.add_argument("--sweep", action="store_true",
@@ -191,7 +193,7 @@ def rel_l2(a, b):
     return float(torch.linalg.vector_norm(a.float() - b.float()) / torch.linalg.vector_norm(b.float()))
 
 
-def sweep(w, X, threads, scale):
+def sweep(w, X, threads, scale, grouping):
     """Denoising-loop sweep: for each (keep, G), steps 0..S-1 with selection on
     the steps divisible by the re-selection interval and reuse on the others;
     every step's output is compared with dense attention on that step."""
@@ -221,7 +223,8 @@ def sweep(w, X, threads, scale):
             ws = torch.empty(mcs.workspace_bytes(X[0][0], G), dtype=torch.uint8, device="cuda")
             mb = torch.empty(int(mcs.meta_layout(H, N, d, 1, G, keeps).bytes), dtype=torch.uint8, device="cuda")
             out = torch.empty_like(X[0][0])
-            mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws)  # warm-up
+            gkw = grouping_kw(wk, grouping)
+            mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws, **gkw)  # warm-up
             torch.cuda.synchronize()
             sel_ms, reuse_ms, err = [], [], []
             meta = None
@@ -230,7 +233,7 @@ def sweep(w, X, threads, scale):
                 if t % R == 0:
                     e0.record(stream)
                     meta, od = mcs.select(*X[t], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws,
-                                          return_dense=True)
+                                          return_dense=True, **gkw)
                     e1.record(stream)
                     torch.cuda.synchronize()
                     sel_ms.append(e0.elapsed_time(e1))
@@ -261,17 +264,24 @@ def sweep(w, X, threads, scale):
     return {"steps": S, "reselect_every": R, "dense_ms": round(dense_med, 4), "points": points}
 
 
-ABLATIONS = [
-    ("mc-sparse", dict(grouping="hash", kv_block=1, residual=True)),
-    ("no residual", dict(grouping="hash", kv_block=1, residual=False)),
-    ("64-key blocks", dict(grouping="hash", kv_block=64, residual=True)),
-    ("raster groups", dict(grouping="raster", kv_block=1, residual=True)),
-    ("centred-hash groups", dict(grouping="centred", kv_block=1, residual=True)),
-    ("raster groups + 64-key blocks + no residual", dict(grouping="raster", kv_block=64, residual=False)),
-]
+def ablations(base):
+    """Each row changes one choice of the benchmarked configuration (`base`
+    grouping, single KV tokens, residual), then the coarse three together."""
+    rows = [("benchmarked: %s groups" % base, dict(grouping=base, kv_block=1, residual=True)),
+            ("no residual", dict(grouping=base, kv_block=1, residual=False)),
+            ("64-key blocks", dict(grouping=base, kv_block=64, residual=True))]
+    for g in ("morton", "hash", "centred", "raster"):
+        if g != base:
+            rows.append(("%s groups" % g, dict(grouping=g, kv_block=1, residual=True)))
+    rows.append(("raster groups + 64-key blocks + no residual", dict(grouping="raster", kv_block=64, residual=False)))
+    return rows
 
 
-def ablation(w, X, keeps, scale):
+def grouping_kw(w, grouping):
+    return dict(grouping=grouping, grid=w.grid) if grouping == "morton" else dict(grouping=grouping)
+
+
+def ablation(w, X, keeps, scale, base):
     """Each failure-mode ablation on the workload's segment (selection on step
     0, reuse on steps 1..T): timings and the relative L2 of every reuse step
     against dense attention on that step."""
@@ -286,10 +296,11 @@ def ablation(w, X, keeps, scale):
     ws = torch.empty(mcs.workspace_bytes(X[0][0], G), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(X[0][0])
     rows = []
-    for name, opt in ABLATIONS:
+    for name, opt in ablations(base):
         if opt["kv_block"] > 1 and (N % opt["kv_block"] or np.any(keeps % opt["kv_block"])):
             rows.append({"variant": name, "skipped": "N or keep not whole 64-key blocks"})
             continue
+        opt = dict(opt, **grouping_kw(w, opt["grouping"]))
         mb = torch.empty(int(mcs.meta_layout(H, N, d, 1, G, keeps).bytes), dtype=torch.uint8, device="cuda")
         mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws, **opt)  # warm-up
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * T + 2)]
@@ -304,7 +315,8 @@ def ablation(w, X, keeps, scale):
             err.append(rel_l2(out, dense[t]))
         torch.cuda.synchronize()
         reuse = [e[2 * t].elapsed_time(e[2 * t + 1]) for t in range(1, T + 1)]
-        rows.append({"variant": name, **opt, "select_ms": round(e[0].elapsed_time(e[1]), 3),
+        rows.append({"variant": name, **{k: (list(v) if k == "grid" else v) for k, v in opt.items()},
+                     "select_ms": round(e[0].elapsed_time(e[1]), 3),
                      "reuse_ms": round(float(np.mean(reuse)), 4),
                      "rel_l2_step1": round(err[0], 6), "rel_l2_mean": round(float(np.mean(err)), 6),
                      "rel_l2_final": round(err[-1], 6)})
@@ -360,7 +372,8 @@ def main():
     def segment(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        meta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=meta_buf, workspace=ws)
+        meta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=meta_buf, workspace=ws,
+                             **grouping_kw(w, args.grouping))
         if ev is not None:
             ev[1].record(stream)
         for t in range(1, T + 1):
@@ -406,8 +419,8 @@ def main():
         fid[str(t)] = round(float(torch.linalg.vector_norm(o_s - o_d) / torch.linalg.vector_norm(o_d)), 6)
     torch.cuda.synchronize()
 
-    sweep_res = sweep(w, X, args.threads, scale) if args.sweep else None
-    ablation_res = ablation(w, X, keeps, scale) if args.ablation else None
+    sweep_res = sweep(w, X, args.threads, scale, args.grouping) if args.sweep else None
+    ablation_res = ablation(w, X, keeps, scale, args.grouping) if args.ablation else None
     peak_mem = int(torch.cuda.max_memory_allocated())
 
     reuse_mean = float(np.mean(reuse_ms))
@@ -422,7 +435,8 @@ def main():
         try:
             with open(TRAFFIC_FILE) as f:
                 tr = json.load(f)
-            if tr.get("source_sha") == src_hash(ATTN_SRC) and tr.get("workload") == args.workload:
+            if (tr.get("source_sha") == src_hash(ATTN_SRC) and tr.get("workload") == args.workload
+                    and tr.get("grouping", "hash") == args.grouping and args.keep is None and args.group is None):
                 traffic = tr.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
@@ -440,7 +454,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded DiT-shaped generator; no model weights)",
         "config": {"workload": describe(w, keeps), "heads": H, "seq_len": N, "head_dim": d, "group": G,
-                   "keep": [int(x) for x in sorted(set(keeps.tolist()))], "reuse_steps": T},
+                   "keep": [int(x) for x in sorted(set(keeps.tolist()))], "reuse_steps": T,
+                   "grouping": {"morton": "z-curve over the %dx%dx%d latent grid" % w.grid,
+                                "hash": "8-bit sign hash", "raster": "raster order",
+                                "centred": "centred 8-bit sign hash"}[args.grouping]},
         "reuse_ms_median": round(float(np.median(reuse_ms)), 4),
         "reuse_ms_p10_p90": [round(float(np.percentile(reuse_ms, 10)), 4),
                              round(float(np.percentile(reuse_ms, 90)), 4)],

@@ -198,13 +198,17 @@ mcs_status mcs_select(const mcs_attn_desc* desc, const void* q, const void* k, c
  * tokens; the list in section "MC-Sparse: three failure modes, one fix" of
  * "The quality cliff nobody admits to").  Each field swaps one of MC-Sparse's
  * choices for the coarser one; all zero-initialised fields but kv_block and
- * residual select MC-Sparse itself.
+ * residual select MC-Sparse itself.  Two further groupings order the queries
+ * differently: the centred hash, and the Z-curve over the latent grid.
  */
 typedef enum mcs_grouping {
   MCS_GROUPING_HASH = 0,          /* 8-bit sign hash + stable sort (MC-Sparse) */
   MCS_GROUPING_RASTER = 1,        /* runs of G tokens in raster order (perm = identity) */
-  MCS_GROUPING_CENTRED_HASH = 2   /* sign hash of q_i - mean_i' q_i' (per head; float64 sums in token
+  MCS_GROUPING_CENTRED_HASH = 2,  /* sign hash of q_i - mean_i' q_i' (per head; float64 sums in token
                                      order, each product and addition rounded separately) + stable sort */
+  MCS_GROUPING_MORTON = 3         /* the tokens, a raster-ordered (T, Y, X) latent grid with token
+                                     (t*Y + y)*X + x, in Z-curve order (bits of x, y, t interleaved, x
+                                     lowest): a group of 64 is a 4x4x4 block of the grid */
 } mcs_grouping;
 
 typedef struct mcs_select_options {
@@ -214,7 +218,8 @@ typedef struct mcs_select_options {
                         multiples of 64 (else MCS_ERROR_UNSUPPORTED_SHAPE) */
   int32_t residual;  /* 1: cache O_dense - O_sparse (MC-Sparse); 0: cache zeros, so reuse returns the
                         sparse output renormalised over the kept keys alone */
-  int32_t reserved;  /* must be 0 */
+  int32_t grid_t, grid_y, grid_x;  /* MCS_GROUPING_MORTON: the latent grid, each in [1, 1024], product N;
+                                      0 for every other grouping */
 } mcs_select_options;
 
 /*

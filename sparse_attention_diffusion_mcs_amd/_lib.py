@@ -24,6 +24,7 @@ MCS_HASH_BITS = 8
 MCS_GROUPING_HASH = 0
 MCS_GROUPING_RASTER = 1
 MCS_GROUPING_CENTRED_HASH = 2
+MCS_GROUPING_MORTON = 3
 
 EXPORTS = ("mcs_version", "mcs_status_string", "mcs_last_hip_error", "mcs_dense_attn", "mcs_meta_layout",
            "mcs_meta_bytes", "mcs_select_workspace_bytes", "mcs_meta_init", "mcs_select", "mcs_select_ex",
@@ -46,7 +47,7 @@ class Meta(ctypes.Structure):
 
 class SelectOptions(ctypes.Structure):
     _fields_ = [("grouping", ctypes.c_int32), ("kv_block", ctypes.c_int32), ("residual", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("grid_t", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_x", ctypes.c_int32)]
 
 
 class McsError(RuntimeError):

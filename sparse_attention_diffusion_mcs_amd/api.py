@@ -170,9 +170,10 @@ def meta_init(q, group_size, keep, meta_buf=None, stream=None) -> MetaCache:
 
 
 def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace=None, heads_per_chunk=None,
-           return_dense=False, stream=None, grouping="hash", kv_block=1, residual=True):
-    """Selection step (mcs_select; mcs_select_ex for the failure-mode
-    ablations: grouping "raster" or "centred", kv_block 64, residual False).  Returns
+           return_dense=False, stream=None, grouping="hash", kv_block=1, residual=True, grid=None):
+    """Selection step (mcs_select; mcs_select_ex for the other groupings --
+    "raster", "centred", "morton" with the (T, Y, X) `grid` -- and the
+    failure-mode ablations kv_block 64, residual False).  Returns
     (MetaCache, dense output or None)."""
     _check_qkv(q, k, v)
     H, N, d = q.shape
@@ -198,10 +199,11 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
                                    _ptr(o_dense), ctypes.byref(m), _stream(stream)), "mcs_select")
     else:
         codes = {"hash": L.MCS_GROUPING_HASH, "raster": L.MCS_GROUPING_RASTER,
-                 "centred": L.MCS_GROUPING_CENTRED_HASH}
+                 "centred": L.MCS_GROUPING_CENTRED_HASH, "morton": L.MCS_GROUPING_MORTON}
         if grouping not in codes:
             raise ValueError(f"unknown grouping {grouping!r}")
-        opts = L.SelectOptions(codes[grouping], int(kv_block), 1 if residual else 0, 0)
+        gt, gy, gx = (int(x) for x in grid) if grouping == "morton" else (0, 0, 0)
+        opts = L.SelectOptions(codes[grouping], int(kv_block), 1 if residual else 0, gt, gy, gx)
         L.check(L.lib().mcs_select_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
                                       ctypes.byref(opts), _ptr(meta_buf), meta_buf.numel(), _ptr(workspace),
                                       workspace.numel(), _ptr(o_dense), ctypes.byref(m), _stream(stream)),

@@ -52,6 +52,8 @@ hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, const i
 hipError_t launch_block_scores(const float* colsum, int ldc, float* bs, int ldb, long long rows, int nb,
                                hipStream_t s);
 hipError_t launch_iota_perm(int32_t* perm, int H, int N, hipStream_t s);
+// Z-curve order of a raster-ordered (T, Y, X) grid, N = T * Y * X, every dim <= 1024
+hipError_t launch_morton_perm(int32_t* perm, int H, int N, int T, int Y, int X, hipStream_t s);
 hipError_t launch_zero_floats(float* p, long long n, hipStream_t s);
 // Writes `nbytes` bytes from host memory to device memory through kernel
 // arguments (asynchronous on s, safe for pageable and stack host memory).

@@ -259,13 +259,19 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
   if ((st = check_desc(d)) != MCS_SUCCESS) return st;
   if ((st = check_group_keep(d, G, keep)) != MCS_SUCCESS) return st;
   if (!meta_out) return MCS_ERROR_INVALID_VALUE;
-  mcs_select_options o{MCS_GROUPING_HASH, 1, 1, 0};
+  mcs_select_options o{MCS_GROUPING_HASH, 1, 1, 0, 0, 0};
   if (opts) o = *opts;
   if ((o.grouping != MCS_GROUPING_HASH && o.grouping != MCS_GROUPING_RASTER &&
-       o.grouping != MCS_GROUPING_CENTRED_HASH) ||
-      (o.kv_block != 1 && o.kv_block != 64) ||
-      (o.residual != 0 && o.residual != 1) || o.reserved != 0)
+       o.grouping != MCS_GROUPING_CENTRED_HASH && o.grouping != MCS_GROUPING_MORTON) ||
+      (o.kv_block != 1 && o.kv_block != 64) || (o.residual != 0 && o.residual != 1))
     return MCS_ERROR_INVALID_VALUE;
+  if (o.grouping == MCS_GROUPING_MORTON) {
+    for (int g : {o.grid_t, o.grid_y, o.grid_x})
+      if (g < 1 || g > 1024) return MCS_ERROR_INVALID_VALUE;
+    if ((int64_t)o.grid_t * o.grid_y * o.grid_x != d->seq_len) return MCS_ERROR_INVALID_VALUE;
+  } else if (o.grid_t != 0 || o.grid_y != 0 || o.grid_x != 0) {
+    return MCS_ERROR_INVALID_VALUE;
+  }
   if (o.kv_block > 1) {
     if (d->seq_len % o.kv_block) return MCS_ERROR_UNSUPPORTED_SHAPE;
     for (int h = 0; h < d->num_heads; ++h)
@@ -309,6 +315,8 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
     if ((e = mcs::launch_fill_bytes(dproj, proj64.data(), proj64.size() * 8, s)) != hipSuccess) return hip_fail(e);
     if ((e = mcs::launch_hash_keys(q, d->dtype, dproj, mean, keys, H, N, D, s)) != hipSuccess) return hip_fail(e);
     if ((e = mcs::launch_perm_sort(keys, perm, H, N, s)) != hipSuccess) return hip_fail(e);
+  } else if (o.grouping == MCS_GROUPING_MORTON) {
+    if ((e = mcs::launch_morton_perm(perm, H, N, o.grid_t, o.grid_y, o.grid_x, s)) != hipSuccess) return hip_fail(e);
   } else if ((e = mcs::launch_iota_perm(perm, H, N, s)) != hipSuccess) {
     return hip_fail(e);
   }

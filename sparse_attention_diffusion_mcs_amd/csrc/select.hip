@@ -307,6 +307,38 @@ __global__ void iota_perm_kernel(int32_t* __restrict__ perm, long long total, in
     perm[i] = (int32_t)(i % N);
 }
 
+// Z-curve groups over a raster-ordered (T, Y, X) grid.  A token's Z-curve
+// code interleaves the bits of x, y, t (x lowest); its rank among the grid's
+// codes is found without sorting: walking the code from the top bit, every
+// 1 bit adds the number of grid cells in the lower half of the current
+// Z-curve subtree (an axis-aligned box clipped to the grid), then descends
+// into the upper half.  perm[h][rank] = token for every head.
+__device__ __forceinline__ long long clipped(int lo, int len, int size) {
+  return lo >= size ? 0 : (long long)(min(lo + len, size) - lo);
+}
+
+__global__ void morton_perm_kernel(int32_t* __restrict__ perm, int H, int N, int T, int Y, int X) {
+  const int tok = blockIdx.x * blockDim.x + threadIdx.x;
+  if (tok >= N) return;
+  const int x = tok % X, y = (tok / X) % Y, t = tok / (X * Y);
+  const int size[3] = {X, Y, T}, coord[3] = {x, y, t};
+  int lo[3] = {0, 0, 0}, len[3] = {1024, 1024, 1024};
+  long long rank = 0;
+  for (int p = 29; p >= 0; --p) {
+    const int a = p % 3, half = len[a] >> 1;
+    if ((coord[a] >> (p / 3)) & 1) {
+      long long vol = clipped(lo[a], half, size[a]);
+#pragma unroll
+      for (int o = 0; o < 3; ++o)
+        if (o != a) vol *= clipped(lo[o], len[o], size[o]);
+      rank += vol;
+      lo[a] += half;
+    }
+    len[a] = half;
+  }
+  for (int h = 0; h < H; ++h) perm[(size_t)h * N + rank] = tok;
+}
+
 __global__ void zero_floats_kernel(float* __restrict__ p, long long n) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
     p[i] = 0.f;
@@ -405,6 +437,12 @@ hipError_t launch_iota_perm(int32_t* perm, int H, int N, hipStream_t s) {
   if (total == 0) return hipSuccess;
   const long long blocks = std::min<long long>((total + 255) / 256, 65536);
   hipLaunchKernelGGL(iota_perm_kernel, dim3((unsigned)blocks), dim3(256), 0, s, perm, total, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_morton_perm(int32_t* perm, int H, int N, int T, int Y, int X, hipStream_t s) {
+  if (H == 0 || N == 0) return hipSuccess;
+  hipLaunchKernelGGL(morton_perm_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, perm, H, N, T, Y, X);
   return hipGetLastError();
 }
 

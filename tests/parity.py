@@ -147,7 +147,7 @@ def sample_groups(ng, extra=4, seed=0):
     return sorted(base | {int(x) for x in pick})
 
 
-def check_units(p: Problem, meta, od, outs, sc, heads, groups, label=""):
+def check_units(p: Problem, meta, od, outs, sc, heads, groups, label="", grouping="hash"):
     """Compares the sampled (head, group) units of a GPU run with the oracle:
     perm of the whole head, kept keys, dense rows, residual and the reuse
     outputs of every generated step.  Returns the number of kept-key sets
@@ -155,7 +155,8 @@ def check_units(p: Problem, meta, od, outs, sc, heads, groups, label=""):
     exact = total = 0
     for h in heads:
         q, k, v = p.heads_np[(h, 0)]
-        perm_o = orc.group_permutation(orc.hash_keys(q, p.proj()))
+        perm_o = orc.select_head(q, k, v, p.proj(), p.G, int(p.keeps[h]), sc, groups=[], grouping=grouping,
+                                 grid=p.grid).perm
         perm_g = meta.perm[h].cpu().numpy()
         assert np.array_equal(perm_g, perm_o), f"{label} head {h}: perm differs"
         kh = int(p.keeps[h])

@@ -1,7 +1,7 @@
-"""GPU parity of the failure-mode ablations (mcs_select_ex): raster query
-groups, centred-hash groups, whole 64-key KV blocks, and no residual, each
-against the CPU oracle run with the same option on every group of every
-head (the permutation bit-exact)."""
+"""GPU parity of the options of mcs_select_ex: raster, centred-hash and
+Z-curve query groups, whole 64-key KV blocks, and no residual, each against
+the CPU oracle run with the same option on every group of every head (the
+permutation bit-exact)."""
 
 import numpy as np
 import pytest
@@ -23,6 +23,9 @@ CASES = {
     "block64_fp32_d64_g128": ((2, 8, 16), 1, 64, "fp32", 128, [128], "hash", 64, True, 125),
     "centred_bf16_d128_ragged": ((3, 9, 23), 3, 128, "bf16", 64, [96, 160, 300], "centred", 1, True, 127),
     "centred_fp32_d64_g128": ((2, 10, 20), 2, 64, "fp32", 128, [50, 200], "centred", 1, True, 128),
+    "morton_bf16_d128": ((4, 8, 16), 2, 128, "bf16", 64, [128, 320], "morton", 1, True, 129),
+    "morton_ragged_bf16_d64_g128": ((3, 9, 23), 2, 64, "bf16", 128, [100, 250], "morton", 1, True, 130),
+    "morton_block64_fp32": ((2, 8, 16), 1, 128, "fp32", 64, [64], "morton", 64, True, 131),
 }
 
 
@@ -35,8 +38,9 @@ def test_ablation_parity(name):
           f"residual={resid}", flush=True)
     p = build_problem(grid, H, d, dtype, G, keeps, 0.02, [2], wid=wid)
     sc = scale_for(d)
+    grid = grid if grouping == "morton" else None
     meta, od = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc, return_dense=True, grouping=grouping,
-                          kv_block=kvb, residual=resid)
+                          kv_block=kvb, residual=resid, grid=grid)
     out = mcs.sparse_attn(*p.dev[2], meta, scale=sc)
     torch.cuda.synchronize()
     perm_g = meta.perm.cpu().numpy()
@@ -44,7 +48,7 @@ def test_ablation_parity(name):
     same = 0
     for h in range(H):
         q, k, v = p.heads_np[(h, 0)]
-        hm = orc.select_head(q, k, v, p.proj(), G, int(p.keeps[h]), sc, groups=[], grouping=grouping)
+        hm = orc.select_head(q, k, v, p.proj(), G, int(p.keeps[h]), sc, groups=[], grouping=grouping, grid=grid)
         assert np.array_equal(perm_g[h], hm.perm), f"head {h}: perm differs"
         assert_close(od_g[h], orc.dense_attention(q, k, v, sc), p.dtype, f"head {h} dense output")
         kh = int(p.keeps[h])

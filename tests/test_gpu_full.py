@@ -21,7 +21,7 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def run_workload(w, steps, heads, label, select_step=0):
+def run_workload(w, steps, heads, label, select_step=0, grouping="hash"):
     print(f"[full] {label}: H={w.heads} N={w.seq_len} d={w.head_dim} G={w.group} keeps={sorted(set(w.keeps()))}",
           flush=True)
     keeps = w.keeps()
@@ -34,10 +34,11 @@ def run_workload(w, steps, heads, label, select_step=0):
         for h in heads:
             p.heads_np[(h, 0)] = p.heads_np[(h, select_step)]
         p.dev[0] = p.dev[select_step]
-    meta, od = mcs.select(*p.dev[0], w.group, keeps, p.proj(), scale=sc, return_dense=True)
+    meta, od = mcs.select(*p.dev[0], w.group, keeps, p.proj(), scale=sc, return_dense=True, grouping=grouping,
+                          grid=w.grid if grouping == "morton" else None)
     outs = {t: mcs.sparse_attn(*p.dev[t], meta, scale=sc) for t in steps}
     torch.cuda.synchronize()
-    exact, total = check_units(p, meta, od, outs, sc, heads, sample_groups(p.ng), label)
+    exact, total = check_units(p, meta, od, outs, sc, heads, sample_groups(p.ng), label, grouping)
     print(f"[full] {label}: kept-key sets equal to the oracle's: {exact}/{total}", flush=True)
 
 
@@ -45,6 +46,19 @@ def test_workload2_video_layer():
     _need_gpu()
     w = WORKLOADS[2]
     run_workload(w, [1, 5, 10], [0, w.heads - 1], "workload 2")
+
+
+def test_workload2_zcurve_groups():
+    """The benchmark's grouping: Z-curve order over the 16 x 30 x 52 grid."""
+    _need_gpu()
+    w = WORKLOADS[2]
+    run_workload(w, [1, 10], [0, w.heads - 1], "workload 2 z-curve", grouping="morton")
+
+
+def test_workload5_zcurve_groups_g128():
+    _need_gpu()
+    w = WORKLOADS[5].with_(group=128)
+    run_workload(w, [9], [0, w.heads - 1], "workload 5 z-curve G=128", grouping="morton")
 
 
 def test_workload3_long_video_layer():

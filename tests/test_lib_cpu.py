@@ -153,17 +153,20 @@ def test_select_ex_options_validation(lib):
                                  NULL, ctypes.byref(m), NULL)
 
     O = L.SelectOptions
-    assert call(O(3, 1, 1, 0)) == L.MCS_ERROR_INVALID_VALUE       # unknown grouping
-    assert call(O(0, 32, 1, 0)) == L.MCS_ERROR_INVALID_VALUE      # block size other than 1 / 64
-    assert call(O(0, 1, 2, 0)) == L.MCS_ERROR_INVALID_VALUE       # residual flag not 0 / 1
-    assert call(O(0, 1, 1, 7)) == L.MCS_ERROR_INVALID_VALUE       # reserved field set
+    assert call(O(4, 1, 1)) == L.MCS_ERROR_INVALID_VALUE          # unknown grouping
+    assert call(O(0, 32, 1)) == L.MCS_ERROR_INVALID_VALUE         # block size other than 1 / 64
+    assert call(O(0, 1, 2)) == L.MCS_ERROR_INVALID_VALUE          # residual flag not 0 / 1
+    assert call(O(0, 1, 1, 2, 8, 8)) == L.MCS_ERROR_INVALID_VALUE   # grid given to a non-grid grouping
+    assert call(O(3, 1, 1)) == L.MCS_ERROR_INVALID_VALUE          # Z-curve without a grid
+    assert call(O(3, 1, 1, 2, 8, 9)) == L.MCS_ERROR_INVALID_VALUE   # grid does not hold N tokens
+    assert call(O(3, 1, 1, 1, 2, 2048)) == L.MCS_ERROR_INVALID_VALUE  # a dimension above 1024
     odd, op = _i32([64, 100])
-    assert call(O(0, 64, 1, 0), keep_p=op) == L.MCS_ERROR_UNSUPPORTED_SHAPE   # keep not whole blocks
+    assert call(O(0, 64, 1), keep_p=op) == L.MCS_ERROR_UNSUPPORTED_SHAPE   # keep not whole blocks
     d2 = ctypes.byref(_desc(H, 130, d))
-    assert call(O(1, 64, 0, 0), desc=d2) == L.MCS_ERROR_UNSUPPORTED_SHAPE     # N not whole blocks
+    assert call(O(1, 64, 0), desc=d2) == L.MCS_ERROR_UNSUPPORTED_SHAPE     # N not whole blocks
     # the options do not bypass the ordinary checks
     zero, zp = _i32([0, 64])
-    assert call(O(1, 1, 0, 0), keep_p=zp) == L.MCS_ERROR_INVALID_VALUE
+    assert call(O(1, 1, 0), keep_p=zp) == L.MCS_ERROR_INVALID_VALUE
 
 
 def test_sparse_validation(lib):

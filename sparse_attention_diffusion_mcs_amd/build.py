@@ -6,6 +6,7 @@
 from __future__ import annotations
 
 import concurrent.futures as cf
+import ctypes
 import os
 import shutil
 import subprocess
@@ -60,6 +61,14 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # A kernel whose host-side compilation hits a deferred error links with an
+    # undefined launch stub; loading the library here turns that into a build
+    # failure instead of a failure on first use.
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"the linked library does not load: {e}") from e
     os.replace(tmp, LIB)
     return LIB
 

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
-  __shared__ float red[MODE == MODE_SELECT ? 2 : 1][NW][BK];
+  __shared__ float red[MODE == MODE_SELECT ? 2 : 1][NW][MODE == MODE_SELECT ? 2 * BK : 1];
   __shared__ float lse_s[MODE == MODE_SELECT ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
@@ -387,6 +387,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   if constexpr (MODE != MODE_SELECT) return;
 
   // ---- pass 2 (selection): per-group key scores c(j) = sum_i exp(s_ij - lse_i)
+  // Only K is needed, so a stage holds two K tiles (2 BK keys) and the
+  // barrier, the cross-wave reduction and the flush to global memory come
+  // once per 2 BK keys; the two halves are scored one after the other.
   __syncthreads();
   float nlse[2][4];
 #pragma unroll
@@ -394,65 +397,80 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) nlse[rb][i] = -lse_s[32 * w + 16 * rb + 4 * lq + i];
 
+  constexpr int BK2 = 2 * BK;
+  const int nt2 = (N + BK2 - 1) / BK2;
   const int wpg = a.G / 32;   // waves per group
   const int gpt = BM / a.G;   // groups per tile
-  auto flush = [&](int j) {   // cross-wave sums of tile j -> colsum
-    for (int t = tid; t < gpt * BK; t += NW * 64) {
-      const int gi = t / BK, col = t % BK, tok = j * BK + col;
+  auto issue_k2 = [&](char* stage, int jj) {  // keys jj*BK2 .. +BK2-1 into both halves of a stage
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+      const int ii = w + NW * u;
+      const int t = ii * GE::RPI + lane / GE::CPR;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int r = jj * BK2 + half * BK + t;
+        const int row = r < N - 1 ? r : N - 1;
+        const int off = (row * GE::ROWB) | chunk_off[u];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + half * GE::TILE + ii * 1024), 16, off, 0, 0, 0);
+      }
+    }
+  };
+  auto flush = [&](int jj) {  // cross-wave sums of super-tile jj -> colsum
+    for (int t = tid; t < gpt * BK2; t += NW * 64) {
+      const int gi = t / BK2, col = t % BK2, tok = jj * BK2 + col;
       const int g = row0 / a.G + gi;
       if (tok < N && g < a.ng) {
         float sum = 0.f;
-        for (int ww = 0; ww < wpg; ++ww) sum += red[j & 1][gi * wpg + ww][col];
+        for (int ww = 0; ww < wpg; ++ww) sum += red[jj & 1][gi * wpg + ww][col];
         a.colsum[((size_t)hs * a.ng + g) * a.ldc + tok] = sum;
       }
     }
   };
-  auto score_tile = [&](int j, const char* cur, char* nxt) {
+  auto score_tile = [&](int jj, const char* cur, char* nxt) {
     wait_vm<0>();
     __syncthreads();
-    if (j + 1 < nt) {
-      issue(nxt, false);
-      fetch_rows(j + 2);
-    }
-    if (j > 0) flush(j - 1);
-    bf16x8 kf[KK][TB];
+    if (jj + 1 < nt2) issue_k2(nxt, jj + 1);
+    if (jj > 0) flush(jj - 1);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int half = 0; half < 2; ++half) {
+      const char* kt = cur + half * GE::TILE;
+      bf16x8 kf[KK][TB];
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) kf[kk][tb] = kfrag(cur, tb, kk);
-    // S[row][token]: lane holds rows 16 rb + 4 lq + i of token 16 tb + lr
-    f32x4 s[2][TB];
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) s[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          s[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rb][kk], kf[kk][tb], s[rb][tb], 0, 0, 0);
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      float cs = 0.f;
+        for (int tb = 0; tb < TB; ++tb) kf[kk][tb] = kfrag(kt, tb, kk);
+      // S[row][token]: lane holds rows 16 rb + 4 lq + i of token 16 tb + lr
+      f32x4 s[2][TB];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cs += fast_exp2(fmaf(s[rb][tb][i], sl2, nlse[rb][i]));
-      cs = quad_rows_sum(cs);
-      if (lq == 0) red[j & 1][w][16 * tb + lr] = cs;
+        for (int tb = 0; tb < TB; ++tb) s[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            s[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rb][kk], kf[kk][tb], s[rb][tb], 0, 0, 0);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        float cs = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cs += fast_exp2(fmaf(s[rb][tb][i], sl2, nlse[rb][i]));
+        cs = quad_rows_sum(cs);
+        if (lq == 0) red[jj & 1][w][half * BK + 16 * tb + lr] = cs;
+      }
     }
   };
-  fetch_rows(0);
-  if (nt > 0) issue(st0, false);
-  fetch_rows(1);
-  for (int j = 0; j < nt; j += 2) {
-    score_tile(j, st0, st1);
-    if (j + 1 < nt) score_tile(j + 1, st1, st0);
+  if (nt2 > 0) issue_k2(st0, 0);
+  for (int jj = 0; jj < nt2; jj += 2) {
+    score_tile(jj, st0, st1);
+    if (jj + 1 < nt2) score_tile(jj + 1, st1, st0);
   }
   __syncthreads();
-  if (nt > 0) flush(nt - 1);
+  if (nt2 > 0) flush(nt2 - 1);
 }
 
 // KV tile size: 32 tokens at d = 128 (the batched K and V operand reads of a

@@ -215,9 +215,26 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
     const int nb = pass == 2 ? 1024 : 2048;
     for (int b = tid; b < 2048; b += TK_NT) hist[b] = 0;
     __syncthreads();
-    for (int j = tid; j < N; j += TK_NT) {
-      const uint32_t u = row[j];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1);
+    // 16 consecutive scores per thread and step: four 16-byte loads in flight
+    // before the histogram updates (rows start 256-byte aligned)
+    for (int j0 = 16 * tid; j0 < N; j0 += 16 * TK_NT) {
+      uint32_t u[16];
+      if (j0 + 16 <= N) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 x = *reinterpret_cast<const uint4*>(row + j0 + 4 * v);
+          u[4 * v] = x.x;
+          u[4 * v + 1] = x.y;
+          u[4 * v + 2] = x.z;
+          u[4 * v + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) u[e] = (j0 + e < N) ? row[j0 + e] : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (j0 + e < N && (u[e] & pmask) == prefix) atomicAdd(&hist[(u[e] >> shift) & (nb - 1)], 1);
     }
     __syncthreads();
     // thread t owns bins [t*per, (t+1)*per); `above` = elements in higher bins
@@ -251,8 +268,16 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
   for (int t0 = 0; t0 < N; t0 += 4 * TK_NT) {
     const int j0 = t0 + 4 * tid;
     uint32_t u[4];
+    if (j0 + 4 <= N) {
+      const uint4 x = *reinterpret_cast<const uint4*>(row + j0);
+      u[0] = x.x;
+      u[1] = x.y;
+      u[2] = x.z;
+      u[3] = x.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = (j0 + e < N) ? row[j0 + e] : 0u;
+      for (int e = 0; e < 4; ++e) u[e] = (j0 + e < N) ? row[j0 + e] : 0u;
+    }
     int ngt = 0, neq = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

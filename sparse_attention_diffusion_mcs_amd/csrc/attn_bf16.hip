@@ -39,6 +39,7 @@ namespace mcs {
 namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr float kLoSkip = 8.0f;        // log2 units: tiles below 2^-8 of the running max carry P as bf16 only
 constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -320,12 +321,32 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
         const bf16x8 vf = as_bf16x8(
             make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y));
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < 2; ++rb)
           oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kc][rb], oacc[db][rb], 0, 0, 0);
-          if constexpr (PRECISE_PV)
-            oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[kc][rb], oacc[db][rb], 0, 0, 0);
-        }
       }
+    if constexpr (PRECISE_PV) {
+      // The low part only matters where probabilities are large: the rounding
+      // error of the output is dominated by its largest terms.  A tile whose
+      // probabilities all stay below 2^-kLoSkip of the running max skips its
+      // low-part products; their rounding errors are at most 2^-(9 + kLoSkip)
+      // of the largest term.  The decision is taken per wave from the tile's
+      // row maxima.
+      bool big = false;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) big |= mx[rb] > m_run[rb] - kLoSkip;
+      if (__ballot(big) != 0ull) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 vf = as_bf16x8(
+                make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y));
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[kc][rb], oacc[db][rb], 0, 0, 0);
+          }
+      }
+    }
   };
 
   fetch_rows(0);

@@ -26,6 +26,12 @@ for every keep fraction and group size, a 30-step loop with re-selection every
 of every step's output against dense attention on that step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--sweep] [--ablation]
+
+Two converters turn rocprofv3 results into the summaries kept in profiles/
+(no GPU needed):
+
+    python bench.py --trace-summary RESULTS.db OUT.md "TITLE" "COMMAND"
+    python bench.py --traffic-summary FETCH.db WRITE.db OUT.json GROUPING
 """
 
 from __future__ import annotations
@@ -325,7 +331,78 @@ def ablation(w, X, keeps, scale, base):
     return rows
 
 
+def trace_summary(db, out, title, command):
+    """Kernel-trace statistics of a rocprofv3 results database as markdown."""
+    import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    lines = [f"# {title}", "", f"command: `{command}`", "",
+             "Template arguments of `attn_bf16_kernel<d, waves, mode, tile>`: mode 0 = dense baseline, 1 = selection "
+             "dense pass with key scores, 2 = reuse step, 3 = selection-time sparse pass and residual. The reuse-step "
+             "average here is the kernel behind the bench's `value`.", "",
+             "| kernel | calls | total us | avg us | % |", "|---|---|---|---|---|"]
+    for name, calls, tot, avg, pct in cur.execute("select * from top_kernels limit 14"):
+        n = name.replace("(anonymous namespace)::", "")
+        n = n.split("(")[0] if "at::native" in n else n
+        lines.append(f"| `{n[:110]}` | {calls} | {tot:.1f} | {avg:.1f} | {pct:.2f} |")
+    lines += ["", "| kernel | vgpr | agpr | sgpr | lds | grid | wg |", "|---|---|---|---|---|---|---|"]
+    for r in cur.execute("select name, vgpr_count, accum_vgpr_count, sgpr_count, lds_size, grid_x, workgroup_x "
+                         "from kernels group by name"):
+        if "mcs::" in r[0]:
+            nm = r[0].replace("(anonymous namespace)::", "").split("(mcs")[0][:80]
+            lines.append(f"| `{nm}` | " + " | ".join(str(x) for x in r[1:]) + " |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def traffic_summary(fetch_db, write_db, out, grouping):
+    """HBM bytes per workload-2 reuse launch from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same
+    counter reads for the plain 1 GiB device copy of --copy-probe."""
+    import sqlite3
+
+    def per_kernel(db):
+        cur = sqlite3.connect(db).cursor()
+        cols = [c[1] for c in cur.execute("pragma table_info(counters_collection)")]
+        rows = [dict(zip(cols, r)) for r in cur.execute("select * from counters_collection")]
+        reuse = [r["value"] for r in rows if "attn_bf16_kernel<128, 2, 2, 32>" in r["kernel_name"]]
+        copies = [r for r in rows if "copy" in r["kernel_name"] and "bfloat16" not in r["kernel_name"]]
+        cp = max(copies, key=lambda r: r["value"])
+        return float(np.mean(reuse)), len(reuse), float(cp["value"]), cp["kernel_name"][:80]
+
+    f_reuse, n1, f_copy, cname = per_kernel(fetch_db)
+    w_reuse, n2, w_copy, _ = per_kernel(write_db)
+    gib = 1 << 30
+    fs, ws = gib / 1024 / f_copy, gib / 1024 / w_copy
+    H, N, d, ng, k = 24, 24960, 128, 390, 2496
+    compulsory = 3 * H * N * d * 2 + H * N * d * 4 + H * ng * k * 4 + H * N * d * 2 + H * N * 4
+    cmd = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c} -o pmc -- python3 bench.py --steps 1 --warmup 0 "
+           "--no-cpu-baseline --copy-probe --grouping " + grouping)
+    res = {
+        "kernel": "attn_bf16_kernel<128,2,REUSE,32> (reuse step)", "workload": 2, "grouping": grouping,
+        "source_sha": src_hash(ATTN_SRC),
+        "fetch_size_kib_per_launch": round(f_reuse, 1), "write_size_kib_per_launch": round(w_reuse, 1),
+        "copy_probe": {"bytes": gib, "kernel": cname, "fetch_size_kib": f_copy, "write_size_kib": w_copy,
+                       "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
+        "bytes_per_launch": int(round(f_reuse * 1024 * fs + w_reuse * 1024 * ws)),
+        "fetch_bytes": int(round(f_reuse * 1024 * fs)), "write_bytes": int(round(w_reuse * 1024 * ws)),
+        "launches_averaged": min(n1, n2), "compulsory_bytes": compulsory,
+        "commands": [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE"),
+                     f"python3 bench.py --traffic-summary {fetch_db} {write_db} {out} {grouping}"],
+        "note": "FETCH_SIZE counts L2 misses served by the fabric (MALL or HBM); each counter is scaled by what it "
+                "reads for a plain 1 GiB device copy (--copy-probe). Compulsory = one read of Q, K, V, residual, "
+                "idx, perm and the O write.",
+    }
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--trace-summary":
+        trace_summary(*sys.argv[2:6])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--traffic-summary":
+        traffic_summary(*sys.argv[2:6])
+        return
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",

@@ -147,7 +147,8 @@ def sample_groups(ng, extra=4, seed=0):
     return sorted(base | {int(x) for x in pick})
 
 
-def check_units(p: Problem, meta, od, outs, sc, heads, groups, label="", grouping="hash"):
+def check_units(p: Problem, meta, od, outs, sc, heads, groups, label="", grouping="hash", kv_block=1,
+                residual=True):
     """Compares the sampled (head, group) units of a GPU run with the oracle:
     perm of the whole head, kept keys, dense rows, residual and the reuse
     outputs of every generated step.  Returns the number of kept-key sets
@@ -166,16 +167,23 @@ def check_units(p: Problem, meta, od, outs, sc, heads, groups, label="", groupin
             s, e = ranges[g]
             rows = perm_o[s:e]
             rows_t = torch.from_numpy(rows.astype(np.int64)).to("cuda")
-            sel = orc.select_group(q, k, v, rows, kh, sc)
+            sel = orc.select_group(q, k, v, rows, kh, sc, kv_block=kv_block, residual=residual)
             gi = gidx[g].cpu().numpy()
-            exact += check_idx(gi, sel.scores, kh, p.N, f"{label} head {h} group {g}")
+            if kv_block == 1:
+                exact += check_idx(gi, sel.scores, kh, p.N, f"{label} head {h} group {g}")
+            else:
+                exact += check_blocks(gi, sel.scores, kh, p.N, kv_block, f"{label} head {h} group {g}")
             total += 1
             if od is not None:
                 assert_close(to_np(od[h].index_select(0, rows_t)), sel.o_dense, p.dtype,
                              f"{label} head {h} group {g} dense rows")
-            res_c = sel.o_dense - orc.sparse_attention(q[rows], k, v, gi, sc)
-            assert_close(to_np(meta.residual[h, s:e]), res_c, p.dtype, f"{label} head {h} group {g} residual",
-                         ref_norm=np.linalg.norm(sel.o_dense))
+            if residual:
+                res_c = sel.o_dense - orc.sparse_attention(q[rows], k, v, gi, sc)
+                assert_close(to_np(meta.residual[h, s:e]), res_c, p.dtype, f"{label} head {h} group {g} residual",
+                             ref_norm=np.linalg.norm(sel.o_dense))
+            else:
+                res_c = np.zeros_like(sel.o_dense)
+                assert float(meta.residual[h, s:e].abs().max()) == 0.0, f"{label} head {h} group {g} residual"
             for t, o in outs.items():
                 ref = orc.reuse_group(*p.heads_np[(h, t)], rows, gi, res_c, sc)
                 assert_close(to_np(o[h].index_select(0, rows_t)), ref, p.dtype,

@@ -21,7 +21,7 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def run_workload(w, steps, heads, label, select_step=0, grouping="hash"):
+def run_workload(w, steps, heads, label, select_step=0, grouping="hash", kv_block=1, residual=True):
     print(f"[full] {label}: H={w.heads} N={w.seq_len} d={w.head_dim} G={w.group} keeps={sorted(set(w.keeps()))}",
           flush=True)
     keeps = w.keeps()
@@ -35,10 +35,11 @@ def run_workload(w, steps, heads, label, select_step=0, grouping="hash"):
             p.heads_np[(h, 0)] = p.heads_np[(h, select_step)]
         p.dev[0] = p.dev[select_step]
     meta, od = mcs.select(*p.dev[0], w.group, keeps, p.proj(), scale=sc, return_dense=True, grouping=grouping,
-                          grid=w.grid if grouping == "morton" else None)
+                          grid=w.grid if grouping == "morton" else None, kv_block=kv_block, residual=residual)
     outs = {t: mcs.sparse_attn(*p.dev[t], meta, scale=sc) for t in steps}
     torch.cuda.synchronize()
-    exact, total = check_units(p, meta, od, outs, sc, heads, sample_groups(p.ng), label, grouping)
+    exact, total = check_units(p, meta, od, outs, sc, heads, sample_groups(p.ng), label, grouping, kv_block,
+                               residual)
     print(f"[full] {label}: kept-key sets equal to the oracle's: {exact}/{total}", flush=True)
 
 
@@ -59,6 +60,20 @@ def test_workload5_zcurve_groups_g128():
     _need_gpu()
     w = WORKLOADS[5].with_(group=128)
     run_workload(w, [9], [0, w.heads - 1], "workload 5 z-curve G=128", grouping="morton")
+
+
+def test_workload2_zcurve_64key_blocks():
+    """Block-granular selection (whole 64-key blocks) at the full workload-2 size."""
+    _need_gpu()
+    w = WORKLOADS[2]
+    run_workload(w, [1, 10], [0, w.heads - 1], "workload 2 z-curve 64-key blocks", grouping="morton", kv_block=64)
+
+
+def test_workload4_no_residual():
+    """Renormalised sparse output alone (no residual) at the full workload-4 size."""
+    _need_gpu()
+    w = WORKLOADS[4]
+    run_workload(w, [1, 15], [0, w.heads - 1], "workload 4 no residual", residual=False)
 
 
 def test_workload3_long_video_layer():

@@ -27,11 +27,12 @@ of every step's output against dense attention on that step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--sweep] [--ablation]
 
-Two converters turn rocprofv3 results into the summaries kept in profiles/
+Three converters turn rocprofv3 results into the summaries kept in profiles/
 (no GPU needed):
 
     python bench.py --trace-summary RESULTS.db OUT.md "TITLE" "COMMAND"
     python bench.py --traffic-summary FETCH.db WRITE.db OUT.json GROUPING
+    python bench.py --counter-summary OUT.md RESULTS.db [RESULTS.db ...]
 """
 
 from __future__ import annotations
@@ -396,7 +397,88 @@ def traffic_summary(fetch_db, write_db, out, grouping):
         json.dump(res, f, indent=1)
 
 
+# Counter passes of --counter-summary: each fits one rocprofv3 --pmc run
+# (at most 8 SQ, 4 TCP, 2 TA, 2 TD, 2 GRBM counters).
+COUNTER_PASSES = [
+    "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
+    "SQ_INSTS_VALU SQ_INSTS_MFMA TA_TA_BUSY_sum TA_ADDR_STALLED_BY_TC_CYCLES_sum TD_TD_BUSY_sum TD_TC_STALL_sum "
+    "GRBM_GUI_ACTIVE",
+    "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE TCP_PENDING_STALL_CYCLES_sum "
+    "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_TOTAL_CACHE_ACCESSES_sum GRBM_GUI_ACTIVE",
+    "TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
+]
+REUSE_KERNEL = "attn_bf16_kernel<128, 2, 2, 32>"
+
+
+def counter_summary(out, *dbs):
+    """Hardware counters of the workload-2 reuse launch (mean over its
+    dispatches) from rocprofv3 --pmc runs of the bench, with the ratios that
+    locate its bottleneck.  GRBM_GUI_ACTIVE is summed over the eight XCDs, so
+    the kernel's own clock is GUI / 8 / duration; per-CU and per-SIMD busy
+    fractions divide by GUI / 8 and by 256 CUs or 1024 SIMDs; the SQ wave
+    counters are in quad-cycles of one wave."""
+    import sqlite3
+    vals, durs = {}, []
+    for db in dbs:
+        cur = sqlite3.connect(db).cursor()
+        acc = {}
+        for name, value, start, end in cur.execute(
+                "select counter_name, value, start, end from counters_collection where kernel_name like ?",
+                (f"%{REUSE_KERNEL}%",)):
+            acc.setdefault(name, []).append(float(value))
+            if name == "GRBM_GUI_ACTIVE":
+                durs.append((end - start) * 1e-9)
+        for name, v in acc.items():
+            vals[name] = float(np.mean(v))
+    xcd_cycles = vals["GRBM_GUI_ACTIVE"] / 8
+    dur = float(np.median(durs))
+
+    def frac(name, units):
+        return vals[name] / units / xcd_cycles if name in vals else float("nan")
+
+    def wave(name):
+        return vals[name] / vals["SQ_WAVE_CYCLES"] if name in vals else float("nan")
+
+    derived = [
+        ("kernel clock (GHz): GUI / 8 / duration", xcd_cycles / dur / 1e9),
+        ("MFMA pipe busy, per SIMD", frac("SQ_VALU_MFMA_BUSY_CYCLES", 1024)),
+        ("TD busy (processing or waiting for data), per CU", frac("TD_TD_BUSY_sum", 256)),
+        ("TD stalled waiting for TC data, per CU", frac("TD_TC_STALL_sum", 256)),
+        ("TA busy, per CU", frac("TA_TA_BUSY_sum", 256)),
+        ("TA address path stalled by TC, per CU", frac("TA_ADDR_STALLED_BY_TC_CYCLES_sum", 256)),
+        ("TCP stalled on data pending from L2, per CU", frac("TCP_PENDING_STALL_CYCLES_sum", 256)),
+        ("mean TCP->L2 read latency (cycles)",
+         vals.get("TCP_TCC_READ_REQ_LATENCY_sum", float("nan")) / vals.get("TCP_TCC_READ_REQ_sum", float("nan"))),
+        ("L2 read requests per gathered 128-byte K/V line (1.0: no L1 reuse; Q, residual and index reads add the "
+         "rest)", vals.get("TCP_TCC_READ_REQ_sum", float("nan")) / (24 * 390 * 2496 * 2 * 256 / 128)),
+        ("L2 hit rate: TCC_HIT / (TCC_HIT + TCC_MISS)",
+         vals.get("TCC_HIT_sum", float("nan")) / (vals.get("TCC_HIT_sum", 0.0) + vals.get("TCC_MISS_sum", 0.0) or
+                                                   float("nan"))),
+        ("wave time waiting (waitcnt, barrier): SQ_WAIT_ANY / SQ_WAVE_CYCLES", wave("SQ_WAIT_ANY")),
+        ("wave time ready but not issued: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES", wave("SQ_WAIT_INST_ANY")),
+        ("wave time issuing: SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES", wave("SQ_ACTIVE_INST_ANY")),
+        ("LDS bank-conflict cycles / LDS active cycles",
+         vals.get("SQ_LDS_BANK_CONFLICT", float("nan")) / vals.get("SQ_LDS_IDX_ACTIVE", float("nan"))),
+    ]
+    cmd = ("rocprofv3 --pmc {c} -d gpurun_out/cnt_{i} -o cnt -- python3 bench.py --steps 1 --warmup 0 "
+           "--no-cpu-baseline")
+    lines = [f"# Counters of the workload-2 reuse launch (`{REUSE_KERNEL}`)", "",
+             f"Source hash of `attn_bf16.hip`: `{src_hash(ATTN_SRC)}`. Mean over the launch's dispatches in each pass; "
+             f"median dispatch time under counter collection {dur * 1e3:.3f} ms.", "", "Commands:", ""]
+    lines += [f"- `{cmd.format(c=c, i=i + 1)}`" for i, c in enumerate(COUNTER_PASSES)]
+    lines += [f"- `python3 bench.py --counter-summary {out} {' '.join(dbs)}`", "",
+              "| derived | value |", "|---|---|"]
+    lines += [f"| {k} | {v:.3f} |" for k, v in derived]
+    lines += ["", "| counter | mean per dispatch |", "|---|---|"]
+    lines += [f"| {k} | {vals[k]:.0f} |" for k in sorted(vals)]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--counter-summary":
+        counter_summary(*sys.argv[2:])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--trace-summary":
         trace_summary(*sys.argv[2:6])
         return

@@ -147,7 +147,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   // ---- tile loads -------------------------------------------------------
   // Load u of this wave covers tile rows ii*RPI .. +RPI-1 (ii = w + NW u); lane
   // `lane` fills stored chunk (lane % CPR) of row ii*RPI + lane / CPR.  Rows
-  // past the end of the key list load key 0 (their scores are masked).
+  // past the end of the key list load key 0 (their scores are masked): the
+  // whole index offset goes in the range-checked vector offset, so those
+  // index reads return 0.
   // The source row of each load is fetched one tile ahead and only turned into
   // a byte offset when the copy is issued, so that nothing waits on the fetch
   // (and, through the in-order memory counter, on the copy issued before it).
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       for (int u = 0; u < UPW; ++u) {
         const int t = (w + NW * u) * GE::RPI + lane / GE::CPR;
         if constexpr (SPARSE)
-          src_row[u] = __builtin_amdgcn_raw_buffer_load_b32(ridx, 4 * t, 4 * BK * j, 0);
+          src_row[u] = __builtin_amdgcn_raw_buffer_load_b32(ridx, 4 * (BK * j + t), 0, 0);
         else
           src_row[u] = j * BK + t;
       }

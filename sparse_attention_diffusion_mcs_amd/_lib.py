@@ -20,6 +20,7 @@ MCS_DTYPE_FP32 = 0
 MCS_DTYPE_BF16 = 1
 MCS_META_VERSION = 1
 MCS_HASH_BITS = 8
+MCS_MAX_SEQ_LEN = 1 << 22
 
 MCS_GROUPING_HASH = 0
 MCS_GROUPING_RASTER = 1

@@ -201,3 +201,17 @@ def test_meta_init_validation(lib):
     assert lib.mcs_meta_init(D, 64, kp, FAKE_MIS, mb, ctypes.byref(m), NULL) == L.MCS_ERROR_MISALIGNED
     assert lib.mcs_meta_init(D, 64, kp, FAKE, mb - 4, ctypes.byref(m), NULL) == L.MCS_ERROR_BUFFER_TOO_SMALL
     assert lib.mcs_meta_init(D, 64, kp, FAKE, mb, None, NULL) == L.MCS_ERROR_INVALID_VALUE
+
+
+def test_max_seq_len_boundary(lib):
+    """N = MCS_MAX_SEQ_LEN is accepted and N + 1 rejected (host-side layout
+    only); the binding's constant is the header's."""
+    import re
+    hdr = open(os.path.join(ROOT, "include", "mcs.h")).read()
+    assert re.search(r"#define MCS_MAX_SEQ_LEN \(1 << (\d+)\)", hdr).group(1) == "22"
+    assert L.MCS_MAX_SEQ_LEN == 1 << 22
+    keep, kp = _i32([64])
+    for d in (64, 128):
+        assert lib.mcs_meta_bytes(ctypes.byref(_desc(1, L.MCS_MAX_SEQ_LEN, d)), 64, kp) > 0
+        assert lib.mcs_meta_bytes(ctypes.byref(_desc(1, L.MCS_MAX_SEQ_LEN + 1, d)), 64, kp) == 0
+        assert lib.mcs_select_workspace_bytes(ctypes.byref(_desc(1, L.MCS_MAX_SEQ_LEN + 1, d)), 64, 1) == 0

@@ -241,6 +241,11 @@ mcs_status mcs_select_ex(const mcs_attn_desc* desc, const void* q, const void* k
  * for every sorted position p of group g, S_g = the group's cached keys.
  * q, k, v: [H][N][d] inputs of this step; meta: from mcs_select or
  * mcs_meta_init with the same H, N, d and dtype; o: [H][N][d] output.
+ * Errors: MCS_ERROR_META_MISMATCH when meta was built for another shape,
+ * dtype or layout version, or when its region offsets or size are not the
+ * ones this layout gives for its own total_idx; indices read from the
+ * regions are clamped to [0, N) on the device, so edited metadata cannot
+ * lead a kernel out of bounds.
  */
 mcs_status mcs_sparse_attn(const mcs_attn_desc* desc, const void* q, const void* k, const void* v,
                            const mcs_meta* meta, void* o, void* stream);

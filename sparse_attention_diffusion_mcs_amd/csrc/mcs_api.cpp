@@ -62,8 +62,27 @@ mcs_status check_group_keep(const mcs_attn_desc* d, int32_t G, const int32_t* ke
   return MCS_SUCCESS;
 }
 
-void make_layout(const mcs_attn_desc* d, int32_t G, const int32_t* keep, mcs_meta* m) {
+// Region offsets and size of a metadata buffer holding `total` kept indices.
+void place_regions(const mcs_attn_desc* d, int64_t total, mcs_meta* m) {
   const uint64_t H = (uint64_t)d->num_heads, N = (uint64_t)d->seq_len, D = (uint64_t)d->head_dim;
+  uint64_t off = 0;
+  m->off_perm = off;
+  off = align_up(off + H * N * 4, kAlign);
+  m->off_keep = off;
+  off = align_up(off + H * 4, kAlign);
+  m->off_idx_start = off;
+  off = align_up(off + H * 8, kAlign);
+  m->off_sched = off;
+  off = align_up(off + H * 4, kAlign);
+  m->off_idx = off;
+  off = align_up(off + (uint64_t)total * 4, kAlign);
+  m->off_residual = off;
+  off = align_up(off + H * N * D * 4, kAlign);
+  m->bytes = off;
+}
+
+void make_layout(const mcs_attn_desc* d, int32_t G, const int32_t* keep, mcs_meta* m) {
+  const uint64_t H = (uint64_t)d->num_heads, N = (uint64_t)d->seq_len;
   std::memset(m, 0, sizeof(*m));
   m->version = MCS_META_VERSION;
   m->num_heads = d->num_heads;
@@ -81,20 +100,7 @@ void make_layout(const mcs_attn_desc* d, int32_t G, const int32_t* keep, mcs_met
     }
   m->max_keep = mk;
   m->total_idx = total;
-  uint64_t off = 0;
-  m->off_perm = off;
-  off = align_up(off + H * N * 4, kAlign);
-  m->off_keep = off;
-  off = align_up(off + H * 4, kAlign);
-  m->off_idx_start = off;
-  off = align_up(off + H * 8, kAlign);
-  m->off_sched = off;
-  off = align_up(off + H * 4, kAlign);
-  m->off_idx = off;
-  off = align_up(off + (uint64_t)total * 4, kAlign);
-  m->off_residual = off;
-  off = align_up(off + H * N * D * 4, kAlign);
-  m->bytes = off;
+  place_regions(d, total, m);
 }
 
 uint64_t colsum_ld(int N) { return align_up((uint64_t)N, 64); }
@@ -368,6 +374,16 @@ mcs_status mcs_sparse_attn(const mcs_attn_desc* d, const void* q, const void* k,
   if (m->version != MCS_META_VERSION || m->num_heads != d->num_heads || m->seq_len != d->seq_len ||
       m->head_dim != d->head_dim || m->dtype != d->dtype || (m->group_size != 64 && m->group_size != 128) ||
       m->num_groups != (d->seq_len + m->group_size - 1) / m->group_size)
+    return MCS_ERROR_META_MISMATCH;
+  // the regions must sit where this layout version puts them for the
+  // struct's own index count (at most every head keeping every key)
+  if (m->total_idx < 0 || (double)m->total_idx > (double)m->num_groups * d->seq_len * d->num_heads)
+    return MCS_ERROR_META_MISMATCH;
+  mcs_meta ref;
+  place_regions(d, m->total_idx, &ref);
+  if (m->off_perm != ref.off_perm || m->off_keep != ref.off_keep || m->off_idx_start != ref.off_idx_start ||
+      m->off_sched != ref.off_sched || m->off_idx != ref.off_idx || m->off_residual != ref.off_residual ||
+      m->bytes != ref.bytes)
     return MCS_ERROR_META_MISMATCH;
   if (empty(d)) return MCS_SUCCESS;
   for (const void* p : {q, k, v, (const void*)o})

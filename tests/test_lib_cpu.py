@@ -215,3 +215,21 @@ def test_max_seq_len_boundary(lib):
         assert lib.mcs_meta_bytes(ctypes.byref(_desc(1, L.MCS_MAX_SEQ_LEN, d)), 64, kp) > 0
         assert lib.mcs_meta_bytes(ctypes.byref(_desc(1, L.MCS_MAX_SEQ_LEN + 1, d)), 64, kp) == 0
         assert lib.mcs_select_workspace_bytes(ctypes.byref(_desc(1, L.MCS_MAX_SEQ_LEN + 1, d)), 64, 1) == 0
+
+
+def test_sparse_attn_rejects_edited_layouts(lib):
+    """A metadata struct whose regions do not sit where the layout puts them
+    is refused before any launch (fake, aligned device pointers: nothing may
+    run)."""
+    H, N, d, G = 2, 1000, 128, 64
+    keep, kp = _i32([64, 100])
+    good = L.Meta()
+    assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), G, kp, ctypes.byref(good)) == L.MCS_SUCCESS
+    for field, delta in (("off_residual", 256), ("off_idx", -256), ("off_perm", 256), ("bytes", 256),
+                         ("total_idx", 64), ("total_idx", -good.total_idx - 1)):
+        m = L.Meta()
+        ctypes.pointer(m)[0] = good
+        m.base = FAKE
+        setattr(m, field, getattr(m, field) + delta)
+        st = lib.mcs_sparse_attn(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, ctypes.byref(m), FAKE, NULL)
+        assert st == L.MCS_ERROR_META_MISMATCH, (field, delta, st)

@@ -243,9 +243,10 @@ mcs_status mcs_select_ex(const mcs_attn_desc* desc, const void* q, const void* k
  * mcs_meta_init with the same H, N, d and dtype; o: [H][N][d] output.
  * Errors: MCS_ERROR_META_MISMATCH when meta was built for another shape,
  * dtype or layout version, or when its region offsets or size are not the
- * ones this layout gives for its own total_idx; indices read from the
- * regions are clamped to [0, N) on the device, so edited metadata cannot
- * lead a kernel out of bounds.
+ * ones this layout gives for its own total_idx.  Edited metadata cannot
+ * lead a kernel out of bounds: permutation entries are clamped to [0, N),
+ * and kept-key gathers go through bounds-checked buffer loads (an index
+ * outside [0, N) reads zeros).
  */
 mcs_status mcs_sparse_attn(const mcs_attn_desc* desc, const void* q, const void* k, const void* v,
                            const mcs_meta* meta, void* o, void* stream);

@@ -26,12 +26,14 @@
 // (8 rows x 2 chunks per half-wave).  All operand reads of a tile are issued
 // before its first MFMA so that their latency overlaps.
 //
-// Each wave computes S^T = K Q^T, so every lane holds scores of one query row;
-// the row max needs one in-lane pass and two row-swap permutes, and the
-// probabilities are already in the B-operand layout of O^T += V^T P^T.  The
-// running max is only moved (and O, l rescaled) when a row's tile max exceeds
-// it by more than 2^8; otherwise probabilities up to 2^8 are accumulated
-// against the stale max, which leaves O / l unchanged.
+// Each wave computes S^T = K Q^T, so every lane holds scores of one query row
+// (a quarter of the tile's tokens; the row's other tokens sit in three lanes
+// at distance 16) and the probabilities are already in the B-operand layout
+// of O^T += V^T P^T.  The running max is only moved (and O, l rescaled) when
+// a row's tile max exceeds it by more than 2^8; otherwise probabilities up to
+// 2^8 are accumulated against the stale max, which leaves O / l unchanged.
+// The check needs only each lane's own maximum; the row max (two row-swap
+// permutes) is formed on the rare rescale.
 #include "device.h"
 #include "launch.h"
 
@@ -176,8 +178,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
       const int ii = w + NW * u;
-      const int row = (int)min((unsigned)src_row[u], (unsigned)(N - 1));
-      const int off = (row * GE::ROWB) | chunk_off[u];
+      // Kept keys come from the metadata, whose indices are < N; an index
+      // outside [0, N) in edited metadata makes an offset past the head's
+      // buffer range, which the bounds check turns into zeros.  The dense
+      // modes clamp the rows of their ragged last tile to the last key.
+      const unsigned row = SPARSE ? (unsigned)src_row[u] : min((unsigned)src_row[u], (unsigned)(N - 1));
+      const int off = (int)((row * GE::ROWB) | (unsigned)chunk_off[u]);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + ii * 1024), 16, off, 0, 0, 0);
       if (with_v)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + GE::TILE + ii * 1024), 16, off, 0, 0, 0);
@@ -255,7 +261,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
           }
     }
 
-    float mx[2];
+    // This lane's maximum over its tokens of the tile (log2 units).  Whether
+    // some row of the wave needs a rescale, or carries large probabilities,
+    // is the same question asked of every lane, so the row maxima across the
+    // four lanes of a row are only formed when a rescale happens.
+    float lmx[2];
     bool need = false;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -264,13 +274,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, s[tb][rb][i]);
-      mx[rb] = quad_rows_max(m) * sl2;
-      need |= mx[rb] > m_run[rb] + kRescaleSlack;
+      lmx[rb] = m * sl2;
+      need |= lmx[rb] > m_run[rb] + kRescaleSlack;
     }
     if (__ballot(need) != 0ull) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const float mnew = __builtin_fmaxf(m_run[rb], mx[rb]);
+        const float mnew = __builtin_fmaxf(m_run[rb], quad_rows_max(lmx[rb]));
         const float alpha = fast_exp2(m_run[rb] - mnew);
         m_run[rb] = mnew;
         l_run[rb] *= alpha;
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i) {
           const float p = fast_exp2(fmaf(s[tb][rb][i], sl2, -m_run[rb]));
           s[tb][rb][i] = p;
-          ls += p;
+          ls = (tb == 0 && i == 0) ? p : ls + p;  // starts at the first term, not 0 + it
         }
       l_run[rb] += ls;
 #pragma unroll
@@ -331,11 +341,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       // error of the output is dominated by its largest terms.  A tile whose
       // probabilities all stay below 2^-kLoSkip of the running max skips its
       // low-part products; their rounding errors are at most 2^-(9 + kLoSkip)
-      // of the largest term.  The decision is taken per wave from the tile's
-      // row maxima.
+      // of the largest term.  The decision is taken per wave from the lanes'
+      // maxima.
       bool big = false;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) big |= mx[rb] > m_run[rb] - kLoSkip;
+      for (int rb = 0; rb < 2; ++rb) big |= lmx[rb] > m_run[rb] - kLoSkip;
       if (__ballot(big) != 0ull) {
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
@@ -481,7 +491,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) cs += fast_exp2(fmaf(s[rb][tb][i], sl2, nlse[rb][i]));
+          for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(fmaf(s[rb][tb][i], sl2, nlse[rb][i]));
+            cs = (rb == 0 && i == 0) ? p : cs + p;
+          }
         cs = quad_rows_sum(cs);
         if (lq == 0) red[jj & 1][w][half * BK + 16 * tb + lr] = cs;
       }

@@ -233,3 +233,29 @@ def test_sparse_attn_rejects_edited_layouts(lib):
         setattr(m, field, getattr(m, field) + delta)
         st = lib.mcs_sparse_attn(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, ctypes.byref(m), FAKE, NULL)
         assert st == L.MCS_ERROR_META_MISMATCH, (field, delta, st)
+
+
+def test_valid_call_without_a_device_reports_the_hip_error():
+    """On a host with no GPU a valid call passes validation, its launch fails
+    and the call returns MCS_ERROR_HIP with the HIP code kept for
+    mcs_last_hip_error (hipErrorNoDevice).  Run in a child process; skipped
+    where a device exists, since the pointers are fake."""
+    import subprocess
+    import sys
+
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: the fake pointers must not reach a kernel")
+    code = (
+        "import ctypes, sys\n"
+        f"sys.path.insert(0, {ROOT!r})\n"
+        "from sparse_attention_diffusion_mcs_amd import _lib as L\n"
+        "lib = L.lib()\n"
+        "d = L.AttnDesc(1, 64, 64, 1, 0.0)\n"
+        "f = ctypes.c_void_p(0x7f0000000000)\n"
+        "st = lib.mcs_dense_attn(ctypes.byref(d), f, f, f, f, None)\n"
+        "print(st, lib.mcs_last_hip_error())\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    st, err = (int(x) for x in r.stdout.split()[-2:])
+    assert st == L.MCS_ERROR_HIP and err == 100

@@ -70,3 +70,32 @@ def test_reuse_step_replays_from_a_graph():
         assert torch.equal(replayed, eager), f"replay on the step-{t} inputs"
     # the replays read the buffers captured, not copies of them
     assert not torch.equal(mcs.sparse_attn(*p.dev[1], meta, scale=sc), mcs.sparse_attn(*p.dev[2], meta, scale=sc))
+
+
+def test_selection_replays_from_a_graph():
+    """The selection step (grouping, dense pass with key scores, top-k,
+    residual: kernel launches only) captured into a graph with caller-owned
+    metadata and workspace buffers; replays on new inputs equal eager
+    selections on those inputs."""
+    _need_gpu()
+    p = _problem()
+    sc = scale_for(p.d)
+    proj = p.proj()
+    q, k, v = (x.clone() for x in p.dev[0])
+    ref_meta, _ = mcs.select(q, k, v, p.G, p.keeps, proj, scale=sc)
+    meta_buf = torch.empty_like(ref_meta.buffer)
+    ws = torch.empty(mcs.workspace_bytes(q, p.G), dtype=torch.uint8, device="cuda")
+    mcs.select(q, k, v, p.G, p.keeps, proj, scale=sc, meta_buf=meta_buf, workspace=ws)  # warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        meta, _ = mcs.select(q, k, v, p.G, p.keeps, proj, scale=sc, meta_buf=meta_buf, workspace=ws)
+    for t in (1, 2, 0):
+        for dst, src in zip((q, k, v), p.dev[t]):
+            dst.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        eager, _ = mcs.select(*p.dev[t], p.G, p.keeps, proj, scale=sc)
+        torch.cuda.synchronize()
+        for region in ("perm", "keep", "idx_start", "sched", "idx", "residual"):
+            assert torch.equal(getattr(meta, region), getattr(eager, region)), f"step {t} {region}"

@@ -32,7 +32,10 @@
  *    into H.
  *  - All calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Results are valid once the stream reaches the call.  No call
- *    synchronises the device.
+ *    synchronises the device.  The device work of every call is kernel
+ *    launches only (no allocation, memset or copy; host tables travel as
+ *    kernel arguments), so a call can be captured in a HIP graph and
+ *    replayed; a replay reads the buffers and host values of the capture.
  *  - The caller owns every device buffer.  The library allocates no device
  *    memory and keeps no global state apart from a per-thread last HIP error.
  *  - Every argument is validated before anything is launched; a call that

@@ -1,7 +1,8 @@
 """GPU parity on seeded random problem shapes: head count, head dim, dtype,
 group size, grid (down to a single token), keep budgets (1 .. N), grouping,
-KV granularity and the residual option are drawn per case, and every group
-of every head is compared with the CPU oracle."""
+KV granularity, the residual option and the softmax scale (the default
+1/sqrt(d) or a caller value) are drawn per case, and every group of every
+head is compared with the CPU oracle."""
 
 import numpy as np
 import pytest
@@ -40,18 +41,19 @@ def draw(seed):
         keeps = [int(r.integers(1, n + 1)) for _ in range(H)]
         keeps[-1] = n if seed % 2 else keeps[-1]
     residual = bool(seed % 5 != 4)
-    return grid, H, d, dtype, G, keeps, grouping, 64 if blocks else 1, residual
+    scale_mult = (1.0, 0.5, 1.5)[seed % 3]
+    return grid, H, d, dtype, G, keeps, grouping, 64 if blocks else 1, residual, scale_mult
 
 
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_shape_parity(seed):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    grid, H, d, dtype, G, keeps, grouping, kvb, resid = draw(seed)
+    grid, H, d, dtype, G, keeps, grouping, kvb, resid, mult = draw(seed)
     print(f"[case] seed={seed} grid={grid} H={H} d={d} {dtype} G={G} keeps={keeps} {grouping} block={kvb} "
-          f"residual={resid}", flush=True)
+          f"residual={resid} scale x{mult}", flush=True)
     p = build_problem(grid, H, d, dtype, G, keeps, 0.02, [1], wid=200 + seed)
-    sc = scale_for(d)
+    sc = scale_for(d) if mult == 1.0 else float(np.float32(mult / np.sqrt(d)))
     meta, od = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc, return_dense=True, grouping=grouping,
                           kv_block=kvb, residual=resid, grid=grid if grouping == "morton" else None)
     out = mcs.sparse_attn(*p.dev[1], meta, scale=sc)

@@ -172,3 +172,24 @@ def test_empty_problems():
         meta, _ = mcs.select(q, q, q, 64, [1] * shape[0], np.zeros((8, 64), np.float32))
         out = mcs.sparse_attn(q, q, q, meta)
         assert out.shape == shape
+
+
+@pytest.mark.parametrize("hc", [1, 2])
+def test_selection_in_head_chunks_matches_one_pass(hc):
+    """A workspace that holds the key scores of only `hc` heads makes the
+    selection run head chunk by head chunk; metadata and dense output are
+    byte-identical to the one-pass run (which the other tests compare with
+    the oracle)."""
+    _need_gpu()
+    grid, H, d, G, keeps = (3, 8, 21), 3, 128, 64, [64, 300, 503]
+    print(f"[case] head chunks of {hc}: grid={grid} H={H} d={d} G={G} keeps={keeps}", flush=True)
+    p = build_problem(grid, H, d, "bf16", G, keeps, 0.02, [1], wid=108)
+    sc = scale_for(d)
+    ref, od_ref = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc, return_dense=True)
+    ws = torch.empty(mcs.workspace_bytes(p.dev[0][0], G, heads_per_chunk=hc), dtype=torch.uint8, device="cuda")
+    assert ws.numel() < mcs.workspace_bytes(p.dev[0][0], G)
+    meta, od = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc, return_dense=True, workspace=ws)
+    torch.cuda.synchronize()
+    for region in ("perm", "keep", "idx_start", "sched", "idx", "residual"):
+        assert torch.equal(getattr(meta, region), getattr(ref, region)), region
+    assert torch.equal(od, od_ref)

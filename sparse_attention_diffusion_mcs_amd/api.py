@@ -32,6 +32,22 @@ def _check_qkv(q, k, v):
         raise ValueError("q, k, v must share shape and dtype")
 
 
+def _check_out(out, q):
+    """A caller-supplied output must be a contiguous device tensor of q's
+    shape and dtype: the kernels write all of [H, N, d] from its pointer."""
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous device tensor")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError(f"out must be {tuple(q.shape)} {q.dtype}, got {tuple(out.shape)} {out.dtype}")
+
+
+def _check_bytes(buf, name):
+    """Metadata and workspace buffers are contiguous uint8 device tensors:
+    their element count is the byte size handed to the library."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous() or buf.dtype != torch.uint8:
+        raise ValueError(f"{name} must be a contiguous uint8 device tensor")
+
+
 def desc_for(q: torch.Tensor, scale: float | None = None) -> L.AttnDesc:
     H, N, d = q.shape
     return L.AttnDesc(H, N, d, _dtype_code(q), float(scale) if scale else 0.0)
@@ -132,6 +148,7 @@ def dense_attn(q, k, v, out=None, scale=None, stream=None):
     _check_qkv(q, k, v)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q)
     desc = desc_for(q, scale)
     L.check(L.lib().mcs_dense_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream(stream)),
             "mcs_dense_attn")
@@ -163,6 +180,7 @@ def meta_init(q, group_size, keep, meta_buf=None, stream=None) -> MetaCache:
         raise L.McsError(L.MCS_ERROR_INVALID_VALUE, "mcs_meta_bytes")
     if meta_buf is None:
         meta_buf = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check_bytes(meta_buf, "meta_buf")
     m = L.Meta()
     L.check(L.lib().mcs_meta_init(ctypes.byref(desc), group_size, _i32p(ka), _ptr(meta_buf), meta_buf.numel(),
                                   ctypes.byref(m), _stream(stream)), "mcs_meta_init")
@@ -187,9 +205,11 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
         raise L.McsError(L.MCS_ERROR_INVALID_VALUE, "mcs_meta_bytes")
     if meta_buf is None:
         meta_buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    _check_bytes(meta_buf, "meta_buf")
     if workspace is None:
         workspace = torch.empty(max(workspace_bytes(q, group_size, heads_per_chunk), 256), dtype=torch.uint8,
                                 device=q.device)
+    _check_bytes(workspace, "workspace")
     o_dense = torch.empty_like(q) if return_dense else None
     m = L.Meta()
     pjp = pj.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
@@ -217,6 +237,7 @@ def sparse_attn(q, k, v, meta: MetaCache, out=None, scale=None, stream=None):
     _check_qkv(q, k, v)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q)
     desc = desc_for(q, scale)
     L.check(L.lib().mcs_sparse_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(meta.meta),
                                     _ptr(out), _stream(stream)), "mcs_sparse_attn")

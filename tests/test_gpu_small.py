@@ -193,3 +193,32 @@ def test_selection_in_head_chunks_matches_one_pass(hc):
     for region in ("perm", "keep", "idx_start", "sched", "idx", "residual"):
         assert torch.equal(getattr(meta, region), getattr(ref, region)), region
     assert torch.equal(od, od_ref)
+
+
+def test_binding_rejects_bad_buffers():
+    """The binding refuses caller buffers the kernels would write past or
+    misread, before calling the library: outputs of another shape or dtype,
+    non-contiguous outputs, and metadata or workspace buffers that are not
+    contiguous uint8."""
+    _need_gpu()
+    p = build_problem((2, 4, 9), 1, 64, "bf16", 64, [16], 0.02, [1], wid=109)
+    q, k, v = p.dev[0]
+    sc = scale_for(64)
+    meta, _ = mcs.select(q, k, v, 64, p.keeps, p.proj(), scale=sc)
+    bad_outs = [torch.empty(q.shape[0], q.shape[1] - 1, q.shape[2], dtype=q.dtype, device="cuda"),
+                torch.empty_like(q, dtype=torch.float32),
+                torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=q.dtype, device="cuda").transpose(1, 2),
+                torch.empty_like(q, device="cpu")]
+    for out in bad_outs:
+        with pytest.raises(ValueError):
+            mcs.sparse_attn(q, k, v, meta, out=out, scale=sc)
+        with pytest.raises(ValueError):
+            mcs.dense_attn(q, k, v, out=out, scale=sc)
+    nbytes = meta.buffer.numel()
+    for buf in (torch.empty(2 * nbytes, dtype=torch.uint8, device="cuda")[::2],
+                torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")):
+        with pytest.raises(ValueError):
+            mcs.select(q, k, v, 64, p.keeps, p.proj(), scale=sc, meta_buf=buf)
+        with pytest.raises(ValueError):
+            mcs.select(q, k, v, 64, p.keeps, p.proj(), scale=sc, workspace=buf)
+    torch.cuda.synchronize()

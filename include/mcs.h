@@ -12,7 +12,7 @@
  *              similar queries that fill whole GPU tiles; each group keeps the
  *              individual KV tokens that carry the most exact attention
  *              probability; the query groups, the kept KV indices and the
- *              residual between dense and sparse outputs are cached;
+ *              difference O_dense - O_sparse of the step's outputs are cached;
  *   reuse      on later denoising steps, attention of each group over only its
  *              cached KV tokens, plus the cached residual.
  *
@@ -155,7 +155,9 @@ size_t mcs_meta_bytes(const mcs_attn_desc* desc, int32_t group_size, const int32
  * Bytes of workspace mcs_select needs to process `heads_per_chunk` heads at a
  * time (clamped to [1, H]; 0 if the arguments are invalid).  The bulk is the
  * per-group key scores, float32 [heads_per_chunk][ceil(N/G)][N rounded up to 64],
- * plus 64-key block scores (1/64 of that) for block-granular selection.
+ * plus 64-key block scores (1/64 of that) for block-granular selection and
+ * the rows' log-sum-exp (float32 [heads_per_chunk][N]) that the dense pass
+ * hands to the key-score pass.
  */
 size_t mcs_select_workspace_bytes(const mcs_attn_desc* desc, int32_t group_size, int32_t heads_per_chunk);
 
@@ -169,12 +171,11 @@ mcs_status mcs_meta_init(const mcs_attn_desc* desc, int32_t group_size, const in
                          void* meta_buf, size_t meta_bytes, mcs_meta* meta_out, void* stream);
 
 /*
- * Selection step ("selects individual key-value (KV) tokens while organizing
- * similar queries into tile-aligned groups ... caches metadata comprising query
- * groups, KV indices selected using exact attention probabilities, and
- * residuals between dense and sparse attention outputs", abstract of
- * "MC-Sparse: Deconstructing and Closing the Dense-Sparse Attention Gap in
- * Diffusion Transformers").
+ * Selection step (abstract of "MC-Sparse: Deconstructing and Closing the
+ * Dense-Sparse Attention Gap in Diffusion Transformers"): groups similar
+ * queries into tile-aligned groups, keeps for each group the individual KV
+ * tokens that the exact attention probabilities rank highest, and caches the
+ * groups, the kept indices and the dense-minus-sparse output difference.
  *   q, k, v        [H][N][d] step inputs (device)
  *   group_size     G, 64 or 128 (query rows per group = one GPU tile)
  *   keep_host      int32 [H] host array, k_h in [1, N], read during the call
@@ -196,10 +197,11 @@ mcs_status mcs_select(const mcs_attn_desc* desc, const void* q, const void* k, c
 /*
  * Ablations of the three failure modes the pages trace the dense-sparse gap
  * to (abstract of "MC-Sparse: Deconstructing and Closing the Dense-Sparse
- * Attention Gap in Diffusion Transformers": constraints of token grouping,
- * inaccurate interaction selection, contributions lost with the discarded
- * tokens; the list in section "MC-Sparse: three failure modes, one fix" of
- * "The quality cliff nobody admits to").  Each field swaps one of MC-Sparse's
+ * Attention Gap in Diffusion Transformers", and the list in section
+ * "MC-Sparse: three failure modes, one fix" of "The quality cliff nobody
+ * admits to"): groups that force one pattern on unlike queries, a selection
+ * that misjudges which interactions matter, and the attention mass of the
+ * dropped tokens.  Each field swaps one of MC-Sparse's
  * choices for the coarser one; all zero-initialised fields but kv_block and
  * residual select MC-Sparse itself.  Two further groupings order the queries
  * differently: the centred hash, and the Z-curve over the latent grid.
@@ -236,8 +238,8 @@ mcs_status mcs_select_ex(const mcs_attn_desc* desc, const void* q, const void* k
                          size_t ws_bytes, void* o_dense_out, mcs_meta* meta_out, void* stream);
 
 /*
- * Reuse step ("reuses them across subsequent denoising steps", same abstract;
- * the residual restores the attention contribution that renormalising over
+ * Reuse step (same abstract: the cached groups, indices and residual serve
+ * the later denoising steps; the residual restores the attention contribution that renormalising over
  * the kept tokens loses, section "What Trips People Up" of "The quality cliff
  * nobody admits to"):
  *   o[h][perm[p]] = sum_{j in S_g} softmax_{j in S_g}(scale q.k_j) v_j + residual[h][p]

@@ -11,9 +11,9 @@ titles as given by the pages):
 * [ABS]  "MC-Sparse: Deconstructing and Closing the Dense-Sparse Attention Gap
   in Diffusion Transformers", arXiv abstract: individual KV tokens are chosen
   with exact attention probabilities; similar queries are organised into
-  tile-aligned groups; the cached metadata is the query groups, the KV
-  indices and the residual between dense and sparse outputs, reused on later
-  denoising steps.
+  tile-aligned groups; the cache holds the query groups, the kept KV indices
+  and the difference of the dense and sparse outputs, and later denoising
+  steps reuse it.
 * [BLOG] "The quality cliff nobody admits to", section "MC-Sparse: three
   failure modes, one fix" (same three cached items, computed once and reused)
   and section "What Trips People Up" (renormalising over the kept tokens moves
@@ -36,9 +36,10 @@ The pages give no formula, so the readings taken where they are silent are:
   (renormalised over them); the residual O_dense - O_sparse is kept per query
   (in sorted order) and added back unchanged on every reuse step.
 
-The ablations of the three failure modes the pages name ([ABS]: constraints
-of token grouping, inaccurate interaction selection, contributions lost with
-the discarded tokens; [BLOG] "MC-Sparse: three failure modes, one fix") swap
+The ablations of the three failure modes the pages name ([ABS] and [BLOG]
+"MC-Sparse: three failure modes, one fix": groups that force one pattern on
+unlike queries, a selection that misjudges which interactions matter, and the
+attention mass of the dropped tokens) swap
 one choice each: raster-order query groups instead of hash groups, whole
 64-token KV blocks ranked by their summed score instead of individual tokens,
 and no residual (the renormalised sparse output alone).  A fourth variant
@@ -63,8 +64,8 @@ HASH_BITS = 8
 
 
 # ---------------------------------------------------------------------------
-# Query grouping ([ABS]: "organizing similar queries into tile-aligned groups";
-# [NARROW]: "Hardware-aware query organization").
+# Query grouping ([ABS]: similar queries share a tile-aligned group;
+# [NARROW]: the hardware-aware query organisation among its design choices).
 # ---------------------------------------------------------------------------
 
 def hash_keys(q: np.ndarray, proj: np.ndarray) -> np.ndarray:
@@ -179,9 +180,8 @@ def dense_attention(q, k, v, scale):
 
 
 # ---------------------------------------------------------------------------
-# Selection ([ABS] / [NARROW]: "individual KV selection" from exact
-# probabilities; [BLOG]: "selects individual KV tokens using exact attention
-# probabilities").
+# Selection ([ABS], [NARROW] and [BLOG]: each group keeps individual KV
+# tokens, ranked by exact attention probabilities).
 # ---------------------------------------------------------------------------
 
 def group_scores(p_rows: np.ndarray) -> np.ndarray:

@@ -20,11 +20,12 @@
 // stages are distinct LDS objects and the tile loop is unrolled by two, so the
 // compiler can see that a tile's reads never alias the copy into the other
 // stage and does not wait for that copy before reading.  Rows are stored with
-// an XOR swizzle of their 16-byte chunks chosen so that both LDS read patterns
-// are free of bank conflicts: the K operand (16-byte reads, 16 rows per
-// quarter-wave) and the V operand, read transposed with ds_read_b64_tr_b16
-// (8 rows x 2 chunks per half-wave).  All operand reads of a tile are issued
-// before its first MFMA so that their latency overlaps.
+// an XOR swizzle of their 16-byte chunks.  The V operand, read transposed
+// with ds_read_b64_tr_b16 (8 rows x 2 chunks per half-wave), is free of bank
+// conflicts; the K operand's 16-byte reads, which the LDS serves 32 lanes at
+// a time, meet a 2-way conflict (a swizzle free of both costs more address
+// registers than the conflict costs time).  All operand reads of a tile are
+// issued before its first MFMA so that their latency overlaps.
 //
 // Each wave computes S^T = K Q^T, so every lane holds scores of one query row
 // (a quarter of the tile's tokens; the row's other tokens sit in three lanes
@@ -34,6 +35,11 @@
 // 2^8 are accumulated against the stale max, which leaves O / l unchanged.
 // The check needs only each lane's own maximum; the row max (two row-swap
 // permutes) is formed on the rare rescale.
+//
+// The selection runs two launches over the same query tiles: the dense pass
+// (MODE_SELECT: dense output and each row's log-sum-exp) and the key-score
+// pass (MODE_SCORE), which recomputes QK^T and sums each group's exact
+// probabilities per key.
 #include "device.h"
 #include "launch.h"
 
@@ -96,8 +102,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
-  __shared__ float red[MODE == MODE_SELECT ? 2 : 1][NW][MODE == MODE_SELECT ? 2 * BK : 1];
-  __shared__ float lse_s[MODE == MODE_SELECT ? BM : 1];
+  __shared__ float red[MODE == MODE_SCORE ? 2 : 1][NW][MODE == MODE_SCORE ? 2 * BK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -206,229 +211,237 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p));
   };
 
-  // ---- pass 1: online-softmax attention over the KV tiles ---------------
-  float m_run[2] = {-1e30f, -1e30f};
-  float l_run[2] = {0.f, 0.f};
-  f32x4 oacc[DB][2];
+  if constexpr (MODE != MODE_SCORE) {  // every mode but the key-score pass
+    // ---- pass 1: online-softmax attention over the KV tiles ---------------
+    float m_run[2] = {-1e30f, -1e30f};
+    float l_run[2] = {0.f, 0.f};
+    f32x4 oacc[DB][2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto attend_tile = [&](int j, const char* cur, char* nxt, auto masked) {
-    wait_vm<0>();
-    __syncthreads();
-    if (j + 1 < nt) {
-      issue(nxt, true);
-      fetch_rows(j + 2);
-    }
-    const char* vt = cur + GE::TILE;
-    bf16x8 kf[KK][TB];
+    auto attend_tile = [&](int j, const char* cur, char* nxt, auto masked) {
+      wait_vm<0>();
+      __syncthreads();
+      if (j + 1 < nt) {
+        issue(nxt, true);
+        fetch_rows(j + 2);
+      }
+      const char* vt = cur + GE::TILE;
+      bf16x8 kf[KK][TB];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) kf[kk][tb] = kfrag(cur, tb, kk);
-    uint2 vr[KC][DB][2];
+        for (int tb = 0; tb < TB; ++tb) kf[kk][tb] = kfrag(cur, tb, kk);
+      uint2 vr[KC][DB][2];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
+      for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) vr[kc][db][hh] = vhalf(vt, kc, db, hh);
+          for (int hh = 0; hh < 2; ++hh) vr[kc][db][hh] = vhalf(vt, kc, db, hh);
 
-    // S^T[token][row]: lane holds tokens 16 tb + 4 lq + i of row 16 rb + lr
-    f32x4 s[TB][2];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) s[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+      // S^T[token][row]: lane holds tokens 16 tb + 4 lq + i of row 16 rb + lr
+      f32x4 s[TB][2];
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          s[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk][tb], qf[rb][kk], s[tb][rb], 0, 0, 0);
-    if constexpr (decltype(masked)::value) {  // the ragged last tile only
-      const int vcols = nkv - j * BK;
+        for (int rb = 0; rb < 2; ++rb) s[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * tb + 4 * lq + i >= vcols) {
-            s[tb][0][i] = -INFINITY;
-            s[tb][1][i] = -INFINITY;
-          }
-    }
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            s[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk][tb], qf[rb][kk], s[tb][rb], 0, 0, 0);
+      if constexpr (decltype(masked)::value) {  // the ragged last tile only
+        const int vcols = nkv - j * BK;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * tb + 4 * lq + i >= vcols) {
+              s[tb][0][i] = -INFINITY;
+              s[tb][1][i] = -INFINITY;
+            }
+      }
 
-    // This lane's maximum over its tokens of the tile (log2 units).  Whether
-    // some row of the wave needs a rescale, or carries large probabilities,
-    // is the same question asked of every lane, so the row maxima across the
-    // four lanes of a row are only formed when a rescale happens.
-    float lmx[2];
-    bool need = false;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float m = s[0][rb][0];
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, s[tb][rb][i]);
-      lmx[rb] = m * sl2;
-      need |= lmx[rb] > m_run[rb] + kRescaleSlack;
-    }
-    if (__ballot(need) != 0ull) {
+      // This lane's maximum over its tokens of the tile (log2 units).  Whether
+      // some row of the wave needs a rescale, or carries large probabilities,
+      // is the same question asked of every lane, so the row maxima across the
+      // four lanes of a row are only formed when a rescale happens.
+      float lmx[2];
+      bool need = false;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const float mnew = __builtin_fmaxf(m_run[rb], quad_rows_max(lmx[rb]));
-        const float alpha = fast_exp2(m_run[rb] - mnew);
-        m_run[rb] = mnew;
-        l_run[rb] *= alpha;
+        float m = s[0][rb][0];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db][rb] *= alpha;
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, s[tb][rb][i]);
+        lmx[rb] = m * sl2;
+        need |= lmx[rb] > m_run[rb] + kRescaleSlack;
+      }
+      if (__ballot(need) != 0ull) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const float mnew = __builtin_fmaxf(m_run[rb], quad_rows_max(lmx[rb]));
+          const float alpha = fast_exp2(m_run[rb] - mnew);
+          m_run[rb] = mnew;
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db][rb] *= alpha;
+        }
+      }
+      bf16x8 pf[KC][2];
+      bf16x8 pl[PRECISE_PV ? KC : 1][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float ls = 0.f;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(fmaf(s[tb][rb][i], sl2, -m_run[rb]));
+            s[tb][rb][i] = p;
+            ls = (tb == 0 && i == 0) ? p : ls + p;  // starts at the first term, not 0 + it
+          }
+        l_run[rb] += ls;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const uint4 hi = make_uint4(pack_bf16x2(s[2 * kc][rb][0], s[2 * kc][rb][1]),
+                                      pack_bf16x2(s[2 * kc][rb][2], s[2 * kc][rb][3]),
+                                      pack_bf16x2(s[2 * kc + 1][rb][0], s[2 * kc + 1][rb][1]),
+                                      pack_bf16x2(s[2 * kc + 1][rb][2], s[2 * kc + 1][rb][3]));
+          pf[kc][rb] = as_bf16x8(hi);
+          if constexpr (PRECISE_PV) {
+            // low part p - bf16(p), so that P = hi + lo to ~16 significant bits
+            const uint32_t h4[4] = {hi.x, hi.y, hi.z, hi.w};
+            uint32_t lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const f32x4 src = s[2 * kc + (e >> 1)][rb];
+              const float r0 = src[2 * (e & 1)] - __uint_as_float(h4[e] << 16);
+              const float r1 = src[2 * (e & 1) + 1] - __uint_as_float(h4[e] & 0xffff0000u);
+              lo[e] = pack_bf16x2(r0, r1);
+            }
+            pl[kc][rb] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+          }
+        }
+      }
+
+      // O^T[dim][row] += V^T P^T
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 vf = as_bf16x8(
+              make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y));
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kc][rb], oacc[db][rb], 0, 0, 0);
+        }
+      if constexpr (PRECISE_PV) {
+        // The low part only matters where probabilities are large: the rounding
+        // error of the output is dominated by its largest terms.  A tile whose
+        // probabilities all stay below 2^-kLoSkip of the running max skips its
+        // low-part products; their rounding errors are at most 2^-(9 + kLoSkip)
+        // of the largest term.  The decision is taken per wave from the lanes'
+        // maxima.
+        bool big = false;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) big |= lmx[rb] > m_run[rb] - kLoSkip;
+        if (__ballot(big) != 0ull) {
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const bf16x8 vf = as_bf16x8(
+                  make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y));
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb)
+                oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[kc][rb], oacc[db][rb], 0, 0, 0);
+            }
+        }
+      }
+    };
+
+    fetch_rows(0);
+    if (nt > 0) issue(st0, true);
+    fetch_rows(1);
+    {
+      const Flag<false> full;
+      const Flag<true> ragged;
+      const int nfull = (nkv % BK) ? nt - 1 : nt;   // tiles that need no masking
+      int j = 0;
+      for (; j + 1 < nfull; j += 2) {
+        attend_tile(j, st0, st1, full);
+        attend_tile(j + 1, st1, st0, full);
+      }
+      if (j < nfull) attend_tile(j++, st0, st1, full);
+      if (j < nt) {
+        if (j & 1)
+          attend_tile(j, st1, st0, ragged);
+        else
+          attend_tile(j, st0, st1, ragged);
       }
     }
-    bf16x8 pf[KC][2];
-    bf16x8 pl[PRECISE_PV ? KC : 1][2];
+
+    // ---- epilogue ---------------------------------------------------------
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float ls = 0.f;
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(fmaf(s[tb][rb][i], sl2, -m_run[rb]));
-          s[tb][rb][i] = p;
-          ls = (tb == 0 && i == 0) ? p : ls + p;  // starts at the first term, not 0 + it
-        }
-      l_run[rb] += ls;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const uint4 hi = make_uint4(pack_bf16x2(s[2 * kc][rb][0], s[2 * kc][rb][1]),
-                                    pack_bf16x2(s[2 * kc][rb][2], s[2 * kc][rb][3]),
-                                    pack_bf16x2(s[2 * kc + 1][rb][0], s[2 * kc + 1][rb][1]),
-                                    pack_bf16x2(s[2 * kc + 1][rb][2], s[2 * kc + 1][rb][3]));
-        pf[kc][rb] = as_bf16x8(hi);
-        if constexpr (PRECISE_PV) {
-          // low part p - bf16(p), so that P = hi + lo to ~16 significant bits
-          const uint32_t h4[4] = {hi.x, hi.y, hi.z, hi.w};
-          uint32_t lo[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const f32x4 src = s[2 * kc + (e >> 1)][rb];
-            const float r0 = src[2 * (e & 1)] - __uint_as_float(h4[e] << 16);
-            const float r1 = src[2 * (e & 1) + 1] - __uint_as_float(h4[e] & 0xffff0000u);
-            lo[e] = pack_bf16x2(r0, r1);
-          }
-          pl[kc][rb] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-        }
+      const float l = quad_rows_sum(l_run[rb]);
+      const float inv = 1.0f / l;
+      const int r = 32 * w + 16 * rb + lr;
+      const int p = row0 + r;
+      if constexpr (MODE == MODE_SELECT) {
+        if (lq == 0 && rvalid[rb]) a.lse[(size_t)hs * N + p] = m_run[rb] + __log2f(l);
       }
-    }
-
-    // O^T[dim][row] += V^T P^T
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
+      if (!rvalid[rb]) continue;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = as_bf16x8(
-            make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y));
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kc][rb], oacc[db][rb], 0, 0, 0);
-      }
-    if constexpr (PRECISE_PV) {
-      // The low part only matters where probabilities are large: the rounding
-      // error of the output is dominated by its largest terms.  A tile whose
-      // probabilities all stay below 2^-kLoSkip of the running max skips its
-      // low-part products; their rounding errors are at most 2^-(9 + kLoSkip)
-      // of the largest term.  The decision is taken per wave from the lanes'
-      // maxima.
-      bool big = false;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) big |= lmx[rb] > m_run[rb] - kLoSkip;
-      if (__ballot(big) != 0ull) {
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 vf = as_bf16x8(
-                make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y));
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-              oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[kc][rb], oacc[db][rb], 0, 0, 0);
-          }
-      }
-    }
-  };
-
-  fetch_rows(0);
-  if (nt > 0) issue(st0, true);
-  fetch_rows(1);
-  {
-    const Flag<false> full;
-    const Flag<true> ragged;
-    const int nfull = (nkv % BK) ? nt - 1 : nt;   // tiles that need no masking
-    int j = 0;
-    for (; j + 1 < nfull; j += 2) {
-      attend_tile(j, st0, st1, full);
-      attend_tile(j + 1, st1, st0, full);
-    }
-    if (j < nfull) attend_tile(j++, st0, st1, full);
-    if (j < nt) {
-      if (j & 1)
-        attend_tile(j, st1, st0, ragged);
-      else
-        attend_tile(j, st0, st1, ragged);
-    }
-  }
-
-  // ---- epilogue ---------------------------------------------------------
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float l = quad_rows_sum(l_run[rb]);
-    const float inv = 1.0f / l;
-    const int r = 32 * w + 16 * rb + lr;
-    const int p = row0 + r;
-    if constexpr (MODE == MODE_SELECT) {
-      if (lq == 0) lse_s[r] = rvalid[rb] ? m_run[rb] + __log2f(l) : INFINITY;
-    }
-    if (!rvalid[rb]) continue;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int col = 16 * db + 4 * lq;
-      const f32x4 o = oacc[db][rb] * inv;
-      if constexpr (MODE == MODE_PLAIN) {
-        uint16_t* out = static_cast<uint16_t*>(a.o) + hoff + (size_t)p * D + col;
-        *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-      } else if constexpr (MODE == MODE_SELECT) {
-        *reinterpret_cast<f32x4*>(a.residual + hoff + (size_t)p * D + col) = o;
-        if (a.o) {
-          uint16_t* out = static_cast<uint16_t*>(a.o) + hoff + (size_t)rtok[rb] * D + col;
+        const int col = 16 * db + 4 * lq;
+        const f32x4 o = oacc[db][rb] * inv;
+        if constexpr (MODE == MODE_PLAIN) {
+          uint16_t* out = static_cast<uint16_t*>(a.o) + hoff + (size_t)p * D + col;
           *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        } else if constexpr (MODE == MODE_SELECT) {
+          *reinterpret_cast<f32x4*>(a.residual + hoff + (size_t)p * D + col) = o;
+          if (a.o) {
+            uint16_t* out = static_cast<uint16_t*>(a.o) + hoff + (size_t)rtok[rb] * D + col;
+            *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+          }
+        } else if constexpr (MODE == MODE_REUSE) {
+          const f32x4 res = *reinterpret_cast<const f32x4*>(a.residual + hoff + (size_t)p * D + col);
+          const f32x4 y = o + res;
+          uint16_t* out = static_cast<uint16_t*>(a.o) + hoff + (size_t)rtok[rb] * D + col;
+          *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+        } else {  // MODE_RESINIT
+          f32x4* rp = reinterpret_cast<f32x4*>(a.residual + hoff + (size_t)p * D + col);
+          *rp = *rp - o;
         }
-      } else if constexpr (MODE == MODE_REUSE) {
-        const f32x4 res = *reinterpret_cast<const f32x4*>(a.residual + hoff + (size_t)p * D + col);
-        const f32x4 y = o + res;
-        uint16_t* out = static_cast<uint16_t*>(a.o) + hoff + (size_t)rtok[rb] * D + col;
-        *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-      } else {  // MODE_RESINIT
-        f32x4* rp = reinterpret_cast<f32x4*>(a.residual + hoff + (size_t)p * D + col);
-        *rp = *rp - o;
       }
     }
-  }
-  if constexpr (MODE != MODE_SELECT) return;
+  }  // MODE != MODE_SCORE
+  if constexpr (MODE != MODE_SCORE) return;
 
-  // ---- pass 2 (selection): per-group key scores c(j) = sum_i exp(s_ij - lse_i)
-  // Only K is needed, so a stage holds two K tiles (2 BK keys) and the
-  // barrier, the cross-wave reduction and the flush to global memory come
-  // once per 2 BK keys; the two halves are scored one after the other.
-  __syncthreads();
+  // ---- key-score pass (selection): per-group key scores
+  // c(j) = sum_i exp(s_ij - lse_i), from the rows' log-sum-exp that the
+  // selection's dense pass left in a.lse.  It is a launch of its own so that
+  // its registers (QK^T operands and scores only) allow four waves per SIMD
+  // instead of the dense pass's two.  Only K is needed, so a stage holds two
+  // K tiles (2 BK keys) and the barrier, the cross-wave reduction and the
+  // flush to global memory come once per 2 BK keys; the two halves are
+  // scored one after the other.
   float nlse[2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nlse[rb][i] = -lse_s[32 * w + 16 * rb + 4 * lq + i];
+    for (int i = 0; i < 4; ++i) {
+      const int p = row0 + 32 * w + 16 * rb + 4 * lq + i;
+      nlse[rb][i] = p < N ? -a.lse[(size_t)hs * N + p] : -INFINITY;
+    }
 
   constexpr int BK2 = 2 * BK;
   const int nt2 = (N + BK2 - 1) / BK2;
@@ -537,6 +550,7 @@ hipError_t launch_d(int mode, const AttnArgs& a, hipStream_t s) {
   switch (mode) {
     case MODE_PLAIN: return launch_one<D, 4, MODE_PLAIN>(a, s);
     case MODE_SELECT: return launch_one<D, 4, MODE_SELECT>(a, s);
+    case MODE_SCORE: return launch_one<D, 4, MODE_SCORE>(a, s);
     case MODE_REUSE:
       return a.G == 64 ? launch_one<D, 2, MODE_REUSE>(a, s) : launch_one<D, 4, MODE_REUSE>(a, s);
     case MODE_RESINIT:

@@ -8,9 +8,11 @@ namespace mcs {
 
 enum AttnMode : int {
   MODE_PLAIN = 0,    // dense, natural row order, O out
-  MODE_SELECT = 1,   // dense over group-sorted rows: O_dense (float32, sorted rows) + per-group key scores
+  MODE_SELECT = 1,   // dense over group-sorted rows: O_dense (float32, sorted rows) + row lse (bf16);
+                     // the float32 kernel also writes the per-group key scores
   MODE_REUSE = 2,    // sparse over cached keys + residual, O out in original order
-  MODE_RESINIT = 3   // sparse over cached keys at selection: residual -= O_sparse
+  MODE_RESINIT = 3,  // sparse over cached keys at selection: residual -= O_sparse
+  MODE_SCORE = 4     // selection key scores from the rows' log-sum-exp (bf16 only)
 };
 
 struct AttnArgs {
@@ -19,7 +21,8 @@ struct AttnArgs {
   const void* v;
   void* o;                   // PLAIN/REUSE: output; SELECT: optional dense output (original order)
   float* residual;           // [H][N][d], sorted-position rows
-  float* colsum;             // SELECT: [nheads][ng][ldc] key scores of the launched heads
+  float* colsum;             // SCORE: [nheads][ng][ldc] key scores of the launched heads
+  float* lse;                // SELECT out, SCORE in: [nheads][N] log2-sum-exp of the sorted rows
   const int32_t* perm;       // [H][N]
   const int32_t* keep;       // [H]
   const int64_t* idx_start;  // [H]

@@ -109,10 +109,10 @@ uint64_t colsum_ld(int N) { return align_up((uint64_t)N, 64); }
 uint64_t block_ld(int N) { return align_up((uint64_t)(N + 63) / 64, 64); }
 
 struct WsLayout {
-  uint64_t off_keys, off_proj, off_mean, off_colsum, per_head_colsum, per_head_block, fixed;
+  uint64_t off_keys, off_proj, off_mean, off_colsum, per_head_colsum, per_head_block, per_head_lse, fixed;
 };
 
-// keys | projections | query means | key scores [hc][ng][ldc] | block scores [hc][ng][ldb]
+// keys | projections | query means | key scores [hc][ng][ldc] | block scores [hc][ng][ldb] | row lse [hc][N]
 WsLayout ws_layout(const mcs_attn_desc* d, int32_t G) {
   const uint64_t H = (uint64_t)d->num_heads, N = (uint64_t)d->seq_len;
   const uint64_t ng = (N + G - 1) / G;
@@ -123,6 +123,7 @@ WsLayout ws_layout(const mcs_attn_desc* d, int32_t G) {
   w.off_colsum = align_up(w.off_mean + H * d->head_dim * 8, kAlign);
   w.per_head_colsum = ng * colsum_ld((int)N) * 4;
   w.per_head_block = ng * block_ld((int)N) * 4;
+  w.per_head_lse = align_up(N * 4, kAlign);
   w.fixed = w.off_colsum;
   return w;
 }
@@ -228,7 +229,7 @@ size_t mcs_select_workspace_bytes(const mcs_attn_desc* d, int32_t G, int32_t hea
   if (G != 64 && G != 128) return 0;
   const WsLayout w = ws_layout(d, G);
   const int64_t hc = std::max<int64_t>(1, std::min<int64_t>(heads_per_chunk, std::max(1, d->num_heads)));
-  return (size_t)(w.fixed + (uint64_t)hc * (w.per_head_colsum + w.per_head_block));
+  return (size_t)(w.fixed + (uint64_t)hc * (w.per_head_colsum + w.per_head_block + w.per_head_lse));
 }
 
 mcs_status mcs_meta_init(const mcs_attn_desc* d, int32_t G, const int32_t* keep, void* meta_buf,
@@ -297,7 +298,7 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
   if (!aligned(meta_buf, kAlign) || !aligned(ws, kAlign)) return MCS_ERROR_MISALIGNED;
   if (meta_bytes < m.bytes) return MCS_ERROR_BUFFER_TOO_SMALL;
   const WsLayout wl = ws_layout(d, G);
-  const uint64_t per_head = wl.per_head_colsum + wl.per_head_block;
+  const uint64_t per_head = wl.per_head_colsum + wl.per_head_block + wl.per_head_lse;
   if (ws_bytes < wl.fixed + per_head) return MCS_ERROR_BUFFER_TOO_SMALL;
   const int H = d->num_heads, N = d->seq_len, D = d->head_dim;
   const int hc = (int)std::min<uint64_t>((uint64_t)H, (ws_bytes - wl.fixed) / per_head);
@@ -311,6 +312,7 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
   uint8_t* keys = at<uint8_t>(ws, wl.off_keys);
   float* colsum = at<float>(ws, wl.off_colsum);
   float* bscore = at<float>(ws, wl.off_colsum + (uint64_t)hc * wl.per_head_colsum);
+  float* lse = at<float>(ws, wl.off_colsum + (uint64_t)hc * (wl.per_head_colsum + wl.per_head_block));
   int32_t* perm = at<int32_t>(meta_buf, m.off_perm);
   if (o.grouping == MCS_GROUPING_HASH || o.grouping == MCS_GROUPING_CENTRED_HASH) {
     double* mean = nullptr;
@@ -330,6 +332,7 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
   mcs::AttnArgs a = base_args(d, q, k, v);
   a.residual = at<float>(meta_buf, m.off_residual);
   a.colsum = colsum;
+  a.lse = lse;
   a.perm = perm;
   a.keep = at<int32_t>(meta_buf, m.off_keep);
   a.idx_start = at<int64_t>(meta_buf, m.off_idx_start);
@@ -344,6 +347,8 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
     a.nheads = std::min(hc, H - h0);
     a.o = o_dense_out;
     if ((e = launch_attn(d->dtype, mcs::MODE_SELECT, a, s)) != hipSuccess) return hip_fail(e);
+    if (d->dtype == MCS_DTYPE_BF16 && (e = launch_attn(d->dtype, mcs::MODE_SCORE, a, s)) != hipSuccess)
+      return hip_fail(e);
     if (o.kv_block == 1) {
       e = mcs::launch_group_topk(colsum, a.ldc, at<int32_t>(meta_buf, m.off_idx), a.keep, a.idx_start, h0,
                                  a.nheads, a.ng, N, 1, s);

@@ -338,7 +338,8 @@ def trace_summary(db, out, title, command):
     cur = sqlite3.connect(db).cursor()
     lines = [f"# {title}", "", f"command: `{command}`", "",
              "Template arguments of `attn_bf16_kernel<d, waves, mode, tile>`: mode 0 = dense baseline, 1 = selection "
-             "dense pass with key scores, 2 = reuse step, 3 = selection-time sparse pass and residual. The reuse-step "
+             "dense pass, 2 = reuse step, 3 = selection-time sparse pass and residual, 4 = selection key scores. The "
+             "reuse-step "
              "average here is the kernel behind the bench's `value`.", "",
              "| kernel | calls | total us | avg us | % |", "|---|---|---|---|---|"]
     for name, calls, tot, avg, pct in cur.execute("select * from top_kernels limit 14"):

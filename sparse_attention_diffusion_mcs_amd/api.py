@@ -30,6 +30,8 @@ def _check_qkv(q, k, v):
             raise ValueError("q, k, v must be contiguous")
     if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share shape and dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
 
 
 def _check_out(out, q):
@@ -39,13 +41,18 @@ def _check_out(out, q):
         raise ValueError("out must be a contiguous device tensor")
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError(f"out must be {tuple(q.shape)} {q.dtype}, got {tuple(out.shape)} {out.dtype}")
+    if out.device != q.device:
+        raise ValueError(f"out must be on {q.device}, got {out.device}")
 
 
-def _check_bytes(buf, name):
-    """Metadata and workspace buffers are contiguous uint8 device tensors:
-    their element count is the byte size handed to the library."""
+def _check_bytes(buf, name, device):
+    """Metadata and workspace buffers are contiguous uint8 tensors on the
+    inputs' device: their element count is the byte size handed to the
+    library."""
     if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous() or buf.dtype != torch.uint8:
         raise ValueError(f"{name} must be a contiguous uint8 device tensor")
+    if buf.device != device:
+        raise ValueError(f"{name} must be on {device}, got {buf.device}")
 
 
 def desc_for(q: torch.Tensor, scale: float | None = None) -> L.AttnDesc:
@@ -57,8 +64,12 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _stream(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
+def _stream(stream, device):
+    """The HIP stream handle for a call on `device`: the given stream, which
+    must belong to that device, or the device's current stream."""
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    if s.device != device:
+        raise ValueError(f"stream belongs to {s.device}, the tensors to {device}")
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -150,8 +161,10 @@ def dense_attn(q, k, v, out=None, scale=None, stream=None):
         out = torch.empty_like(q)
     _check_out(out, q)
     desc = desc_for(q, scale)
-    L.check(L.lib().mcs_dense_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream(stream)),
-            "mcs_dense_attn")
+    st = _stream(stream, q.device)
+    with torch.cuda.device(q.device):  # launches go to the calling thread's current device
+        L.check(L.lib().mcs_dense_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), st),
+                "mcs_dense_attn")
     return out
 
 
@@ -178,12 +191,16 @@ def meta_init(q, group_size, keep, meta_buf=None, stream=None) -> MetaCache:
     nbytes = int(L.lib().mcs_meta_bytes(ctypes.byref(desc), group_size, _i32p(ka)))
     if nbytes == 0:
         raise L.McsError(L.MCS_ERROR_INVALID_VALUE, "mcs_meta_bytes")
+    if not isinstance(q, torch.Tensor) or not q.is_cuda:
+        raise ValueError("q must be a device tensor")
     if meta_buf is None:
         meta_buf = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    _check_bytes(meta_buf, "meta_buf")
+    _check_bytes(meta_buf, "meta_buf", q.device)
     m = L.Meta()
-    L.check(L.lib().mcs_meta_init(ctypes.byref(desc), group_size, _i32p(ka), _ptr(meta_buf), meta_buf.numel(),
-                                  ctypes.byref(m), _stream(stream)), "mcs_meta_init")
+    st = _stream(stream, q.device)
+    with torch.cuda.device(q.device):
+        L.check(L.lib().mcs_meta_init(ctypes.byref(desc), group_size, _i32p(ka), _ptr(meta_buf), meta_buf.numel(),
+                                      ctypes.byref(m), st), "mcs_meta_init")
     return MetaCache(m, meta_buf)
 
 
@@ -205,18 +222,20 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
         raise L.McsError(L.MCS_ERROR_INVALID_VALUE, "mcs_meta_bytes")
     if meta_buf is None:
         meta_buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
-    _check_bytes(meta_buf, "meta_buf")
+    _check_bytes(meta_buf, "meta_buf", q.device)
     if workspace is None:
         workspace = torch.empty(max(workspace_bytes(q, group_size, heads_per_chunk), 256), dtype=torch.uint8,
                                 device=q.device)
-    _check_bytes(workspace, "workspace")
+    _check_bytes(workspace, "workspace", q.device)
     o_dense = torch.empty_like(q) if return_dense else None
     m = L.Meta()
     pjp = pj.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    st = _stream(stream, q.device)
     if grouping == "hash" and kv_block == 1 and residual:
-        L.check(L.lib().mcs_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
-                                   _ptr(meta_buf), meta_buf.numel(), _ptr(workspace), workspace.numel(),
-                                   _ptr(o_dense), ctypes.byref(m), _stream(stream)), "mcs_select")
+        with torch.cuda.device(q.device):
+            L.check(L.lib().mcs_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
+                                       _ptr(meta_buf), meta_buf.numel(), _ptr(workspace), workspace.numel(),
+                                       _ptr(o_dense), ctypes.byref(m), st), "mcs_select")
     else:
         codes = {"hash": L.MCS_GROUPING_HASH, "raster": L.MCS_GROUPING_RASTER,
                  "centred": L.MCS_GROUPING_CENTRED_HASH, "morton": L.MCS_GROUPING_MORTON}
@@ -224,10 +243,10 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
             raise ValueError(f"unknown grouping {grouping!r}")
         gt, gy, gx = (int(x) for x in grid) if grouping == "morton" else (0, 0, 0)
         opts = L.SelectOptions(codes[grouping], int(kv_block), 1 if residual else 0, gt, gy, gx)
-        L.check(L.lib().mcs_select_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
-                                      ctypes.byref(opts), _ptr(meta_buf), meta_buf.numel(), _ptr(workspace),
-                                      workspace.numel(), _ptr(o_dense), ctypes.byref(m), _stream(stream)),
-                "mcs_select_ex")
+        with torch.cuda.device(q.device):
+            L.check(L.lib().mcs_select_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
+                                          ctypes.byref(opts), _ptr(meta_buf), meta_buf.numel(), _ptr(workspace),
+                                          workspace.numel(), _ptr(o_dense), ctypes.byref(m), st), "mcs_select_ex")
     return MetaCache(m, meta_buf), o_dense
 
 
@@ -238,7 +257,10 @@ def sparse_attn(q, k, v, meta: MetaCache, out=None, scale=None, stream=None):
     if out is None:
         out = torch.empty_like(q)
     _check_out(out, q)
+    _check_bytes(meta.buffer, "the metadata buffer", q.device)
     desc = desc_for(q, scale)
-    L.check(L.lib().mcs_sparse_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(meta.meta),
-                                    _ptr(out), _stream(stream)), "mcs_sparse_attn")
+    st = _stream(stream, q.device)
+    with torch.cuda.device(q.device):
+        L.check(L.lib().mcs_sparse_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(meta.meta),
+                                        _ptr(out), st), "mcs_sparse_attn")
     return out

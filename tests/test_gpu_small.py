@@ -198,8 +198,8 @@ def test_selection_in_head_chunks_matches_one_pass(hc):
 def test_binding_rejects_bad_buffers():
     """The binding refuses caller buffers the kernels would write past or
     misread, before calling the library: outputs of another shape or dtype,
-    non-contiguous outputs, and metadata or workspace buffers that are not
-    contiguous uint8."""
+    non-contiguous outputs, metadata or workspace buffers that are not
+    contiguous uint8, and buffers or inputs off the inputs' device."""
     _need_gpu()
     p = build_problem((2, 4, 9), 1, 64, "bf16", 64, [16], 0.02, [1], wid=109)
     q, k, v = p.dev[0]
@@ -221,4 +221,9 @@ def test_binding_rejects_bad_buffers():
             mcs.select(q, k, v, 64, p.keeps, p.proj(), scale=sc, meta_buf=buf)
         with pytest.raises(ValueError):
             mcs.select(q, k, v, 64, p.keeps, p.proj(), scale=sc, workspace=buf)
+    host_meta = mcs.MetaCache(meta.meta, meta.buffer.cpu())
+    with pytest.raises(ValueError):
+        mcs.sparse_attn(q, k, v, host_meta, scale=sc)
+    with pytest.raises(ValueError):
+        mcs.dense_attn(q, k.cpu(), v, scale=sc)
     torch.cuda.synchronize()

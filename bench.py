@@ -195,6 +195,36 @@ def cpu_baseline(w, keeps, T, scale, n_groups, seed=0):
     }
 
 
+FLUSH_BYTES = 512 << 20  # more than the 256 MB MALL and every XCD's L2 together
+
+
+def cold_cache(X, meta, scale, T, steps, stream, mcs):
+    """Reuse and dense calls timed with cold caches: before each timed call a
+    512 MiB buffer is overwritten, which evicts the K/V rows that the
+    previous call left in the L2s and the MALL.  The fill runs outside the
+    events; the same treatment is given to both kernels."""
+    import torch
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(X[0][0])
+
+    def timed(fn, k):
+        flush.fill_(k & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        return a, b
+
+    reuse = [timed(lambda t=t: mcs.sparse_attn(*X[t], meta, out=out, scale=scale), t) for t in range(1, T + 1)]
+    dense = [timed(lambda k=k: mcs.dense_attn(*X[1 + k % T], out=out, scale=scale), k) for k in range(steps)]
+    torch.cuda.synchronize()
+    r = float(np.median([a.elapsed_time(b) for a, b in reuse]))
+    dn = float(np.median([a.elapsed_time(b) for a, b in dense]))
+    del flush
+    return {"flush_bytes": FLUSH_BYTES, "reuse_ms_median": round(r, 4), "dense_ms_median": round(dn, 4),
+            "speedup_vs_dense": round(dn / r, 3)}
+
+
 def rel_l2(a, b):
     import torch
     return float(torch.linalg.vector_norm(a.float() - b.float()) / torch.linalg.vector_norm(b.float()))
@@ -571,6 +601,8 @@ def main():
     torch.cuda.synchronize()
     dense_ms = [a.elapsed_time(b) for a, b in dev]
 
+    cold = cold_cache(X, meta, scale, T, args.steps, stream, mcs)
+
     # fidelity of reuse steps against dense attention on the same step
     fid = {}
     for t in sorted({1, max(1, T // 2), T}):
@@ -630,6 +662,7 @@ def main():
         "pct_bf16_peak_dense": round(100.0 * flops_dense / (dense_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "select_tflops": round(flops_select / (sel_med * 1e-3) / 1e12, 1),
         "fidelity_rel_l2_vs_dense": fid,
+        "cold_cache": cold,
         "meta_bytes": int(meta_buf.numel()),
         "select_workspace_bytes": int(ws.numel()),
         "peak_device_bytes": peak_mem,

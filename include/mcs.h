@@ -44,6 +44,10 @@
  *    host-side output struct and returns MCS_SUCCESS without launching.
  *  - The functions are re-entrant; calls that share output buffers on
  *    different streams race.
+ *  - Inputs are expected to be finite.  A NaN or infinity in Q, K or V
+ *    gives unspecified values in the outputs that depend on it (never an
+ *    access outside the buffers); the bf16 kernels are compiled on the
+ *    assumption that no NaN arises.
  */
 #ifndef MCS_H_
 #define MCS_H_

@@ -20,12 +20,15 @@ segment with raster query groups, centred-hash groups, whole 64-key KV
 blocks, no residual, and the coarse three together, each with its timings
 and per-step fidelity.
 
+With --cold-cache the line also carries reuse and dense times measured with
+the L2s and the MALL flushed (a 512 MiB buffer overwritten) before each call.
+
 With --sweep (workload 5) the line also carries the denoising-loop sweep:
 for every keep fraction and group size, a 30-step loop with re-selection every
 10 steps, its amortised time against 30 dense steps and the relative L2 error
 of every step's output against dense attention on that step.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--sweep] [--ablation]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--sweep] [--ablation] [--cold-cache]
 
 Three converters turn rocprofv3 results into the summaries kept in profiles/
 (no GPU needed):
@@ -73,6 +76,8 @@ def parse():
     ap.add_argument("--keep", type=float, default=None, help="override the keep fraction")
     ap.add_argument("--group", type=int, default=None, help="override the group size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="also time reuse and dense calls with the L2s and the MALL flushed before each call")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (a known-size reference for HBM counters)")
     ap.add_argument("--cpu-groups", type=int, default=288, help="oracle groups sampled per sampled head")
@@ -601,7 +606,7 @@ def main():
     torch.cuda.synchronize()
     dense_ms = [a.elapsed_time(b) for a, b in dev]
 
-    cold = cold_cache(X, meta, scale, T, args.steps, stream, mcs)
+    cold = cold_cache(X, meta, scale, T, args.steps, stream, mcs) if args.cold_cache else None
 
     # fidelity of reuse steps against dense attention on the same step
     fid = {}
@@ -662,7 +667,6 @@ def main():
         "pct_bf16_peak_dense": round(100.0 * flops_dense / (dense_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "select_tflops": round(flops_select / (sel_med * 1e-3) / 1e12, 1),
         "fidelity_rel_l2_vs_dense": fid,
-        "cold_cache": cold,
         "meta_bytes": int(meta_buf.numel()),
         "select_workspace_bytes": int(ws.numel()),
         "peak_device_bytes": peak_mem,
@@ -674,6 +678,8 @@ def main():
     if len(set(keeps.tolist())) > 1:
         ks, cnt = np.unique(keeps, return_counts=True)
         result["keep_histogram"] = {str(int(k)): int(c) for k, c in zip(ks, cnt)}
+    if cold is not None:
+        result["cold_cache"] = cold
     if sweep_res is not None:
         result["sweep"] = sweep_res
     if ablation_res is not None:

@@ -47,7 +47,7 @@ namespace mcs {
 namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
-constexpr float kLoSkip = 8.0f;        // log2 units: tiles below 2^-8 of the running max carry P as bf16 only
+constexpr float kLoSkip = 4.0f;        // log2 units: row blocks below 2^-4 of the running max carry P as bf16 only
 constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -294,6 +294,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
           for (int db = 0; db < DB; ++db) oacc[db][rb] *= alpha;
         }
       }
+      // The low part only matters where probabilities are large: the rounding
+      // error of the output is dominated by its largest terms.  A 16-row
+      // block whose probabilities in this tile all stay below 2^-kLoSkip of
+      // the running max neither forms nor multiplies its low parts; their
+      // rounding errors are at most 2^-(9 + kLoSkip) of the largest term.  The
+      // decision is taken per row block from the lanes' maxima.
+      bool big[2] = {false, false};
+      if constexpr (PRECISE_PV) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) big[rb] = __ballot(lmx[rb] > m_run[rb] - kLoSkip) != 0ull;
+      }
       bf16x8 pf[KC][2];
       bf16x8 pl[PRECISE_PV ? KC : 1][2];
 #pragma unroll
@@ -316,6 +327,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
                                       pack_bf16x2(s[2 * kc + 1][rb][2], s[2 * kc + 1][rb][3]));
           pf[kc][rb] = as_bf16x8(hi);
           if constexpr (PRECISE_PV) {
+            if (!big[rb]) continue;
             // low part p - bf16(p), so that P = hi + lo to ~16 significant bits
             const uint32_t h4[4] = {hi.x, hi.y, hi.z, hi.w};
             uint32_t lo[4];
@@ -343,25 +355,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
             oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kc][rb], oacc[db][rb], 0, 0, 0);
         }
       if constexpr (PRECISE_PV) {
-        // The low part only matters where probabilities are large: the rounding
-        // error of the output is dominated by its largest terms.  A tile whose
-        // probabilities all stay below 2^-kLoSkip of the running max skips its
-        // low-part products; their rounding errors are at most 2^-(9 + kLoSkip)
-        // of the largest term.  The decision is taken per wave from the lanes'
-        // maxima.
-        bool big = false;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) big |= lmx[rb] > m_run[rb] - kLoSkip;
-        if (__ballot(big) != 0ull) {
+        for (int rb = 0; rb < 2; ++rb) {
+          if (!big[rb]) continue;
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
               const bf16x8 vf = as_bf16x8(
                   make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y));
-#pragma unroll
-              for (int rb = 0; rb < 2; ++rb)
-                oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[kc][rb], oacc[db][rb], 0, 0, 0);
+              oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[kc][rb], oacc[db][rb], 0, 0, 0);
             }
         }
       }

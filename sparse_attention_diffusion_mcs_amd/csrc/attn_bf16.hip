@@ -10,7 +10,7 @@
 // softmax is renormalised over the kept tokens; the residual corrects it).
 //
 // Work decomposition.  A workgroup owns a tile of query rows, 32 rows per wave
-// (two 16-row MFMA blocks).  In the sparse modes the tile is exactly one query
+// (two 16-row MFMA blocks; 64 rows in the key-score pass).  In the sparse modes the tile is exactly one query
 // group (G = 64 -> 2 waves, G = 128 -> 4 waves), so all waves share the
 // group's gathered KV tiles; in the dense modes it is 128 rows (4 waves).
 //
@@ -85,7 +85,11 @@ __device__ __forceinline__ void wait_vm() {
 template <int D, int NW, int MODE, int BK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   using GE = Geo<D, BK>;
-  constexpr int BM = NW * 32;
+  // Query rows per wave: two 16-row MFMA blocks, or four in the key-score
+  // pass, whose registers hold only QK^T operands and scores.
+  constexpr int RB = (MODE == MODE_SCORE) ? 4 : 2;
+  constexpr int RPW = 16 * RB;
+  constexpr int BM = NW * RPW;
   constexpr int KK = D / 32;                 // k-steps of QK^T
   constexpr int DB = D / 16;                 // output column blocks
   constexpr int TB = BK / 16;                // 16-token blocks per tile
@@ -135,12 +139,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   const float sl2 = a.scale * kLog2e;
 
   // ---- Q fragments: lane holds row (16 rb + lr) of its wave, dims 8 lq + 32 kk ..
-  bf16x8 qf[2][KK];
-  int rtok[2];
-  bool rvalid[2];
+  bf16x8 qf[RB][KK];
+  int rtok[RB];
+  bool rvalid[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int p = row0 + 32 * w + 16 * rb + lr;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int p = row0 + RPW * w + 16 * rb + lr;
     rvalid[rb] = p < N;
     rtok[rb] = (MODE == MODE_PLAIN) ? p : (rvalid[rb] ? clamp_index(permh[p], N) : 0);
 #pragma unroll
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int rb = 0; rb < 2; ++rb) {
       const float l = quad_rows_sum(l_run[rb]);
       const float inv = 1.0f / l;
-      const int r = 32 * w + 16 * rb + lr;
+      const int r = RPW * w + 16 * rb + lr;
       const int p = row0 + r;
       if constexpr (MODE == MODE_SELECT) {
         if (lq == 0 && rvalid[rb]) a.lse[(size_t)hs * N + p] = m_run[rb] + __log2f(l);
@@ -432,23 +436,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   // ---- key-score pass (selection): per-group key scores
   // c(j) = sum_i exp(s_ij - lse_i), from the rows' log-sum-exp that the
   // selection's dense pass left in a.lse.  It is a launch of its own so that
-  // its registers (QK^T operands and scores only) allow four waves per SIMD
-  // instead of the dense pass's two.  Only K is needed, so a stage holds two
-  // K tiles (2 BK keys) and the barrier, the cross-wave reduction and the
-  // flush to global memory come once per 2 BK keys; the two halves are
-  // scored one after the other.
-  float nlse[2][4];
+  // its registers hold only QK^T operands and scores: 64 query rows per wave
+  // (each K operand read feeds twice the MFMAs, and a group of 64 needs no
+  // cross-wave sum) at three waves per SIMD, where the dense pass runs two.
+  // Only K is needed, so a stage holds two K tiles (2 BK keys) and the
+  // barrier, the reduction through LDS and the flush to global memory come
+  // once per 2 BK keys; the two halves are scored one after the other.
+  float nlse[RB][4];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int p = row0 + 32 * w + 16 * rb + 4 * lq + i;
+      const int p = row0 + RPW * w + 16 * rb + 4 * lq + i;
       nlse[rb][i] = p < N ? -a.lse[(size_t)hs * N + p] : -INFINITY;
     }
 
   constexpr int BK2 = 2 * BK;
   const int nt2 = (N + BK2 - 1) / BK2;
-  const int wpg = a.G / 32;   // waves per group
+  const int wpg = a.G / RPW;  // waves per group
   const int gpt = BM / a.G;   // groups per tile
   auto issue_k2 = [&](char* stage, int jj) {  // keys jj*BK2 .. +BK2-1 into both halves of a stage
 #pragma unroll
@@ -489,9 +494,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) kf[kk][tb] = kfrag(kt, tb, kk);
       // S[row][token]: lane holds rows 16 rb + 4 lq + i of token 16 tb + lr
-      f32x4 s[2][TB];
+      f32x4 s[RB][TB];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) s[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -499,13 +504,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
+          for (int rb = 0; rb < RB; ++rb)
             s[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rb][kk], kf[kk][tb], s[rb][tb], 0, 0, 0);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         float cs = 0.f;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float p = fast_exp2(fmaf(s[rb][tb][i], sl2, nlse[rb][i]));
@@ -538,7 +543,7 @@ constexpr int tile_tokens() {
 
 template <int D, int NW, int MODE>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  constexpr int BM = NW * 32;
+  constexpr int BM = NW * (MODE == MODE_SCORE ? 64 : 32);
   const int tiles = (MODE == MODE_REUSE || MODE == MODE_RESINIT) ? a.ng : (a.N + BM - 1) / BM;
   const long long nblocks = (long long)a.nheads * tiles;
   if (nblocks == 0) return hipSuccess;

@@ -219,6 +219,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     // ---- pass 1: online-softmax attention over the KV tiles ---------------
     float m_run[2] = {-1e30f, -1e30f};
     float l_run[2] = {0.f, 0.f};
+    float lref[2] = {-1e30f, -1e30f};  // this lane's maximum over the earlier tiles (low-part test)
     f32x4 oacc[DB][2];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -300,14 +301,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       }
       // The low part only matters where probabilities are large: the rounding
       // error of the output is dominated by its largest terms.  A 16-row
-      // block whose probabilities in this tile all stay below 2^-kLoSkip of
-      // the running max neither forms nor multiplies its low parts; their
-      // rounding errors are at most 2^-(9 + kLoSkip) of the largest term.  The
-      // decision is taken per row block from the lanes' maxima.
+      // block whose probabilities in this tile all stay below 2^-kLoSkip of a
+      // reference neither forms nor multiplies its low parts.  The reference
+      // is the larger of the lazily kept running max and the lane's own
+      // maximum over the earlier tiles; both are at most the row's true
+      // maximum, so the skipped rounding errors are at most 2^-(9 + kLoSkip)
+      // of the largest term.  The decision is taken per row block from the
+      // lanes' maxima.
       bool big[2] = {false, false};
       if constexpr (PRECISE_PV) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) big[rb] = __ballot(lmx[rb] > m_run[rb] - kLoSkip) != 0ull;
+        for (int rb = 0; rb < 2; ++rb) {
+          big[rb] = __ballot(lmx[rb] > __builtin_fmaxf(m_run[rb], lref[rb]) - kLoSkip) != 0ull;
+          lref[rb] = __builtin_fmaxf(lref[rb], lmx[rb]);
+        }
       }
       bf16x8 pf[KC][2];
       bf16x8 pl[PRECISE_PV ? KC : 1][2];

@@ -35,7 +35,7 @@ Three converters turn rocprofv3 results into the summaries kept in profiles/
 
     python bench.py --trace-summary RESULTS.db OUT.md "TITLE" "COMMAND"
     python bench.py --traffic-summary FETCH.db WRITE.db OUT.json GROUPING
-    python bench.py --counter-summary OUT.md RESULTS.db [RESULTS.db ...]
+    python bench.py --counter-summary OUT.md RESULTS.db [RESULTS.db ...] [--kernel NAME]
 """
 
 from __future__ import annotations
@@ -446,21 +446,29 @@ COUNTER_PASSES = [
 REUSE_KERNEL = "attn_bf16_kernel<128, 2, 2, 32>"
 
 
-def counter_summary(out, *dbs):
-    """Hardware counters of the workload-2 reuse launch (mean over its
-    dispatches) from rocprofv3 --pmc runs of the bench, with the ratios that
+def counter_summary(out, *args):
+    """Hardware counters of one kernel of the workload-2 bench (mean over its
+    dispatches; by default the reuse launch, else the kernel named after
+    --kernel) from rocprofv3 --pmc runs of the bench, with the ratios that
     locate its bottleneck.  GRBM_GUI_ACTIVE is summed over the eight XCDs, so
     the kernel's own clock is GUI / 8 / duration; per-CU and per-SIMD busy
     fractions divide by GUI / 8 and by 256 CUs or 1024 SIMDs; the SQ wave
     counters are in quad-cycles of one wave."""
     import sqlite3
+    args = list(args)
+    kernel = REUSE_KERNEL
+    if "--kernel" in args:
+        i = args.index("--kernel")
+        kernel = args[i + 1]
+        del args[i:i + 2]
+    dbs = args
     vals, durs = {}, []
     for db in dbs:
         cur = sqlite3.connect(db).cursor()
         acc = {}
         for name, value, start, end in cur.execute(
                 "select counter_name, value, start, end from counters_collection where kernel_name like ?",
-                (f"%{REUSE_KERNEL}%",)):
+                (f"%{kernel}%",)):
             acc.setdefault(name, []).append(float(value))
             if name == "GRBM_GUI_ACTIVE":
                 durs.append((end - start) * 1e-9)
@@ -486,7 +494,8 @@ def counter_summary(out, *dbs):
         ("mean TCP->L2 read latency (cycles)",
          vals.get("TCP_TCC_READ_REQ_LATENCY_sum", float("nan")) / vals.get("TCP_TCC_READ_REQ_sum", float("nan"))),
         ("L2 read requests per gathered 128-byte K/V line (1.0: no L1 reuse; Q, residual and index reads add the "
-         "rest)", vals.get("TCP_TCC_READ_REQ_sum", float("nan")) / (24 * 390 * 2496 * 2 * 256 / 128)),
+         "rest)", vals.get("TCP_TCC_READ_REQ_sum", float("nan")) / (24 * 390 * 2496 * 2 * 256 / 128)
+         if kernel == REUSE_KERNEL else float("nan")),
         ("L2 hit rate: TCC_HIT / (TCC_HIT + TCC_MISS)",
          vals.get("TCC_HIT_sum", float("nan")) / (vals.get("TCC_HIT_sum", 0.0) + vals.get("TCC_MISS_sum", 0.0) or
                                                    float("nan"))),
@@ -498,11 +507,13 @@ def counter_summary(out, *dbs):
     ]
     cmd = ("rocprofv3 --pmc {c} -d gpurun_out/cnt_{i} -o cnt -- python3 bench.py --steps 1 --warmup 0 "
            "--no-cpu-baseline")
-    lines = [f"# Counters of the workload-2 reuse launch (`{REUSE_KERNEL}`)", "",
+    what = "reuse launch" if kernel == REUSE_KERNEL else "launch"
+    lines = [f"# Counters of the workload-2 {what} (`{kernel}`)", "",
              f"Source hash of `attn_bf16.hip`: `{src_hash(ATTN_SRC)}`. Mean over the launch's dispatches in each pass; "
              f"median dispatch time under counter collection {dur * 1e3:.3f} ms.", "", "Commands:", ""]
     lines += [f"- `{cmd.format(c=c, i=i + 1)}`" for i, c in enumerate(COUNTER_PASSES)]
-    lines += [f"- `python3 bench.py --counter-summary {out} {' '.join(dbs)}`", "",
+    sel = "" if kernel == REUSE_KERNEL else f' --kernel "{kernel}"'
+    lines += [f"- `python3 bench.py --counter-summary {out} {' '.join(dbs)}{sel}`", "",
               "| derived | value |", "|---|---|"]
     lines += [f"| {k} | {v:.3f} |" for k, v in derived]
     lines += ["", "| counter | mean per dispatch |", "|---|---|"]

@@ -58,6 +58,17 @@ def test_counter_summary_ratios(tmp_path):
     assert "| mean TCP->L2 read latency (cycles) | 250.000 |" in text
     assert "| TD stalled waiting for TC data, per CU | nan |" in text  # not collected
     assert b.src_hash(b.ATTN_SRC) in text
+    # --kernel selects another launch of the same run: its GUI cycles are 7x
+    # over the same 1 ms, so its clock reads 14 GHz and its busy fractions
+    # keep their ratios
+    out2 = tmp_path / "c2.md"
+    b.counter_summary(str(out2), db, "--kernel", "attn_bf16_kernel<128, 4, 0, 32>")
+    text2 = out2.read_text()
+    assert "attn_bf16_kernel<128, 4, 0, 32>" in text2.splitlines()[0]
+    assert "| kernel clock (GHz): GUI / 8 / duration | 14.000 |" in text2
+    assert "| MFMA pipe busy, per SIMD | 0.400 |" in text2
+    assert "gathered 128-byte K/V line" in text2 and "line (1.0: no L1 reuse; Q, residual and index reads add the " \
+        "rest) | nan |" in text2
 
 
 def test_traffic_summary_scales_by_the_copy_probe(tmp_path):

@@ -48,7 +48,8 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 constexpr float kLoSkip = 4.0f;        // log2 units: row blocks below 2^-4 of the running max carry P as bf16 only
-constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
+constexpr int kBufferConfig = 0x00020000;
+constexpr long long kScoreItems = 12288;   // key-score work items to aim for (~16 rounds of resident workgroups)  // raw buffer resource word 3 (gfx9 family)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -114,8 +115,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 
   // ---- work item -------------------------------------------------------
   const int tiles = SPARSE ? a.ng : (N + BM - 1) / BM;
-  const int L = xcd_remap(blockIdx.x, a.nheads * tiles, a.run);
-  const int hs = L / tiles, tile = L % tiles;
+  // The key-score pass also splits the keys into kchunks ranges (scores of
+  // different keys are independent); its work items run row tile fastest, so
+  // the items in flight on an XCD share a key range of one head.
+  const int kchunks = (MODE == MODE_SCORE && a.kchunks > 1) ? a.kchunks : 1;
+  const int L = xcd_remap(blockIdx.x, a.nheads * tiles * kchunks, a.run);
+  const int hs = L / (tiles * kchunks), tile = L % tiles, kc = (L / tiles) % kchunks;
   const int h = (MODE == MODE_REUSE) ? clamp_index(a.sched[hs], a.H) : a.head0 + hs;
   const int row0 = tile * BM;
   const size_t hoff = (size_t)h * N * D;
@@ -460,6 +465,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 
   constexpr int BK2 = 2 * BK;
   const int nt2 = (N + BK2 - 1) / BK2;
+  const int per = (nt2 + kchunks - 1) / kchunks;  // super-tiles per key range
+  const int jbeg = min(nt2, kc * per), jend = min(nt2, jbeg + per);
   const int wpg = a.G / RPW;  // waves per group
   const int gpt = BM / a.G;   // groups per tile
   auto issue_k2 = [&](char* stage, int jj) {  // keys jj*BK2 .. +BK2-1 into both halves of a stage
@@ -490,8 +497,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   auto score_tile = [&](int jj, const char* cur, char* nxt) {
     wait_vm<0>();
     __syncthreads();
-    if (jj + 1 < nt2) issue_k2(nxt, jj + 1);
-    if (jj > 0) flush(jj - 1);
+    if (jj + 1 < jend) issue_k2(nxt, jj + 1);
+    if (jj > jbeg) flush(jj - 1);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const char* kt = cur + half * GE::TILE;
@@ -528,13 +535,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  if (nt2 > 0) issue_k2(st0, 0);
-  for (int jj = 0; jj < nt2; jj += 2) {
+  if (jend > jbeg) issue_k2(st0, jbeg);
+  for (int jj = jbeg; jj < jend; jj += 2) {
     score_tile(jj, st0, st1);
-    if (jj + 1 < nt2) score_tile(jj + 1, st1, st0);
+    if (jj + 1 < jend) score_tile(jj + 1, st1, st0);
   }
   __syncthreads();
-  if (nt2 > 0) flush(nt2 - 1);
+  if (jend > jbeg) flush(jend - 1);
 }
 
 // KV tile size: 32 tokens at d = 128 (the batched K and V operand reads of a
@@ -552,11 +559,20 @@ template <int D, int NW, int MODE>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int BM = NW * (MODE == MODE_SCORE ? 64 : 32);
   const int tiles = (MODE == MODE_REUSE || MODE == MODE_RESINIT) ? a.ng : (a.N + BM - 1) / BM;
-  const long long nblocks = (long long)a.nheads * tiles;
+  AttnArgs b = a;
+  b.kchunks = 1;
+  if constexpr (MODE == MODE_SCORE) {
+    // Enough work items for the last of the rounds of resident workgroups
+    // to be a small part of the launch.
+    const long long items = (long long)a.nheads * tiles;
+    const int nt2 = (a.N + 2 * tile_tokens<D>() - 1) / (2 * tile_tokens<D>());
+    if (items > 0) b.kchunks = (int)std::max<long long>(1, std::min<long long>(nt2, (kScoreItems + items - 1) / items));
+  }
+  const long long nblocks = (long long)a.nheads * tiles * b.kchunks;
   if (nblocks == 0) return hipSuccess;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_bf16_kernel<D, NW, MODE, tile_tokens<D>()>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
-                     s, a);
+                     s, b);
   return hipGetLastError();
 }
 

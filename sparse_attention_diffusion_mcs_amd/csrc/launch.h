@@ -34,6 +34,7 @@ struct AttnArgs {
   int nheads;                // heads in the launch
   float scale;               // softmax scale
   int run;                   // XCD run length (logical blocks per XCD per round)
+  int kchunks;               // SCORE: key ranges per row tile (set at launch)
 };
 
 // bf16 MFMA kernels (attn_bf16.hip)

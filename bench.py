@@ -265,6 +265,7 @@ def sweep(w, X, threads, scale, grouping):
             ws = torch.empty(mcs.workspace_bytes(X[0][0], G), dtype=torch.uint8, device="cuda")
             mb = torch.empty(int(mcs.meta_layout(H, N, d, 1, G, keeps).bytes), dtype=torch.uint8, device="cuda")
             out = torch.empty_like(X[0][0])
+            od = torch.empty_like(X[0][0])
             gkw = grouping_kw(wk, grouping)
             mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws, **gkw)  # warm-up
             torch.cuda.synchronize()
@@ -274,8 +275,8 @@ def sweep(w, X, threads, scale, grouping):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 if t % R == 0:
                     e0.record(stream)
-                    meta, od = mcs.select(*X[t], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws,
-                                          return_dense=True, **gkw)
+                    meta, _ = mcs.select(*X[t], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws,
+                                         dense_out=od, **gkw)
                     e1.record(stream)
                     torch.cuda.synchronize()
                     sel_ms.append(e0.elapsed_time(e1))
@@ -347,7 +348,7 @@ def ablation(w, X, keeps, scale, base):
         mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws, **opt)  # warm-up
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * T + 2)]
         e[0].record(stream)
-        meta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws, **opt)
+        meta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws, dense_out=out, **opt)
         e[1].record(stream)
         err = []
         for t in range(1, T + 1):
@@ -578,7 +579,9 @@ def main():
     def segment(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        meta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=meta_buf, workspace=ws,
+        # the selection step also produces its own attention output (the exact
+        # dense one), as it would inside a denoising loop
+        meta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=meta_buf, workspace=ws, dense_out=out,
                              **grouping_kw(w, args.grouping))
         if ev is not None:
             ev[1].record(stream)

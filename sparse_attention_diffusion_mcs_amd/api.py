@@ -205,11 +205,13 @@ def meta_init(q, group_size, keep, meta_buf=None, stream=None) -> MetaCache:
 
 
 def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace=None, heads_per_chunk=None,
-           return_dense=False, stream=None, grouping="hash", kv_block=1, residual=True, grid=None):
+           return_dense=False, stream=None, grouping="hash", kv_block=1, residual=True, grid=None, dense_out=None):
     """Selection step (mcs_select; mcs_select_ex for the other groupings --
     "raster", "centred", "morton" with the (T, Y, X) `grid` -- and the
-    failure-mode ablations kv_block 64, residual False).  Returns
-    (MetaCache, dense output or None)."""
+    failure-mode ablations kv_block 64, residual False).  The step's exact
+    dense output is written to `dense_out` when given (a tensor like q), else
+    to a new tensor when return_dense is set.  Returns (MetaCache, dense
+    output or None)."""
     _check_qkv(q, k, v)
     H, N, d = q.shape
     desc = desc_for(q, scale)
@@ -227,7 +229,11 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
         workspace = torch.empty(max(workspace_bytes(q, group_size, heads_per_chunk), 256), dtype=torch.uint8,
                                 device=q.device)
     _check_bytes(workspace, "workspace", q.device)
-    o_dense = torch.empty_like(q) if return_dense else None
+    if dense_out is not None:
+        _check_out(dense_out, q)
+        o_dense = dense_out
+    else:
+        o_dense = torch.empty_like(q) if return_dense else None
     m = L.Meta()
     pjp = pj.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
     st = _stream(stream, q.device)

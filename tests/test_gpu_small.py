@@ -195,6 +195,21 @@ def test_selection_in_head_chunks_matches_one_pass(hc):
     assert torch.equal(od, od_ref)
 
 
+def test_selection_writes_a_caller_dense_output():
+    """`dense_out` receives the same bytes as the dense output the binding
+    allocates with return_dense; a buffer of another shape is refused."""
+    _need_gpu()
+    p = build_problem((2, 4, 9), 1, 64, "bf16", 64, [16], 0.02, [1], wid=110)
+    sc = scale_for(64)
+    _, od = mcs.select(*p.dev[0], 64, p.keeps, p.proj(), scale=sc, return_dense=True)
+    buf = torch.full_like(od, float("nan"))
+    _, od2 = mcs.select(*p.dev[0], 64, p.keeps, p.proj(), scale=sc, dense_out=buf)
+    torch.cuda.synchronize()
+    assert od2 is buf and torch.equal(buf, od)
+    with pytest.raises(ValueError):
+        mcs.select(*p.dev[0], 64, p.keeps, p.proj(), scale=sc, dense_out=buf[:, :-1])
+
+
 def test_binding_rejects_bad_buffers():
     """The binding refuses caller buffers the kernels would write past or
     misread, before calling the library: outputs of another shape or dtype,

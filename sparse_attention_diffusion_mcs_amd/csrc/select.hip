@@ -152,8 +152,12 @@ __global__ __launch_bounds__(SORT_NT) void perm_sort_kernel(const uint8_t* __res
 // so their bit patterns order like the values.  Three histogram passes over
 // bits [31:21], [20:10], [9:0] find the k-th largest pattern T exactly; a
 // final ordered pass writes every index with score > T and the lowest-index
-// (k - #greater) indices with score == T, in ascending index order.
+// (k - #greater) indices with score == T, in ascending index order.  When
+// the first pass's bin of T holds at most TK_CAP scores, a second read copies
+// them into LDS and the last two passes run there: three reads of the row
+// instead of four.
 constexpr int TK_NT = 256;
+constexpr int TK_CAP = 4096;
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = __lane_id();
@@ -200,8 +204,9 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
                                                            const int64_t* __restrict__ idx_start, int head0, int ng,
                                                            int N, int block) {
   __shared__ int hist[2048];
+  __shared__ uint32_t cand[TK_CAP];
   __shared__ int sh[8];
-  __shared__ int found[2];
+  __shared__ int found[3];
   const int tid = threadIdx.x;
   const int g = blockIdx.x, hl = blockIdx.y, h = head0 + hl;
   const uint32_t* row = reinterpret_cast<const uint32_t*>(colsum + ((size_t)hl * ng + g) * ldc);
@@ -210,13 +215,10 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
 
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : 2048;
-    for (int b = tid; b < 2048; b += TK_NT) hist[b] = 0;
-    __syncthreads();
-    // 16 consecutive scores per thread and step: four 16-byte loads in flight
-    // before the histogram updates (rows start 256-byte aligned)
+  // Reads the row 16 consecutive scores per thread and step (four 16-byte
+  // loads in flight; rows start 256-byte aligned) and hands each in-range
+  // score to f.
+  auto scan_row = [&](auto f) {
     for (int j0 = 16 * tid; j0 < N; j0 += 16 * TK_NT) {
       uint32_t u[16];
       if (j0 + 16 <= N) {
@@ -234,7 +236,23 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        if (j0 + e < N && (u[e] & pmask) == prefix) atomicAdd(&hist[(u[e] >> shift) & (nb - 1)], 1);
+        if (j0 + e < N) f(u[e]);
+    }
+  };
+  bool in_lds = false;
+  int ncand = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    for (int b = tid; b < 2048; b += TK_NT) hist[b] = 0;
+    __syncthreads();
+    auto count = [&](uint32_t x) {
+      if ((x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & (nb - 1)], 1);
+    };
+    if (in_lds) {
+      for (int c = tid; c < ncand; c += TK_NT) count(cand[c]);
+    } else {
+      scan_row(count);
     }
     __syncthreads();
     // thread t owns bins [t*per, (t+1)*per); `above` = elements in higher bins
@@ -250,6 +268,7 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
         if (above + hist[bin] >= krem) {
           found[0] = bin;
           found[1] = above;
+          found[2] = hist[bin];
           break;
         }
         above += hist[bin];
@@ -259,7 +278,19 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
     prefix |= (uint32_t)found[0] << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     krem -= found[1];
+    const int in_bin = found[2];
     __syncthreads();
+    if (pass == 0 && in_bin <= TK_CAP) {
+      // second read: the scores in T's bin, to LDS (exactly in_bin of them)
+      if (tid == 0) sh[0] = 0;
+      __syncthreads();
+      scan_row([&](uint32_t x) {
+        if ((x & pmask) == prefix) cand[atomicAdd(&sh[0], 1)] = x;
+      });
+      __syncthreads();
+      ncand = in_bin;
+      in_lds = true;
+    }
   }
   const uint32_t T = prefix;
 

@@ -7,7 +7,7 @@ import torch
 
 import oracle.mcs_oracle as orc
 from mcs_inputs import WORKLOADS
-from parity import assert_close, build_problem, check_idx, scale_for, to_np
+from parity import assert_close, build_problem, check_idx, sample_groups, scale_for, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -193,6 +193,34 @@ def test_selection_in_head_chunks_matches_one_pass(hc):
     for region in ("perm", "keep", "idx_start", "sched", "idx", "residual"):
         assert torch.equal(getattr(meta, region), getattr(ref, region)), region
     assert torch.equal(od, od_ref)
+
+
+def test_topk_on_rows_with_one_crowded_bin():
+    """Rows whose scores are all equal (q = 0) or nearly equal put far more
+    than the 4096 scores the top-k holds in LDS into the first-pass bin of
+    the k-th score, so its last passes run over global memory.  Equal scores
+    keep exactly the lowest indices; near-equal ones meet the kept-key rule
+    against the oracle."""
+    _need_gpu()
+    N, d, G, keep = 8192, 64, 64, 300
+    sc = scale_for(d)
+    g = torch.Generator().manual_seed(7)
+    proj = np.zeros((8, d), np.float32)
+    for case, qscale in (("equal", 0.0), ("near-equal", 1e-3)):
+        print(f"[case] crowded top-k bin: {case}, N={N}, keep={keep}", flush=True)
+        q = (qscale * torch.randn((1, N, d), generator=g)).to(torch.bfloat16)
+        k = torch.randn((1, N, d), generator=g).to(torch.bfloat16)
+        v = torch.randn((1, N, d), generator=g).to(torch.bfloat16)
+        meta, _ = mcs.select(q.cuda(), k.cuda(), v.cuda(), G, [keep], proj, scale=sc, grouping="raster")
+        idx = meta.head_idx(0, keep).cpu().numpy()
+        torch.cuda.synchronize()
+        qn, kn, vn = (t[0].float().numpy() for t in (q, k, v))
+        for gi in sample_groups(N // G, extra=2, seed=1):
+            if case == "equal":
+                assert np.array_equal(idx[gi], np.arange(keep)), f"group {gi}: {idx[gi][:8]}"
+            else:
+                _, pr = orc.attention(qn[gi * G:(gi + 1) * G], kn, vn, sc)
+                check_idx(idx[gi], orc.group_scores(pr), keep, N, f"near-equal group {gi}")
 
 
 def test_selection_writes_a_caller_dense_output():

@@ -20,15 +20,21 @@ segment with raster query groups, centred-hash groups, whole 64-key KV
 blocks, no residual, and the coarse three together, each with its timings
 and per-step fidelity.
 
-With --cold-cache the line also carries reuse and dense times measured with
-the L2s and the MALL flushed (a 512 MiB buffer overwritten) before each call.
+The line also carries reuse and dense times measured with the L2s and the
+MALL flushed (a 512 MiB buffer overwritten) before each call (--no-cold-cache
+skips them), the selection's phases timed with events the library records
+between them, the achieved HBM rates of the index-gather kernels (top-k,
+hash and sort) on algorithmic bytes, and the same segment with Z-curve
+query groups as a secondary measurement (--no-zcurve skips it).  Queries are
+grouped by MC-Sparse's 8-bit sign hash unless --grouping says otherwise.
 
 With --sweep (workload 5) the line also carries the denoising-loop sweep:
 for every keep fraction and group size, a 30-step loop with re-selection every
 10 steps, its amortised time against 30 dense steps and the relative L2 error
 of every step's output against dense attention on that step.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--sweep] [--ablation] [--cold-cache]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--seed 0] [--grouping hash]
+                    [--sweep] [--ablation] [--no-cold-cache] [--no-zcurve] [--no-cpu-baseline]
 
 Three converters turn rocprofv3 results into the summaries kept in profiles/
 (no GPU needed):
@@ -76,14 +82,17 @@ def parse():
     ap.add_argument("--keep", type=float, default=None, help="override the keep fraction")
     ap.add_argument("--group", type=int, default=None, help="override the group size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-cache", action="store_true",
-                    help="also time reuse and dense calls with the L2s and the MALL flushed before each call")
+    ap.add_argument("--no-cold-cache", action="store_true",
+                    help="skip timing reuse and dense calls with the L2s and the MALL flushed before each call")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (a known-size reference for HBM counters)")
     ap.add_argument("--cpu-groups", type=int, default=288, help="oracle groups sampled per sampled head")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 8))
-    ap.add_argument("--grouping", default="morton", choices=["morton", "hash", "raster", "centred"],
-                    help="query grouping: Z-curve over the latent grid (default), sign hash, raster, centred hash")
+    ap.add_argument("--grouping", default="hash", choices=["hash", "morton", "raster", "centred"],
+                    help="query grouping: 8-bit sign hash (default, MC-Sparse), Z-curve over the latent grid, "
+                         "raster, centred hash")
+    ap.add_argument("--seed", type=int, default=0, help="seed of the synthetic inputs and hash projections")
+    ap.add_argument("--no-zcurve", action="store_true", help="skip the secondary Z-curve-grouping measurement")
     ap.add_argument("--ablation", action="store_true",
                     help="add the failure-mode ablations (raster groups, 64-key blocks, no residual)")
     ap.add_argument("--sweep", action="store_true",
@@ -235,7 +244,7 @@ def rel_l2(a, b):
     return float(torch.linalg.vector_norm(a.float() - b.float()) / torch.linalg.vector_norm(b.float()))
 
 
-def sweep(w, X, threads, scale, grouping):
+def sweep(w, X, threads, scale, grouping, seed=0):
     """Denoising-loop sweep: for each (keep, G), steps 0..S-1 with selection on
     the steps divisible by the re-selection interval and reuse on the others;
     every step's output is compared with dense attention on that step."""
@@ -246,7 +255,7 @@ def sweep(w, X, threads, scale, grouping):
     S, R = w.sweep["steps"], w.reselect
     H, N, d = w.heads, w.seq_len, w.head_dim
     stream = torch.cuda.current_stream()
-    proj = hash_projections(0, w.wid, d)
+    proj = hash_projections(seed, w.wid, d)
     dense = {}
     dense_ms = []
     for t in range(S):  # dense outputs of every step (the fidelity reference), each timed
@@ -261,7 +270,7 @@ def sweep(w, X, threads, scale, grouping):
     for G in w.sweep["group"]:
         for frac in w.sweep["keep"]:
             wk = w.with_(keep_frac=(frac,), group=G)
-            keeps = wk.keeps()
+            keeps = wk.keeps(seed)
             ws = torch.empty(mcs.workspace_bytes(X[0][0], G), dtype=torch.uint8, device="cuda")
             mb = torch.empty(int(mcs.meta_layout(H, N, d, 1, G, keeps).bytes), dtype=torch.uint8, device="cuda")
             out = torch.empty_like(X[0][0])
@@ -324,7 +333,7 @@ def grouping_kw(w, grouping):
     return dict(grouping=grouping, grid=w.grid) if grouping == "morton" else dict(grouping=grouping)
 
 
-def ablation(w, X, keeps, scale, base):
+def ablation(w, X, keeps, scale, base, seed=0):
     """Each failure-mode ablation on the workload's segment (selection on step
     0, reuse on steps 1..T): timings and the relative L2 of every reuse step
     against dense attention on that step."""
@@ -334,7 +343,7 @@ def ablation(w, X, keeps, scale, base):
 
     H, N, d, G, T = w.heads, w.seq_len, w.head_dim, w.group, w.reuse_steps
     stream = torch.cuda.current_stream()
-    proj = hash_projections(0, w.wid, d)
+    proj = hash_projections(seed, w.wid, d)
     dense = {t: mcs.dense_attn(*X[t], scale=scale) for t in range(1, T + 1)}
     ws = torch.empty(mcs.workspace_bytes(X[0][0], G), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(X[0][0])
@@ -523,6 +532,89 @@ def counter_summary(out, *args):
         f.write("\n".join(lines) + "\n")
 
 
+PHASES = ("grouping", "dense_pass", "key_scores", "topk", "residual_pass")
+
+
+def gather_rates(w, keeps, phase_ms, grouping):
+    """Achieved HBM rates of the index-gather kernels of the selection, on
+    algorithmic bytes: the top-k reads every score row once and writes the
+    kept indices; the sign-hash grouping reads Q once and writes the 8-bit
+    keys, and the stable sort reads the keys and writes the permutation."""
+    H, N, d, ng = w.heads, w.seq_len, w.head_dim, w.num_groups
+    ldc = -(-N // 64) * 64
+    topk_bytes = H * ng * N * 4 + int(np.sum(keeps)) * ng * 4
+    rows = [("topk", topk_bytes, phase_ms["topk"])]
+    if grouping in ("hash", "centred"):
+        rows.append(("hash_and_sort", H * N * d * 2 + H * N + H * N + H * N * 4, phase_ms["grouping"]))
+    out = {}
+    for name, nbytes, ms in rows:
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"bytes": int(nbytes), "us": round(ms * 1e3, 1), "gbs": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    out["topk"]["score_row_stride_floats"] = ldc
+    return out
+
+
+def time_segments(mcs, X, w, keeps, proj, scale, grouping, steps, warmup, meta_buf, ws, out):
+    """Selection on step 0 (phases marked with events) and T reuse steps,
+    `steps` times after `warmup` untimed segments; returns the per-segment
+    events, the phase events and the wall time."""
+    import torch
+    T, G = w.reuse_steps, w.group
+    stream = torch.cuda.current_stream()
+    gkw = grouping_kw(w, grouping)
+
+    def segment(ev=None, ph=None):
+        if ev is not None:
+            ev[0].record(stream)
+        # the selection step also produces its own attention output (the exact
+        # dense one), as it would inside a denoising loop
+        meta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=meta_buf, workspace=ws, dense_out=out,
+                             phase_events=ph, **gkw)
+        if ev is not None:
+            ev[1].record(stream)
+        for t in range(1, T + 1):
+            if ev is not None:
+                ev[2 * t].record(stream)
+            mcs.sparse_attn(*X[t], meta, out=out, scale=scale)
+            if ev is not None:
+                ev[2 * t + 1].record(stream)
+        return meta
+
+    for _ in range(warmup):
+        segment()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * T + 2)] for _ in range(steps)]
+    phs = [[torch.cuda.Event(enable_timing=True) for _ in PHASES] for _ in range(steps)]
+    for ph in phs:  # the HIP events exist once recorded; recorded here, outside the timed region
+        for e in ph:
+            e.record(stream)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(steps):
+        meta = segment(evs[k], phs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    reuse_ms = [e[2 * t].elapsed_time(e[2 * t + 1]) for e in evs for t in range(1, T + 1)]
+    phase_ms = {}
+    for i, name in enumerate(PHASES):
+        phase_ms[name] = float(np.median([(e[0] if i == 0 else ph[i - 1]).elapsed_time(ph[i])
+                                          for e, ph in zip(evs, phs)]))
+    return meta, sel_ms, reuse_ms, phase_ms, wall
+
+
+def fidelity(mcs, X, meta, scale, T):
+    import torch
+    fid = {}
+    for t in sorted({1, max(1, T // 2), T}):
+        o_s = mcs.sparse_attn(*X[t], meta, scale=scale).float()
+        o_d = mcs.dense_attn(*X[t], scale=scale).float()
+        fid[str(t)] = round(float(torch.linalg.vector_norm(o_s - o_d) / torch.linalg.vector_norm(o_d)), 6)
+    torch.cuda.synchronize()
+    return fid
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--counter-summary":
         counter_summary(*sys.argv[2:])
@@ -548,16 +640,16 @@ def main():
     mcs.lib()  # fail loudly if the library is missing
 
     w = workload_of(args)
-    keeps = w.keeps()
+    keeps = w.keeps(args.seed)
     H, N, d, G, T = w.heads, w.seq_len, w.head_dim, w.group, w.reuse_steps
     scale = float(np.float32(1.0 / math.sqrt(d)))
-    log(f"workload {args.workload}: {describe(w, keeps)}")
+    log(f"workload {args.workload}: {describe(w, keeps)}; grouping {args.grouping}; seed {args.seed}")
     if args.sweep and not w.sweep:
         print("--sweep needs a workload with a sweep (workload 5)", file=sys.stderr)
         sys.exit(2)
     t0 = time.time()
     n_steps = max(T + 1, w.sweep["steps"] if args.sweep else 0)
-    X = generate(w, range(0, n_steps), args.threads)
+    X = generate(w, range(0, n_steps), args.threads, args.seed)
     torch.cuda.synchronize()
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -568,7 +660,7 @@ def main():
         del src, dst
     log(f"inputs generated and resident ({time.time() - t0:.1f} s)")
 
-    proj = hash_projections(0, w.wid, d)
+    proj = hash_projections(args.seed, w.wid, d)
     q0 = X[0][0]
     ws = torch.empty(mcs.workspace_bytes(q0, G), dtype=torch.uint8, device="cuda")
     meta_probe = mcs.meta_layout(H, N, d, 1, G, keeps)
@@ -576,37 +668,10 @@ def main():
     out = torch.empty_like(q0)
     stream = torch.cuda.current_stream()
 
-    def segment(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        # the selection step also produces its own attention output (the exact
-        # dense one), as it would inside a denoising loop
-        meta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=meta_buf, workspace=ws, dense_out=out,
-                             **grouping_kw(w, args.grouping))
-        if ev is not None:
-            ev[1].record(stream)
-        for t in range(1, T + 1):
-            if ev is not None:
-                ev[2 * t].record(stream)
-            mcs.sparse_attn(*X[t], meta, out=out, scale=scale)
-            if ev is not None:
-                ev[2 * t + 1].record(stream)
-        return meta
-
-    for _ in range(args.warmup):
-        segment()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * T + 2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(args.steps):
-        meta = segment(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    reuse_ms = [e[2 * t].elapsed_time(e[2 * t + 1]) for e in evs for t in range(1, T + 1)]
+    meta, sel_ms, reuse_ms, phase_ms, wall = time_segments(mcs, X, w, keeps, proj, scale, args.grouping, args.steps,
+                                                           args.warmup, meta_buf, ws, out)
     log(f"segments: wall {1e3 * wall / args.steps:.3f} ms/segment; select {np.median(sel_ms):.3f} ms; "
-        f"reuse mean {np.mean(reuse_ms):.4f} ms")
+        f"reuse mean {np.mean(reuse_ms):.4f} ms; phases {phase_ms}")
 
     # dense baseline on the same inputs
     dense_out = torch.empty_like(q0)
@@ -620,19 +685,8 @@ def main():
     torch.cuda.synchronize()
     dense_ms = [a.elapsed_time(b) for a, b in dev]
 
-    cold = cold_cache(X, meta, scale, T, args.steps, stream, mcs) if args.cold_cache else None
-
-    # fidelity of reuse steps against dense attention on the same step
-    fid = {}
-    for t in sorted({1, max(1, T // 2), T}):
-        o_s = mcs.sparse_attn(*X[t], meta, scale=scale).float()
-        o_d = mcs.dense_attn(*X[t], scale=scale).float()
-        fid[str(t)] = round(float(torch.linalg.vector_norm(o_s - o_d) / torch.linalg.vector_norm(o_d)), 6)
-    torch.cuda.synchronize()
-
-    sweep_res = sweep(w, X, args.threads, scale, args.grouping) if args.sweep else None
-    ablation_res = ablation(w, X, keeps, scale, args.grouping) if args.ablation else None
-    peak_mem = int(torch.cuda.max_memory_allocated())
+    cold = None if args.no_cold_cache else cold_cache(X, meta, scale, T, args.steps, stream, mcs)
+    fid = fidelity(mcs, X, meta, scale, T)
 
     reuse_mean = float(np.mean(reuse_ms))
     sel_med = float(np.median(sel_ms))
@@ -640,6 +694,27 @@ def main():
     flops_reuse = 4.0 * N * float(np.sum(keeps)) * d  # sum over heads of 4 N k_h d
     flops_dense = 4.0 * N * N * d * H
     flops_select = 1.5 * flops_dense + flops_reuse
+
+    zc = None
+    if not args.no_zcurve and args.grouping != "morton":
+        # the same segment with Z-curve groups over the latent grid (a grouping
+        # the pages do not name; secondary to the sign hash)
+        _, zsel, zreuse, zphase, _ = time_segments(mcs, X, w, keeps, proj, scale, "morton", args.steps, 1, meta_buf,
+                                                   ws, out)
+        zmeta, _ = mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=meta_buf, workspace=ws,
+                              **grouping_kw(w, "morton"))
+        zr = float(np.mean(zreuse))
+        zc = {"grouping": "z-curve over the %dx%dx%d latent grid" % w.grid, "reuse_ms": round(zr, 4),
+              "select_ms": round(float(np.median(zsel)), 3),
+              "pct_bf16_peak_reuse": round(100.0 * flops_reuse / (zr * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+              "speedup_vs_dense": round(dense_med / zr, 3),
+              "fidelity_rel_l2_vs_dense": fidelity(mcs, X, zmeta, scale, T)}
+        del zmeta
+
+    sweep_res = sweep(w, X, args.threads, scale, args.grouping, args.seed) if args.sweep else None
+    ablation_res = ablation(w, X, keeps, scale, args.grouping, args.seed) if args.ablation else None
+    peak_mem = int(torch.cuda.max_memory_allocated())
+
     achieved = flops_reuse / (reuse_mean * 1e-3) / 1e12
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -647,7 +722,8 @@ def main():
             with open(TRAFFIC_FILE) as f:
                 tr = json.load(f)
             if (tr.get("source_sha") == src_hash(ATTN_SRC) and tr.get("workload") == args.workload
-                    and tr.get("grouping", "hash") == args.grouping and args.keep is None and args.group is None):
+                    and tr.get("grouping", "hash") == args.grouping and args.keep is None and args.group is None
+                    and args.seed == 0):
                 traffic = tr.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
@@ -665,7 +741,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded DiT-shaped generator; no model weights)",
         "config": {"workload": describe(w, keeps), "heads": H, "seq_len": N, "head_dim": d, "group": G,
-                   "keep": [int(x) for x in sorted(set(keeps.tolist()))], "reuse_steps": T,
+                   "keep": [int(x) for x in sorted(set(keeps.tolist()))], "reuse_steps": T, "seed": args.seed,
                    "grouping": {"morton": "z-curve over the %dx%dx%d latent grid" % w.grid,
                                 "hash": "8-bit sign hash", "raster": "raster order",
                                 "centred": "centred 8-bit sign hash"}[args.grouping]},
@@ -675,12 +751,14 @@ def main():
         "dense_ms": round(dense_med, 4),
         "speedup_vs_dense": round(dense_med / reuse_mean, 3),
         "select_ms": round(sel_med, 3),
+        "select_phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "amortised_ms_per_denoising_step": round((sel_med + T * reuse_mean) / (T + 1), 4),
         "amortised_speedup_vs_dense": round(dense_med * (T + 1) / (sel_med + T * reuse_mean), 3),
         "pct_bf16_peak_reuse": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
         "pct_bf16_peak_dense": round(100.0 * flops_dense / (dense_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "select_tflops": round(flops_select / (sel_med * 1e-3) / 1e12, 1),
         "fidelity_rel_l2_vs_dense": fid,
+        "gather": gather_rates(w, keeps, phase_ms, args.grouping),
         "meta_bytes": int(meta_buf.numel()),
         "select_workspace_bytes": int(ws.numel()),
         "peak_device_bytes": peak_mem,
@@ -694,13 +772,15 @@ def main():
         result["keep_histogram"] = {str(int(k)): int(c) for k, c in zip(ks, cnt)}
     if cold is not None:
         result["cold_cache"] = cold
+    if zc is not None:
+        result["zcurve"] = zc
     if sweep_res is not None:
         result["sweep"] = sweep_res
     if ablation_res is not None:
         result["ablation"] = ablation_res
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(w, keeps, T, scale, args.cpu_groups)
+        result["cpu_baseline"] = cpu_baseline(w, keeps, T, scale, args.cpu_groups, args.seed)
     print(json.dumps(result), flush=True)
 
 

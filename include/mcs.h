@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MCS_VERSION 1
+#define MCS_VERSION 2
 #define MCS_META_VERSION 1
 #define MCS_HASH_BITS 8
 #define MCS_MAX_SEQ_LEN (1 << 22)
@@ -229,7 +229,16 @@ typedef struct mcs_select_options {
                         sparse output renormalised over the kept keys alone */
   int32_t grid_t, grid_y, grid_x;  /* MCS_GROUPING_MORTON: the latent grid, each in [1, 1024], product N;
                                       0 for every other grouping */
+  /* Tracing (no effect on the results): NULL, or an array of num_phase_events (0 to
+     MCS_SELECT_PHASES) hipEvent_t handles created by the caller on the device of the call.  Event i
+     is recorded on the stream when phase i of the selection has been launched: 0 grouping (hash and
+     sort, or the fixed order), 1 dense pass, 2 key scores, 3 top-k, 4 residual pass.  When the
+     workspace makes the selection run in head chunks, events 1-4 mark the last chunk's phases. */
+  void* const* phase_events;
+  int32_t num_phase_events;
 } mcs_select_options;
+
+#define MCS_SELECT_PHASES 5
 
 /*
  * mcs_select with options (NULL = MC-Sparse: hash groups, single tokens,

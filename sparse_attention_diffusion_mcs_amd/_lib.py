@@ -20,6 +20,8 @@ MCS_DTYPE_FP32 = 0
 MCS_DTYPE_BF16 = 1
 MCS_META_VERSION = 1
 MCS_HASH_BITS = 8
+MCS_VERSION = 2
+MCS_SELECT_PHASES = 5
 MCS_MAX_SEQ_LEN = 1 << 22
 
 MCS_GROUPING_HASH = 0
@@ -48,7 +50,8 @@ class Meta(ctypes.Structure):
 
 class SelectOptions(ctypes.Structure):
     _fields_ = [("grouping", ctypes.c_int32), ("kv_block", ctypes.c_int32), ("residual", ctypes.c_int32),
-                ("grid_t", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_x", ctypes.c_int32)]
+                ("grid_t", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_x", ctypes.c_int32),
+                ("phase_events", ctypes.POINTER(ctypes.c_void_p)), ("num_phase_events", ctypes.c_int32)]
 
 
 class McsError(RuntimeError):

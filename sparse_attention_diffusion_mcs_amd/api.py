@@ -205,13 +205,16 @@ def meta_init(q, group_size, keep, meta_buf=None, stream=None) -> MetaCache:
 
 
 def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace=None, heads_per_chunk=None,
-           return_dense=False, stream=None, grouping="hash", kv_block=1, residual=True, grid=None, dense_out=None):
+           return_dense=False, stream=None, grouping="hash", kv_block=1, residual=True, grid=None, dense_out=None,
+           phase_events=None):
     """Selection step (mcs_select; mcs_select_ex for the other groupings --
-    "raster", "centred", "morton" with the (T, Y, X) `grid` -- and the
-    failure-mode ablations kv_block 64, residual False).  The step's exact
-    dense output is written to `dense_out` when given (a tensor like q), else
-    to a new tensor when return_dense is set.  Returns (MetaCache, dense
-    output or None)."""
+    "raster", "centred", "morton" with the (T, Y, X) `grid` -- the
+    failure-mode ablations kv_block 64, residual False, and tracing).  The
+    step's exact dense output is written to `dense_out` when given (a tensor
+    like q), else to a new tensor when return_dense is set.  `phase_events`:
+    up to MCS_SELECT_PHASES torch.cuda.Event objects, recorded on the stream
+    as the grouping, dense pass, key scores, top-k and residual pass are
+    launched.  Returns (MetaCache, dense output or None)."""
     _check_qkv(q, k, v)
     H, N, d = q.shape
     desc = desc_for(q, scale)
@@ -237,7 +240,17 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
     m = L.Meta()
     pjp = pj.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
     st = _stream(stream, q.device)
-    if grouping == "hash" and kv_block == 1 and residual:
+    ev_arr = None
+    if phase_events:
+        if len(phase_events) > L.MCS_SELECT_PHASES:
+            raise ValueError(f"at most {L.MCS_SELECT_PHASES} phase events")
+        handles = []
+        for ev in phase_events:
+            if ev.cuda_event == 0:  # torch creates the HIP event on its first record
+                ev.record(torch.cuda.current_stream(q.device))
+            handles.append(ev.cuda_event)
+        ev_arr = (ctypes.c_void_p * len(handles))(*handles)
+    if grouping == "hash" and kv_block == 1 and residual and ev_arr is None:
         with torch.cuda.device(q.device):
             L.check(L.lib().mcs_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
                                        _ptr(meta_buf), meta_buf.numel(), _ptr(workspace), workspace.numel(),
@@ -248,7 +261,9 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
         if grouping not in codes:
             raise ValueError(f"unknown grouping {grouping!r}")
         gt, gy, gx = (int(x) for x in grid) if grouping == "morton" else (0, 0, 0)
-        opts = L.SelectOptions(codes[grouping], int(kv_block), 1 if residual else 0, gt, gy, gx)
+        opts = L.SelectOptions(codes[grouping], int(kv_block), 1 if residual else 0, gt, gy, gx,
+                               ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr is not None else None,
+                               len(phase_events) if ev_arr is not None else 0)
         with torch.cuda.device(q.device):
             L.check(L.lib().mcs_select_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
                                           ctypes.byref(opts), _ptr(meta_buf), meta_buf.numel(), _ptr(workspace),

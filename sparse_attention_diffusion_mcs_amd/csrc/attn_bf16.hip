@@ -48,8 +48,8 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 constexpr float kLoSkip = 4.0f;        // log2 units: row blocks below 2^-4 of the running max carry P as bf16 only
-constexpr int kBufferConfig = 0x00020000;
-constexpr long long kScoreItems = 12288;   // key-score work items to aim for (~16 rounds of resident workgroups)  // raw buffer resource word 3 (gfx9 family)
+constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
+constexpr long long kScoreItems = 12288;   // key-score work items to aim for (~16 rounds of resident workgroups)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -548,11 +548,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 // 64-token tile would not fit the register budget), 64 tokens at d = 64.
 template <int D>
 constexpr int tile_tokens() {
-#ifdef MCS_BK
-  return MCS_BK;
-#else
   return D == 128 ? 32 : 64;
-#endif
 }
 
 template <int D, int NW, int MODE>

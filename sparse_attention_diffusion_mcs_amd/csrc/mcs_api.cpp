@@ -17,10 +17,9 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr uint64_t kAlign = 256;
-#ifndef MCS_XCD_RUN
-#define MCS_XCD_RUN 128
-#endif
-constexpr int kXcdRun = MCS_XCD_RUN;  // consecutive work items per XCD per round
+// Consecutive work items per XCD per round of the block remap: 128 groups of
+// one head share an XCD's L2 (runs of 32, 64 and 256 measured slower).
+constexpr int kXcdRun = 128;
 
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -266,12 +265,16 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
   if ((st = check_desc(d)) != MCS_SUCCESS) return st;
   if ((st = check_group_keep(d, G, keep)) != MCS_SUCCESS) return st;
   if (!meta_out) return MCS_ERROR_INVALID_VALUE;
-  mcs_select_options o{MCS_GROUPING_HASH, 1, 1, 0, 0, 0};
+  mcs_select_options o{MCS_GROUPING_HASH, 1, 1, 0, 0, 0, nullptr, 0};
   if (opts) o = *opts;
   if ((o.grouping != MCS_GROUPING_HASH && o.grouping != MCS_GROUPING_RASTER &&
        o.grouping != MCS_GROUPING_CENTRED_HASH && o.grouping != MCS_GROUPING_MORTON) ||
       (o.kv_block != 1 && o.kv_block != 64) || (o.residual != 0 && o.residual != 1))
     return MCS_ERROR_INVALID_VALUE;
+  if (o.num_phase_events < 0 || o.num_phase_events > MCS_SELECT_PHASES || (o.num_phase_events > 0 && !o.phase_events))
+    return MCS_ERROR_INVALID_VALUE;
+  for (int i = 0; i < o.num_phase_events; ++i)
+    if (!o.phase_events[i]) return MCS_ERROR_INVALID_VALUE;
   if (o.grouping == MCS_GROUPING_MORTON) {
     for (int g : {o.grid_t, o.grid_y, o.grid_x})
       if (g < 1 || g > 1024) return MCS_ERROR_INVALID_VALUE;
@@ -328,6 +331,12 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
   } else if ((e = mcs::launch_iota_perm(perm, H, N, s)) != hipSuccess) {
     return hip_fail(e);
   }
+  // Tracing: event i marks the end of phase i on the stream.
+  auto mark = [&](int phase) -> hipError_t {
+    return phase < o.num_phase_events ? hipEventRecord(static_cast<hipEvent_t>(o.phase_events[phase]), s)
+                                      : hipSuccess;
+  };
+  if ((e = mark(0)) != hipSuccess) return hip_fail(e);
 
   mcs::AttnArgs a = base_args(d, q, k, v);
   a.residual = at<float>(meta_buf, m.off_residual);
@@ -346,9 +355,11 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
     a.head0 = h0;
     a.nheads = std::min(hc, H - h0);
     a.o = o_dense_out;
-    if ((e = launch_attn(d->dtype, mcs::MODE_SELECT, a, s)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_attn(d->dtype, mcs::MODE_SELECT, a, s)) != hipSuccess || (e = mark(1)) != hipSuccess)
+      return hip_fail(e);
     if (d->dtype == MCS_DTYPE_BF16 && (e = launch_attn(d->dtype, mcs::MODE_SCORE, a, s)) != hipSuccess)
       return hip_fail(e);
+    if ((e = mark(2)) != hipSuccess) return hip_fail(e);
     if (o.kv_block == 1) {
       e = mcs::launch_group_topk(colsum, a.ldc, at<int32_t>(meta_buf, m.off_idx), a.keep, a.idx_start, h0,
                                  a.nheads, a.ng, N, 1, s);
@@ -359,13 +370,13 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
         e = mcs::launch_group_topk(bscore, ldb, at<int32_t>(meta_buf, m.off_idx), a.keep, a.idx_start, h0,
                                    a.nheads, a.ng, nb, o.kv_block, s);
     }
-    if (e != hipSuccess) return hip_fail(e);
+    if (e != hipSuccess || (e = mark(3)) != hipSuccess) return hip_fail(e);
     a.o = nullptr;
     if (o.residual)
       e = launch_attn(d->dtype, mcs::MODE_RESINIT, a, s);
     else
       e = mcs::launch_zero_floats(a.residual + (size_t)h0 * N * D, (long long)a.nheads * N * D, s);
-    if (e != hipSuccess) return hip_fail(e);
+    if (e != hipSuccess || (e = mark(4)) != hipSuccess) return hip_fail(e);
   }
   *meta_out = m;
   return MCS_SUCCESS;

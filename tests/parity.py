@@ -216,3 +216,79 @@ def check_blocks(gpu_idx, scores, k, n, block, what):
     assert low.size == 0, f"{what}: clearly-out blocks kept {low[:8]}"
     _, _, ob = orc.topk_blocks(scores, k, block)
     return bool(np.array_equal(ob, kept))
+
+
+def check_every_unit(p: Problem, meta, sc, outs, heads, label="", dense=(), dense_heads=(), grouping="hash"):
+    """Compares every (head, group) unit of the listed heads with the oracle,
+    on host copies of the GPU's outputs.
+
+    For every head in `heads` (a thread per head): the permutation of the
+    whole head (oracle grouping), every group's kept keys (ascending,
+    distinct, in range), and every group's reuse output at every step in
+    `outs`, against the oracle evaluated on the GPU's own permutation, kept
+    keys and residual.
+
+    For every head in `dense_heads` (a subset of `heads`) the dense side is
+    checked on every row as well: each group's kept keys against the oracle's
+    exact group scores (kept-key rule), the cached residual against the
+    oracle's dense minus sparse rows, and the dense output `dense` (original
+    token order) against the oracle's dense rows, for each (name, tensor) in
+    `dense`.
+
+    Returns the number of kept-key sets equal to the oracle's and the number
+    checked (dense_heads only)."""
+    import threadpoolctl
+
+    perm_all = meta.perm.cpu().numpy()
+    idx_all = meta.idx.cpu().numpy()
+    starts = meta.idx_start.cpu().numpy()
+    res_all = meta.residual.cpu().numpy()
+    outs_h = {t: to_np(o) for t, o in outs.items()}
+    dense_h = [(name, to_np(x)) for name, x in dense]
+    ranges = orc.group_ranges(p.N, p.G)
+
+    def kept(h):
+        kh = int(p.keeps[h])
+        return idx_all[starts[h]:starts[h] + p.ng * kh].reshape(p.ng, kh).astype(np.int64)
+
+    def head_job(h):
+        kh = int(p.keeps[h])
+        q0, k0, v0 = p.heads_np[(h, 0)]
+        perm_o = orc.select_head(q0, k0, v0, p.proj(), p.G, kh, sc, groups=[], grouping=grouping, grid=p.grid).perm
+        assert np.array_equal(perm_all[h], perm_o), f"{label} head {h}: perm differs"
+        gidx = kept(h)
+        assert np.all(np.diff(gidx, axis=1) > 0), f"{label} head {h}: kept keys not strictly ascending"
+        assert gidx.min() >= 0 and gidx.max() < p.N, f"{label} head {h}: kept key out of range"
+        for t, o in outs_h.items():
+            qt, kt, vt = p.heads_np[(h, t)]
+            for g, (s, e) in enumerate(ranges):
+                rows = perm_all[h, s:e]
+                ref = orc.reuse_group(qt, kt, vt, rows, gidx[g], res_all[h, s:e].astype(np.float64), sc)
+                assert_close(o[h, rows], ref, p.dtype, f"{label} head {h} group {g} reuse step {t}")
+
+    with threadpoolctl.threadpool_limits(1), cf.ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(head_job, heads))
+
+    exact = total = 0
+    for h in dense_heads:
+        # whole chunks of groups in sorted order: the exact probabilities of a
+        # chunk's rows give each group's scores, dense rows and residual
+        kh = int(p.keeps[h])
+        q0, k0, v0 = p.heads_np[(h, 0)]
+        gidx = kept(h)
+        per = max(1, 1024 // p.G)
+        for g0 in range(0, p.ng, per):
+            gs = range(g0, min(p.ng, g0 + per))
+            base = ranges[gs[0]][0]
+            rows = perm_all[h, base:ranges[gs[-1]][1]]
+            o_d, pr = orc.attention(q0[rows], k0, v0, sc)
+            for name, x in dense_h:
+                assert_close(x[h, rows], o_d, p.dtype, f"{label} head {h} {name}, rows of groups {g0}..")
+            for g in gs:
+                a, b = ranges[g][0] - base, ranges[g][1] - base
+                exact += check_idx(gidx[g], orc.group_scores(pr[a:b]), kh, p.N, f"{label} head {h} group {g}")
+                total += 1
+                res_c = o_d[a:b] - orc.sparse_attention(q0[rows[a:b]], k0, v0, gidx[g], sc)
+                assert_close(res_all[h, ranges[g][0]:ranges[g][1]], res_c, p.dtype,
+                             f"{label} head {h} group {g} residual", ref_norm=np.linalg.norm(o_d[a:b]))
+    return exact, total

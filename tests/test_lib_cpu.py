@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mcs_version() == 1
+    assert lib.mcs_version() == L.MCS_VERSION == 2
     assert lib.mcs_status_string(0) == b"MCS_SUCCESS"
     assert lib.mcs_status_string(6) == b"MCS_ERROR_HIP"
     assert lib.mcs_status_string(99) == b"MCS_UNKNOWN_STATUS"
@@ -168,6 +168,14 @@ def test_select_ex_options_validation(lib):
     # the options do not bypass the ordinary checks
     zero, zp = _i32([0, 64])
     assert call(O(1, 1, 0), keep_p=zp) == L.MCS_ERROR_INVALID_VALUE
+    # tracing events: at most MCS_SELECT_PHASES, an array when any, no null handle
+    evs = (ctypes.c_void_p * 6)(*([FAKE.value] * 6))
+    ep = ctypes.cast(evs, ctypes.POINTER(ctypes.c_void_p))
+    assert call(O(0, 1, 1, 0, 0, 0, ep, L.MCS_SELECT_PHASES + 1)) == L.MCS_ERROR_INVALID_VALUE
+    assert call(O(0, 1, 1, 0, 0, 0, None, 1)) == L.MCS_ERROR_INVALID_VALUE
+    assert call(O(0, 1, 1, 0, 0, 0, ep, -1)) == L.MCS_ERROR_INVALID_VALUE
+    evs[1] = None
+    assert call(O(0, 1, 1, 0, 0, 0, ep, 2)) == L.MCS_ERROR_INVALID_VALUE
 
 
 def test_sparse_validation(lib):

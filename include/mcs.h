@@ -251,6 +251,28 @@ mcs_status mcs_select_ex(const mcs_attn_desc* desc, const void* q, const void* k
                          size_t ws_bytes, void* o_dense_out, mcs_meta* meta_out, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * mcs_select_ex without a caller workspace.  The workspace is an array of
+ * MCS_NOALLOC_SCRATCH_BYTES inside the library, one per device, held from
+ * the first use on that device until the process ends.  It must hold the
+ * selection's fixed workspace part plus one head's scores, i.e.
+ * mcs_select_workspace_bytes(desc, group_size, 1) <= MCS_NOALLOC_SCRATCH_BYTES
+ * (else MCS_ERROR_BUFFER_TOO_SMALL, before any other check or launch); the
+ * heads then run in as many chunks as the array needs.  Every other argument,
+ * result and error is as for mcs_select_ex.  All calls on one device share
+ * the array: calls that overlap on one device (on different streams, or
+ * from different threads without ordering) race.  Nothing in the array
+ * needs to start at zero, so each call may follow any earlier one.
+ */
+#define MCS_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+mcs_status mcs_select_noalloc(const mcs_attn_desc* desc, const void* q, const void* k, const void* v,
+                              int32_t group_size, const int32_t* keep_host, const float* hash_proj_host,
+                              const mcs_select_options* options, void* meta_buf, size_t meta_bytes,
+                              void* o_dense_out, mcs_meta* meta_out, void* stream);
+
+/*
  * Reuse step (same abstract: the cached groups, indices and residual serve
  * the later denoising steps; the residual restores the attention contribution that renormalising over
  * the kept tokens loses, section "What Trips People Up" of "The quality cliff

@@ -22,6 +22,7 @@ MCS_META_VERSION = 1
 MCS_HASH_BITS = 8
 MCS_VERSION = 2
 MCS_SELECT_PHASES = 5
+MCS_NOALLOC_SCRATCH_BYTES = 128 << 20
 MCS_MAX_SEQ_LEN = 1 << 22
 
 MCS_GROUPING_HASH = 0
@@ -31,7 +32,7 @@ MCS_GROUPING_MORTON = 3
 
 EXPORTS = ("mcs_version", "mcs_status_string", "mcs_last_hip_error", "mcs_dense_attn", "mcs_meta_layout",
            "mcs_meta_bytes", "mcs_select_workspace_bytes", "mcs_meta_init", "mcs_select", "mcs_select_ex",
-           "mcs_sparse_attn")
+           "mcs_sparse_attn", "mcs_select_noalloc")
 
 
 class AttnDesc(ctypes.Structure):
@@ -107,6 +108,9 @@ def open_library(path):
     lib.mcs_select_ex.restype = ctypes.c_int
     lib.mcs_select_ex.argtypes = [DP, P, P, P, ctypes.c_int32, I32P, F32P, ctypes.POINTER(SelectOptions), P,
                                   ctypes.c_size_t, P, ctypes.c_size_t, P, MP, P]
+    lib.mcs_select_noalloc.restype = ctypes.c_int
+    lib.mcs_select_noalloc.argtypes = [DP, P, P, P, ctypes.c_int32, I32P, F32P, ctypes.POINTER(SelectOptions), P,
+                                       ctypes.c_size_t, P, MP, P]
     lib.mcs_sparse_attn.restype = ctypes.c_int
     lib.mcs_sparse_attn.argtypes = [DP, P, P, P, MP, P, P]
     return lib

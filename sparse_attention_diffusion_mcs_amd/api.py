@@ -206,7 +206,7 @@ def meta_init(q, group_size, keep, meta_buf=None, stream=None) -> MetaCache:
 
 def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace=None, heads_per_chunk=None,
            return_dense=False, stream=None, grouping="hash", kv_block=1, residual=True, grid=None, dense_out=None,
-           phase_events=None):
+           phase_events=None, noalloc=False):
     """Selection step (mcs_select; mcs_select_ex for the other groupings --
     "raster", "centred", "morton" with the (T, Y, X) `grid` -- the
     failure-mode ablations kv_block 64, residual False, and tracing).  The
@@ -214,7 +214,9 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
     like q), else to a new tensor when return_dense is set.  `phase_events`:
     up to MCS_SELECT_PHASES torch.cuda.Event objects, recorded on the stream
     as the grouping, dense pass, key scores, top-k and residual pass are
-    launched.  Returns (MetaCache, dense output or None)."""
+    launched.  With noalloc the call is mcs_select_noalloc: the workspace is
+    the library's own per-device array (no `workspace` may be given).
+    Returns (MetaCache, dense output or None)."""
     _check_qkv(q, k, v)
     H, N, d = q.shape
     desc = desc_for(q, scale)
@@ -228,10 +230,14 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
     if meta_buf is None:
         meta_buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     _check_bytes(meta_buf, "meta_buf", q.device)
-    if workspace is None:
-        workspace = torch.empty(max(workspace_bytes(q, group_size, heads_per_chunk), 256), dtype=torch.uint8,
-                                device=q.device)
-    _check_bytes(workspace, "workspace", q.device)
+    if noalloc:
+        if workspace is not None or heads_per_chunk is not None:
+            raise ValueError("noalloc uses the library's own workspace")
+    else:
+        if workspace is None:
+            workspace = torch.empty(max(workspace_bytes(q, group_size, heads_per_chunk), 256), dtype=torch.uint8,
+                                    device=q.device)
+        _check_bytes(workspace, "workspace", q.device)
     if dense_out is not None:
         _check_out(dense_out, q)
         o_dense = dense_out
@@ -250,7 +256,7 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
                 ev.record(torch.cuda.current_stream(q.device))
             handles.append(ev.cuda_event)
         ev_arr = (ctypes.c_void_p * len(handles))(*handles)
-    if grouping == "hash" and kv_block == 1 and residual and ev_arr is None:
+    if grouping == "hash" and kv_block == 1 and residual and ev_arr is None and not noalloc:
         with torch.cuda.device(q.device):
             L.check(L.lib().mcs_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
                                        _ptr(meta_buf), meta_buf.numel(), _ptr(workspace), workspace.numel(),
@@ -265,9 +271,16 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
                                ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr is not None else None,
                                len(phase_events) if ev_arr is not None else 0)
         with torch.cuda.device(q.device):
-            L.check(L.lib().mcs_select_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
-                                          ctypes.byref(opts), _ptr(meta_buf), meta_buf.numel(), _ptr(workspace),
-                                          workspace.numel(), _ptr(o_dense), ctypes.byref(m), st), "mcs_select_ex")
+            if noalloc:
+                L.check(L.lib().mcs_select_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size,
+                                                   _i32p(ka), pjp, ctypes.byref(opts), _ptr(meta_buf),
+                                                   meta_buf.numel(), _ptr(o_dense), ctypes.byref(m), st),
+                        "mcs_select_noalloc")
+            else:
+                L.check(L.lib().mcs_select_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka),
+                                              pjp, ctypes.byref(opts), _ptr(meta_buf), meta_buf.numel(),
+                                              _ptr(workspace), workspace.numel(), _ptr(o_dense), ctypes.byref(m),
+                                              st), "mcs_select_ex")
     return MetaCache(m, meta_buf), o_dense
 
 

@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmcs.so")
 ARCH = os.environ.get("MCS_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["attn_bf16.hip", "attn_f32.hip", "select.hip", "mcs_api.cpp"]
+SOURCES = ["attn_bf16.hip", "attn_f32.hip", "select.hip", "mcs_api.cpp", "noalloc.hip"]
 
 # Packed fp32 VALU instructions are turned off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

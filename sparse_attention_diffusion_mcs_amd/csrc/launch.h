@@ -59,6 +59,9 @@ hipError_t launch_iota_perm(int32_t* perm, int H, int N, hipStream_t s);
 // Z-curve order of a raster-ordered (T, Y, X) grid, N = T * Y * X, every dim <= 1024
 hipError_t launch_morton_perm(int32_t* perm, int H, int N, int T, int Y, int X, hipStream_t s);
 hipError_t launch_zero_floats(float* p, long long n, hipStream_t s);
+// Device address of the current device's MCS_NOALLOC_SCRATCH_BYTES scratch
+// array (noalloc.hip), the workspace of mcs_select_noalloc.
+hipError_t noalloc_scratch(void** out);
 // Writes `nbytes` bytes from host memory to device memory through kernel
 // arguments (asynchronous on s, safe for pageable and stack host memory).
 hipError_t launch_fill_bytes(void* dst, const void* src, size_t nbytes, hipStream_t s);

@@ -257,10 +257,15 @@ mcs_status mcs_select(const mcs_attn_desc* d, const void* q, const void* k, cons
                        meta_out, stream);
 }
 
-mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, const void* v, int32_t G,
-                         const int32_t* keep, const float* proj, const mcs_select_options* opts, void* meta_buf,
-                         size_t meta_bytes, void* ws, size_t ws_bytes, void* o_dense_out, mcs_meta* meta_out,
-                         void* stream) {
+namespace {
+
+// The selection step.  With `scratch` the workspace is the library's own
+// array (mcs_select_noalloc), looked up once every argument has been
+// validated; otherwise it is the caller's (ws, ws_bytes).
+mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, const void* v, int32_t G,
+                       const int32_t* keep, const float* proj, const mcs_select_options* opts, void* meta_buf,
+                       size_t meta_bytes, void* ws, size_t ws_bytes, void* o_dense_out, mcs_meta* meta_out,
+                       void* stream, bool scratch) {
   mcs_status st;
   if ((st = check_desc(d)) != MCS_SUCCESS) return st;
   if ((st = check_group_keep(d, G, keep)) != MCS_SUCCESS) return st;
@@ -297,12 +302,17 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
   for (const void* p : {q, k, v})
     if ((st = check_tensor(p)) != MCS_SUCCESS) return st;
   if (o_dense_out && !aligned(o_dense_out, 16)) return MCS_ERROR_MISALIGNED;
-  if (!proj || !meta_buf || !ws) return MCS_ERROR_INVALID_VALUE;
-  if (!aligned(meta_buf, kAlign) || !aligned(ws, kAlign)) return MCS_ERROR_MISALIGNED;
+  if (!proj || !meta_buf || (!ws && !scratch)) return MCS_ERROR_INVALID_VALUE;
+  if (!aligned(meta_buf, kAlign) || (!scratch && !aligned(ws, kAlign))) return MCS_ERROR_MISALIGNED;
   if (meta_bytes < m.bytes) return MCS_ERROR_BUFFER_TOO_SMALL;
   const WsLayout wl = ws_layout(d, G);
   const uint64_t per_head = wl.per_head_colsum + wl.per_head_block + wl.per_head_lse;
+  if (scratch) ws_bytes = MCS_NOALLOC_SCRATCH_BYTES;
   if (ws_bytes < wl.fixed + per_head) return MCS_ERROR_BUFFER_TOO_SMALL;
+  if (scratch) {
+    hipError_t e = mcs::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   const int H = d->num_heads, N = d->seq_len, D = d->head_dim;
   const int hc = (int)std::min<uint64_t>((uint64_t)H, (ws_bytes - wl.fixed) / per_head);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -380,6 +390,28 @@ mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, c
   }
   *meta_out = m;
   return MCS_SUCCESS;
+}
+
+}  // namespace
+
+mcs_status mcs_select_ex(const mcs_attn_desc* d, const void* q, const void* k, const void* v, int32_t G,
+                         const int32_t* keep, const float* proj, const mcs_select_options* opts, void* meta_buf,
+                         size_t meta_bytes, void* ws, size_t ws_bytes, void* o_dense_out, mcs_meta* meta_out,
+                         void* stream) {
+  return select_impl(d, q, k, v, G, keep, proj, opts, meta_buf, meta_bytes, ws, ws_bytes, o_dense_out, meta_out,
+                     stream, false);
+}
+
+mcs_status mcs_select_noalloc(const mcs_attn_desc* d, const void* q, const void* k, const void* v, int32_t G,
+                              const int32_t* keep, const float* proj, const mcs_select_options* opts,
+                              void* meta_buf, size_t meta_bytes, void* o_dense_out, mcs_meta* meta_out,
+                              void* stream) {
+  // Shapes whose fixed workspace and one head's scores exceed the array are
+  // refused first (a zero size is an invalid descriptor or group size, which
+  // the ordinary validation reports).
+  if (mcs_select_workspace_bytes(d, G, 1) > MCS_NOALLOC_SCRATCH_BYTES) return MCS_ERROR_BUFFER_TOO_SMALL;
+  return select_impl(d, q, k, v, G, keep, proj, opts, meta_buf, meta_bytes, nullptr, 0, o_dense_out, meta_out,
+                     stream, true);
 }
 
 mcs_status mcs_sparse_attn(const mcs_attn_desc* d, const void* q, const void* k, const void* v,

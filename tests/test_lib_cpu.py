@@ -268,3 +268,24 @@ def test_valid_call_without_a_device_reports_the_hip_error():
     assert r.returncode == 0, r.stderr[-2000:]
     st, err = (int(x) for x in r.stdout.split()[-2:])
     assert st == L.MCS_ERROR_HIP and err == 100
+
+
+def test_noalloc_refuses_shapes_beyond_its_array(lib):
+    """mcs_select_noalloc refuses a shape whose fixed workspace plus one
+    head's scores exceed MCS_NOALLOC_SCRATCH_BYTES before any other check or
+    device call (the long-video layer: 357 MB of scores per head), and takes
+    the ordinary validation path otherwise."""
+    keep, kp = _i32([3776] * 24)
+    proj = np.zeros((8, 128), np.float32)
+    pp = proj.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    m = L.Meta()
+    big = _desc(24, 75600, 128)
+    assert lib.mcs_select_workspace_bytes(ctypes.byref(big), 64, 1) > L.MCS_NOALLOC_SCRATCH_BYTES
+    assert lib.mcs_select_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, 64, kp, pp, None, FAKE, 1 << 40, NULL,
+                                  ctypes.byref(m), NULL) == L.MCS_ERROR_BUFFER_TOO_SMALL
+    small = _desc(2, 1000, 128)
+    keep2, kp2 = _i32([0, 64])
+    assert lib.mcs_select_noalloc(ctypes.byref(small), FAKE, FAKE, FAKE, 64, kp2, pp, None, FAKE, 1 << 30, NULL,
+                                  ctypes.byref(m), NULL) == L.MCS_ERROR_INVALID_VALUE
+    assert lib.mcs_select_noalloc(ctypes.byref(small), FAKE, FAKE, FAKE, 96, kp, pp, None, FAKE, 1 << 30, NULL,
+                                  ctypes.byref(m), NULL) == L.MCS_ERROR_UNSUPPORTED_SHAPE

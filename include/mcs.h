@@ -146,22 +146,32 @@ mcs_status mcs_dense_attn(const mcs_attn_desc* desc, const void* q, const void* 
                           void* o, void* stream);
 
 /*
- * Host-only: computes the metadata layout for group size G and per-head keep
- * budgets keep_host[H] (read during the call).  Fills *layout with base = NULL.
+ * Host-only: computes the metadata layout (the cached query groups, kept KV
+ * indices and residual that the abstract of "MC-Sparse: Deconstructing and
+ * Closing the Dense-Sparse Attention Gap in Diffusion Transformers" names)
+ * for group size G and per-head keep budgets keep_host[H] (read during the
+ * call).  Fills *layout with base = NULL.  Errors as for mcs_select's
+ * validation of the same arguments.
  */
 mcs_status mcs_meta_layout(const mcs_attn_desc* desc, int32_t group_size, const int32_t* keep_host,
                            mcs_meta* layout);
 
-/* Bytes of metadata buffer that mcs_select needs (0 if the arguments are invalid). */
+/* Bytes of metadata buffer that mcs_select needs for the cached groups, kept
+ * indices and residual of the abstract of "MC-Sparse: Deconstructing and
+ * Closing the Dense-Sparse Attention Gap in Diffusion Transformers" (0 if the
+ * arguments are invalid). */
 size_t mcs_meta_bytes(const mcs_attn_desc* desc, int32_t group_size, const int32_t* keep_host);
 
 /*
  * Bytes of workspace mcs_select needs to process `heads_per_chunk` heads at a
  * time (clamped to [1, H]; 0 if the arguments are invalid).  The bulk is the
- * per-group key scores, float32 [heads_per_chunk][ceil(N/G)][N rounded up to 64],
- * plus 64-key block scores (1/64 of that) for block-granular selection and
- * the rows' log-sum-exp (float32 [heads_per_chunk][N]) that the dense pass
- * hands to the key-score pass.
+ * per-group key scores of the selection (each group's exact probability mass
+ * per key: abstract of "MC-Sparse: Deconstructing and Closing the
+ * Dense-Sparse Attention Gap in Diffusion Transformers"), float32
+ * [heads_per_chunk][ceil(N/G)][N rounded up to 64], plus 64-key block scores
+ * (1/64 of that) for block-granular selection and the rows' log-sum-exp
+ * (float32 [heads_per_chunk][N]) that the dense pass hands to the key-score
+ * pass.
  */
 size_t mcs_select_workspace_bytes(const mcs_attn_desc* desc, int32_t group_size, int32_t heads_per_chunk);
 

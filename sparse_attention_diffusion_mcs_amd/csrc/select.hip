@@ -35,27 +35,58 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return
 // exactly.  Without it every product of a bf16/float32 value and a float32
 // projection is exact in float64 and one fused multiply-add per term gives
 // the same sum.
+//
+// A workgroup hashes HT consecutive tokens (rows of the flattened [H*N]
+// queries).  The rows are first copied to LDS with 16-byte loads that
+// consecutive threads issue for consecutive addresses, then each thread sums
+// its own row in dimension order, 8 dimensions per 16-byte LDS read.  The
+// LDS rows are padded by 16 bytes: the row stride in 4-byte banks is then
+// odd in units of four banks, so the 16-byte reads of 32 lanes of different
+// rows fall into distinct bank groups.  The projections are read with uniform
+// addresses (scalar loads).
+constexpr int HT = 128;
+
 template <typename T, int D, bool CENTRED>
-__global__ __launch_bounds__(256) void hash_keys_kernel(const T* __restrict__ q, const double* __restrict__ proj,
-                                                         const double* __restrict__ mean, uint8_t* __restrict__ keys,
-                                                         long long total, int N) {
-  __shared__ double r[8][D];
-  for (int e = threadIdx.x; e < 8 * D; e += 256) r[e / D][e % D] = proj[e];
+__global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, const double* __restrict__ proj,
+                                                        const double* __restrict__ mean, uint8_t* __restrict__ keys,
+                                                        long long total, int N) {
+  constexpr int ROWB = D * (int)sizeof(T);   // bytes per query row
+  constexpr int STRIDE = ROWB + 16;          // padded LDS row
+  constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
+  __shared__ __attribute__((aligned(16))) unsigned char rows[HT * STRIDE];
+  const long long t0 = (long long)blockIdx.x * HT;
+  const int nrows = (int)min((long long)HT, total - t0);
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(q + t0 * D);
+  for (int e = threadIdx.x; e < nrows * CPR; e += HT) {
+    const int r = e / CPR, c = e % CPR;
+    *reinterpret_cast<uint4*>(rows + r * STRIDE + 16 * c) = *reinterpret_cast<const uint4*>(src + 16 * e);
+  }
   __syncthreads();
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const T* row = q + i * D;
+  const int r = threadIdx.x;
+  if (r >= nrows) return;
+  const long long i = t0 + r;
   const double* mu = CENTRED ? mean + (i / N) * D : nullptr;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int c = 0; c < D; ++c) {
-    const double x = (double)load_elem<T>(row + c);
-    if constexpr (CENTRED) {
-      const double xc = x - mu[c];
+  for (int c = 0; c < CPR; ++c) {
+    const uint4 u = *reinterpret_cast<const uint4*>(rows + r * STRIDE + 16 * c);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int b = 0; b < 8; ++b) acc[b] = __dadd_rn(acc[b], __dmul_rn(xc, r[b][c]));
-    } else {
+    for (int e = 0; e < EPC; ++e) {
+      double x;
+      if constexpr (sizeof(T) == 2)
+        x = (double)bf16_to_f32((uint16_t)(w[e / 2] >> (16 * (e % 2))));
+      else
+        x = (double)__uint_as_float(w[e]);
+      const int dim = c * EPC + e;
+      if constexpr (CENTRED) {
+        const double xc = x - mu[dim];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) acc[b] = __fma_rn(x, r[b][c], acc[b]);
+        for (int b = 0; b < 8; ++b) acc[b] = __dadd_rn(acc[b], __dmul_rn(xc, proj[b * D + dim]));
+      } else {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[b] = __fma_rn(x, proj[b * D + dim], acc[b]);
+      }
     }
   }
   uint32_t key = 0;
@@ -416,12 +447,12 @@ namespace {
 template <typename T, int D>
 void hash_launch(const void* q, const double* proj, const double* mean, uint8_t* keys, long long total, int N,
                  hipStream_t s) {
-  const dim3 grid((unsigned)((total + 255) / 256));
+  const dim3 grid((unsigned)((total + HT - 1) / HT));
   if (mean)
-    hipLaunchKernelGGL((hash_keys_kernel<T, D, true>), grid, dim3(256), 0, s, static_cast<const T*>(q), proj, mean,
+    hipLaunchKernelGGL((hash_keys_kernel<T, D, true>), grid, dim3(HT), 0, s, static_cast<const T*>(q), proj, mean,
                        keys, total, N);
   else
-    hipLaunchKernelGGL((hash_keys_kernel<T, D, false>), grid, dim3(256), 0, s, static_cast<const T*>(q), proj,
+    hipLaunchKernelGGL((hash_keys_kernel<T, D, false>), grid, dim3(HT), 0, s, static_cast<const T*>(q), proj,
                        mean, keys, total, N);
 }
 }  // namespace

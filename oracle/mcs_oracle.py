@@ -50,6 +50,13 @@ Morton (Z-curve) order, so that a group of G = 64 tokens is a 4 x 4 x 4
 block of the grid: spatially compact queries, the similar queries of a
 position-driven DiT.
 
+Two extensions beyond the pages: a per-group keep budget from a retained
+probability-mass target (the fewest keys whose group scores reach a fraction
+of the group's mass, capped by the head's budget -- per-head budgets
+generalised, as the benchmark's 3D-asset workload draws them per head), and
+a residual cached in bfloat16 instead of float32 (half the cache, the
+"metadata cache per step" the pages count as MC-Sparse's extra cost).
+
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
 
@@ -206,6 +213,52 @@ def topk_select(c: np.ndarray, k: int):
     return idx, gap
 
 
+MASS_FRAC_BITS = 48
+
+
+def mass_keep_count(c: np.ndarray, mass: float, group_len: int, cap: int) -> int:
+    """Per-group budget from a retained-mass target (an extension of the
+    per-head budgets of the benchmark's 3D-asset workload; the pages fix
+    none): the fewest keys, taken in the top-k order of the group's scores,
+    whose scores add up to at least `mass` of the group's total probability
+    mass |g| (the scores of a group sum to its number of queries), at most
+    `cap` and at least 1.  When even all keys fall short, all are needed (then
+    the cap).
+
+    The sum is decided exactly: every float32 score is a fixed-point integer
+    of 2^-48 units (floor), the target is ceil(mass * |g| * 2^48), and the
+    prefix sums in the top-k order (score descending, index ascending) are
+    integers, so the count does not depend on a summation order."""
+    c32 = np.asarray(c, dtype=np.float64).astype(np.float32).astype(np.float64)
+    n = c32.shape[0]
+    if not 1 <= cap <= n:
+        raise ValueError(f"cap {cap} outside [1, {n}]")
+    q = np.floor(np.ldexp(c32, MASS_FRAC_BITS)).astype(np.int64)
+    target = math.ceil(float(np.float32(mass)) * group_len * 2.0 ** MASS_FRAC_BITS)
+    order = np.lexsort((np.arange(n), -c32))
+    prefix = np.cumsum(q[order])
+    hit = np.nonzero(prefix >= target)[0]
+    m = int(hit[0]) + 1 if hit.size else n
+    return max(1, min(m, cap))
+
+
+def topk_mass_select(c: np.ndarray, mass: float, group_len: int, cap: int):
+    """The kept keys under a retained-mass target: the top mass_keep_count
+    keys (ascending), with the float32-score gap after the last one."""
+    n = mass_keep_count(c, mass, group_len, cap)
+    idx, gap = topk_select(c, n)
+    return idx, gap, n
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """x rounded to float32, then to bfloat16 (round to nearest, ties to
+    even), returned as float64: the storage of a bf16 cached residual."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def block_scores(c: np.ndarray, block: int) -> np.ndarray:
     """Score of each run of `block` consecutive keys: the sum of the group's
     key scores over the run (float64 [N / block])."""
@@ -246,24 +299,31 @@ class GroupSelection:
     residual: np.ndarray    # o_dense - o_sparse, float64 [|g|, d]
 
 
-def select_group(q, k, v, rows, keep, scale, kv_block=1, residual=True) -> GroupSelection:
+def select_group(q, k, v, rows, keep, scale, kv_block=1, residual=True, keep_mass=0.0,
+                 residual_bf16=False) -> GroupSelection:
     """Selection step for one query group ([ABS], [BLOG] "MC-Sparse: three
     failure modes, one fix"): exact dense rows, group scores, top-k, sparse
     rows over the kept keys and the residual between the two.
 
     Ablations: kv_block > 1 keeps whole key blocks (topk_blocks); residual
     False caches a zero residual, so reuse returns the renormalised sparse
-    output alone."""
+    output alone.  Extensions: keep_mass > 0 keeps the fewest keys reaching
+    that retained mass, at most `keep` (topk_mass_select); residual_bf16
+    caches the residual rounded to bfloat16 (round_bf16)."""
     rows = np.asarray(rows, dtype=np.int64)
     qg = np.asarray(q)[rows]
     o_d, p = attention(qg, k, v, scale)
     c = group_scores(p)
-    if kv_block == 1:
+    if kv_block == 1 and keep_mass > 0:
+        idx, gap, _ = topk_mass_select(c, keep_mass, len(rows), keep)
+    elif kv_block == 1:
         idx, gap = topk_select(c, keep)
     else:
         idx, gap, _ = topk_blocks(c, keep, kv_block)
     o_s = sparse_attention(qg, k, v, idx, scale)
     res = o_d - o_s if residual else np.zeros_like(o_d)
+    if residual_bf16:
+        res = round_bf16(res)
     return GroupSelection(rows.astype(np.int32), c, idx, gap, o_d, o_s, res)
 
 
@@ -288,7 +348,7 @@ class HeadMeta:
 
 
 def select_head(q, k, v, proj, group, keep, scale, groups=None, grouping="hash", kv_block=1,
-                residual=True, grid=None) -> HeadMeta:
+                residual=True, grid=None, keep_mass=0.0, residual_bf16=False) -> HeadMeta:
     """Selection for one head; `groups` restricts the work to a subset of
     group ids (the permutation always covers the whole head).  `grouping`
     "raster" replaces the hash groups by raster-order runs (keys are then 0);
@@ -313,7 +373,8 @@ def select_head(q, k, v, proj, group, keep, scale, groups=None, grouping="hash",
         raise ValueError(f"unknown grouping {grouping!r}")
     ranges = group_ranges(n, group)
     gids = range(len(ranges)) if groups is None else groups
-    sel = {g: select_group(q, k, v, perm[ranges[g][0]:ranges[g][1]], keep, scale, kv_block, residual)
+    sel = {g: select_group(q, k, v, perm[ranges[g][0]:ranges[g][1]], keep, scale, kv_block, residual,
+                           keep_mass=keep_mass, residual_bf16=residual_bf16)
            for g in gids}
     return HeadMeta(perm, keys, sel)
 

@@ -18,7 +18,10 @@ What the checks compare against:
   one query is per-query top-k attention;
 * for the failure-mode ablations: brute force over every choice of whole key
   blocks (block selection), the identity order together with a hash whose
-  keys all agree (raster groups), and library masked attention (no residual).
+  keys all agree (raster groups), and library masked attention (no residual);
+* for the retained-mass budgets: exact rational brute force over every key
+  subset of tiny rows, closed forms, and the retained mass computed from
+  library softmax; for the bf16 residual: torch's bfloat16 conversion.
 """
 
 from __future__ import annotations
@@ -398,6 +401,112 @@ def check_no_residual(impl, seed=15):
     assert np.max(np.abs(re - _sdpa(q[rows], kk, v, 0.35))) > 1e-6
 
 
+# ------------------------------------------------- retained-mass budgets
+
+def check_mass_count_exact_rational(impl, seed=17):
+    """The per-group budget for a retained-mass target is the size of the
+    smallest key subset whose exact (rational) score sum reaches
+    mass * |g|: brute force over every subset of tiny rows, with scores
+    from library softmax; cases whose best subset sums lie within 2^-30 of
+    the target are skipped, so the fixed-point decision cannot differ from
+    the exact one."""
+    r = np.random.default_rng(seed)
+    tried = 0
+    for trial in range(40):
+        n = int(r.integers(3, 10))
+        g = int(r.integers(1, 4))
+        d = 4
+        q = r.standard_normal((g, d)) * 1.5
+        kk = r.standard_normal((n, d)) * 1.5
+        p = _lib_probs(q, kk, 0.8)
+        c = p.sum(axis=0).astype(np.float32)
+        for mass in (0.3, 0.5, 0.8, 0.95, 1.0):
+            target = Fraction(float(np.float32(mass))) * g
+            best = {}
+            for m in range(1, n + 1):
+                best[m] = max(sum(Fraction(float(c[j])) for j in sub) for sub in itertools.combinations(range(n), m))
+            if any(abs(best[m] - target) < Fraction(1, 2 ** 30) for m in best):
+                continue
+            reach = [m for m in range(1, n + 1) if best[m] >= target]
+            m = reach[0] if reach else n
+            for cap in (1, max(1, n // 2), n):
+                want = max(1, min(m, cap))
+                got = impl.mass_keep_count(c, mass, g, cap)
+                assert got == want, (trial, mass, cap, got, want, c.tolist())
+                tried += 1
+    assert tried > 100
+
+
+def check_mass_closed_forms(impl):
+    """Equal scores need ceil(mass * N) keys; one key that holds the target
+    alone is enough; the cap bounds the count; the kept keys are the top
+    ones under the top-k's order."""
+    c = np.full(16, 4.0)                      # 16 keys, a group of 64 queries
+    assert impl.mass_keep_count(c, 0.5, 64, 16) == 8
+    assert impl.mass_keep_count(c, 0.51, 64, 16) == 9
+    assert impl.mass_keep_count(c, 1.0, 64, 16) == 16
+    assert impl.mass_keep_count(c, 1.0, 64, 5) == 5
+    assert impl.mass_keep_count(c, 1e-9, 64, 16) == 1
+    dom = np.array([1.0, 60.0, 2.0, 1.0])
+    assert impl.mass_keep_count(dom, 0.9, 64, 4) == 1
+    assert impl.mass_keep_count(dom, 0.96, 64, 4) == 2
+    idx, _, n = impl.topk_mass_select(np.array([3.0, 1.0, 3.0, 8.0, 1.0, 0.0]), 0.7, 16, 6)
+    assert n == 3 and idx.tolist() == [0, 2, 3]   # 8 + 3 + 3 = 14 >= 11.2; ties at 3 both needed
+
+
+def check_mass_selection(impl, seed=18):
+    """A mass-targeted selection keeps a set whose retained probability mass
+    (library softmax over the group's rows) reaches the target, and dropping
+    its weakest key falls short of it (unless the cap stopped it)."""
+    r = np.random.default_rng(seed)
+    n, d = 60, 8
+    q, kk, v = r.standard_normal((n, d)) * 2, r.standard_normal((n, d)) * 2, r.standard_normal((n, d))
+    rows = list(range(0, 60, 5))
+    for mass, cap in ((0.6, 60), (0.9, 60), (0.99, 60), (0.9, 4)):
+        sel = impl.select_group(q, kk, v, rows, cap, 0.4, keep_mass=mass)
+        p = _lib_probs(q[rows], kk, 0.4)
+        kept = p[:, sel.idx].sum()
+        target = mass * len(rows)
+        if len(sel.idx) < cap:
+            assert kept >= target - 1e-9, (mass, kept, target)
+            weakest = sel.idx[np.argmin(p[:, sel.idx].sum(axis=0))]
+            assert kept - p[:, weakest].sum() < target + 1e-9
+        else:
+            assert len(sel.idx) == cap
+
+
+# ------------------------------------------------------- bf16 residual
+
+def check_bf16_rounding(impl, seed=19):
+    """bf16 storage of the residual rounds like torch's float32 -> bfloat16
+    conversion (round to nearest, ties to even), halfway cases included."""
+    r = np.random.default_rng(seed)
+    x = np.concatenate([r.standard_normal(2000) * 10.0 ** r.integers(-6, 3, 2000),
+                        [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0, 3.0]])
+    want = torch.tensor(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    got = impl.round_bf16(x)
+    assert np.array_equal(got, want)
+    assert got[-5] == 1.0 and got[-4] == 1.0 + 2 ** -6
+
+
+def check_bf16_residual(impl, seed=20):
+    """A bf16 residual is the float32 residual rounded to bf16, and reuse on
+    the selection inputs then reproduces dense attention to within half a
+    bf16 unit of the residual."""
+    r = np.random.default_rng(seed)
+    n, d = 48, 8
+    q, kk, v = r.standard_normal((n, d)) * 2, r.standard_normal((n, d)) * 2, r.standard_normal((n, d))
+    rows = list(range(3, 48, 3))
+    a = impl.select_group(q, kk, v, rows, 9, 0.35)
+    b = impl.select_group(q, kk, v, rows, 9, 0.35, residual_bf16=True)
+    assert np.array_equal(a.idx, b.idx)
+    tb = torch.tensor(a.residual.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(b.residual, tb)
+    re = impl.reuse_group(q, kk, v, rows, b.idx, b.residual, 0.35)
+    dense = _sdpa(q[rows], kk, v, 0.35)
+    assert np.max(np.abs(re - dense)) <= np.max(np.abs(a.residual)) * 2 ** -8 + 1e-12
+
+
 ALL_CHECKS = [
     check_hash_golden, check_hash_exact_rational, check_perm_stable_sort,
     check_dense_vs_sdpa, check_two_token_golden, check_closed_forms,
@@ -405,5 +514,6 @@ ALL_CHECKS = [
     check_topk_ties_lower_index, check_single_query_topk,
     check_sparse_vs_masked_sdpa, check_keep_one_and_all, check_reuse_identity,
     check_block_topk_bruteforce, check_raster_groups, check_no_residual, check_centred_hash,
-    check_morton_groups,
+    check_morton_groups, check_mass_count_exact_rational, check_mass_closed_forms, check_mass_selection,
+    check_bf16_rounding, check_bf16_residual,
 ]

@@ -59,14 +59,14 @@ def _sparse_unnormalised(q, k, v, idx, scale):
     return p[:, idx] @ np.asarray(v, np.float64)[idx]
 
 
-def _select_residual_flipped(q, k, v, rows, keep, scale, kv_block=1, residual=True):
-    s = orig_select(q, k, v, rows, keep, scale, kv_block, residual)
+def _select_residual_flipped(q, k, v, rows, keep, scale, kv_block=1, residual=True, **kw):
+    s = orig_select(q, k, v, rows, keep, scale, kv_block, residual, **kw)
     s.residual = -s.residual
     return s
 
 
-def _select_ignores_no_residual(q, k, v, rows, keep, scale, kv_block=1, residual=True):
-    return orig_select(q, k, v, rows, keep, scale, kv_block, True)
+def _select_ignores_no_residual(q, k, v, rows, keep, scale, kv_block=1, residual=True, **kw):
+    return orig_select(q, k, v, rows, keep, scale, kv_block, True, **kw)
 
 
 def _block_scores_max(c, block):
@@ -108,7 +108,33 @@ def _reuse_no_residual(q_t, k_t, v_t, rows, idx, residual, scale):
     return orc.sparse_attention(qg, k_t, v_t, idx, scale)
 
 
+def _mass_no_cap(c, mass, group_len, cap):
+    return orig_mass_count(c, mass, group_len, len(c))
+
+
+def _mass_from_smallest(c, mass, group_len, cap):
+    c32 = np.asarray(c, np.float64).astype(np.float32).astype(np.float64)
+    target = mass * group_len
+    prefix = np.cumsum(np.sort(c32))
+    hit = np.nonzero(prefix >= target)[0]
+    return max(1, min(int(hit[0]) + 1 if hit.size else len(c), cap))
+
+
+def _mass_one_more(c, mass, group_len, cap):
+    return min(orig_mass_count(c, mass, group_len, cap) + 1, cap)
+
+
+def _mass_over_n(c, mass, group_len, cap):
+    return orig_mass_count(c, mass * len(c) / group_len, group_len, cap)
+
+
+def _bf16_truncate(x):
+    f = np.ascontiguousarray(np.asarray(x, np.float64).astype(np.float32))
+    return (f.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+
+
 orig_select = orc.select_group
+orig_mass_count = orc.mass_keep_count
 orig_morton_code = orc.morton_code
 
 MUTANTS = {
@@ -131,6 +157,11 @@ MUTANTS = {
     "mean over half the queries": ("query_mean", _mean_first_half),
     "morton x and y swapped": ("morton_permutation", _morton_xy_swapped),
     "morton t in the low bit": ("morton_code", _morton_code_t_low),
+    "mass budget ignores the cap": ("mass_keep_count", _mass_no_cap),
+    "mass counted from the smallest scores": ("mass_keep_count", _mass_from_smallest),
+    "mass budget one key too many": ("mass_keep_count", _mass_one_more),
+    "mass target relative to N": ("mass_keep_count", _mass_over_n),
+    "bf16 residual truncated": ("round_bf16", _bf16_truncate),
 }
 
 

@@ -60,7 +60,7 @@ extern "C" {
 #endif
 
 #define MCS_VERSION 2
-#define MCS_META_VERSION 1
+#define MCS_META_VERSION 2
 #define MCS_HASH_BITS 8
 #define MCS_MAX_SEQ_LEN (1 << 22)
 
@@ -96,14 +96,19 @@ typedef struct mcs_attn_desc {
  *
  *   perm      int32 [H][N]     perm[h][p] = original token at sorted position p;
  *                              group g of head h is positions [g*G, min(N,(g+1)*G))
- *   keep      int32 [H]        k_h, kept keys per group of head h, 1 <= k_h <= N
+ *   keep      int32 [H]        k_h, the kept-key budget (index slots) per group of
+ *                              head h, 1 <= k_h <= N
  *   idx_start int64 [H]        element offset of head h's indices in `idx`
  *   sched     int32 [H]        heads by decreasing k_h (ties: lower head first);
  *                              reuse launches the costliest heads first
- *   idx       int32 [total_idx] head h, group g: k_h kept key indices, ascending,
- *                              at idx[idx_start[h] + g*k_h ...]
- *   residual  float32 [H][N][d] O_dense - O_sparse of the selection step, row p
- *                              = sorted position p (not the original token)
+ *   count     int32 [H][ng]    keys kept by group g of head h, 1 <= count <= k_h
+ *                              (k_h unless a retained-mass target chose fewer)
+ *   idx       int32 [total_idx] head h, group g: the slot of k_h indices at
+ *                              idx[idx_start[h] + g*k_h ...]; its first count[h][g]
+ *                              entries are the kept keys, ascending
+ *   residual  [H][N][d]        O_dense - O_sparse of the selection step, row p
+ *                              = sorted position p (not the original token), in
+ *                              float32 or (residual_dtype MCS_DTYPE_BF16) bfloat16
  */
 typedef struct mcs_meta {
   int32_t version;         /* MCS_META_VERSION */
@@ -114,6 +119,8 @@ typedef struct mcs_meta {
   int32_t group_size;      /* G */
   int32_t num_groups;      /* ceil(N / G) */
   int32_t max_keep;        /* max_h k_h */
+  int32_t residual_dtype;  /* mcs_dtype of the residual region */
+  int32_t reserved;        /* 0 */
   int64_t total_idx;       /* sum_h num_groups * k_h */
   void* base;              /* device pointer to the metadata buffer (NULL from mcs_meta_layout) */
   uint64_t bytes;          /* bytes the layout occupies from base */
@@ -121,6 +128,7 @@ typedef struct mcs_meta {
   uint64_t off_keep;
   uint64_t off_idx_start;
   uint64_t off_sched;
+  uint64_t off_count;
   uint64_t off_idx;
   uint64_t off_residual;
 } mcs_meta;
@@ -163,6 +171,17 @@ mcs_status mcs_meta_layout(const mcs_attn_desc* desc, int32_t group_size, const 
 size_t mcs_meta_bytes(const mcs_attn_desc* desc, int32_t group_size, const int32_t* keep_host);
 
 /*
+ * mcs_meta_layout for a residual kept in residual_dtype (MCS_DTYPE_FP32, or
+ * MCS_DTYPE_BF16 for bf16 problems: half the residual region, the largest
+ * part of the metadata cache that the pages count as the method's extra cost,
+ * section "MC-Sparse: three failure modes, one fix" of "The quality cliff
+ * nobody admits to").  Other residual_dtype values, or BF16 for a float32
+ * problem, give MCS_ERROR_INVALID_VALUE.
+ */
+mcs_status mcs_meta_layout_ex(const mcs_attn_desc* desc, int32_t group_size, const int32_t* keep_host,
+                              int32_t residual_dtype, mcs_meta* layout);
+
+/*
  * Bytes of workspace mcs_select needs to process `heads_per_chunk` heads at a
  * time (clamped to [1, H]; 0 if the arguments are invalid).  The bulk is the
  * per-group key scores of the selection (each group's exact probability mass
@@ -175,6 +194,15 @@ size_t mcs_meta_bytes(const mcs_attn_desc* desc, int32_t group_size, const int32
  */
 size_t mcs_select_workspace_bytes(const mcs_attn_desc* desc, int32_t group_size, int32_t heads_per_chunk);
 
+struct mcs_select_options; /* defined below */
+
+/* mcs_select_workspace_bytes for a selection with `options` (NULL = the
+ * defaults): a bf16 residual adds each head's float32 dense output (float32
+ * [heads_per_chunk][N][d]), from which the residual is formed before it is
+ * rounded.  0 if the arguments or options are invalid. */
+size_t mcs_select_workspace_bytes_ex(const mcs_attn_desc* desc, int32_t group_size, int32_t heads_per_chunk,
+                                     const struct mcs_select_options* options);
+
 /*
  * Lays out metadata in meta_buf (device, 256-byte aligned, meta_bytes long)
  * and writes its keep, idx_start and sched regions; perm, idx and residual
@@ -183,6 +211,12 @@ size_t mcs_select_workspace_bytes(const mcs_attn_desc* desc, int32_t group_size,
  */
 mcs_status mcs_meta_init(const mcs_attn_desc* desc, int32_t group_size, const int32_t* keep_host,
                          void* meta_buf, size_t meta_bytes, mcs_meta* meta_out, void* stream);
+
+/* mcs_meta_init for a residual kept in residual_dtype (as mcs_meta_layout_ex).
+ * Both write the count region with k_h for every group. */
+mcs_status mcs_meta_init_ex(const mcs_attn_desc* desc, int32_t group_size, const int32_t* keep_host,
+                            int32_t residual_dtype, void* meta_buf, size_t meta_bytes, mcs_meta* meta_out,
+                            void* stream);
 
 /*
  * Selection step (abstract of "MC-Sparse: Deconstructing and Closing the
@@ -239,6 +273,19 @@ typedef struct mcs_select_options {
                         sparse output renormalised over the kept keys alone */
   int32_t grid_t, grid_y, grid_x;  /* MCS_GROUPING_MORTON: the latent grid, each in [1, 1024], product N;
                                       0 for every other grouping */
+  /* Extensions of the method (zero selects the method as read):
+     residual_dtype  MCS_DTYPE_FP32 or, for bf16 problems, MCS_DTYPE_BF16: the cached residual
+                     O_dense - O_sparse rounded to bfloat16 (computed in float32), half the cache;
+                     the metadata buffer is then laid out by mcs_meta_layout_ex with that dtype,
+                     and the workspace by mcs_select_workspace_bytes_ex with these options;
+     keep_mass       0, or a retained-mass target in (0, 1]: each group keeps the fewest keys, in
+                     the top-k order of its scores, whose scores sum to at least keep_mass * |g|
+                     (its queries' probability mass: every query's probabilities sum to 1), at
+                     most k_h and at least 1; the sum is decided on the float32 scores as
+                     fixed-point integers of 2^-48 (floor) against ceil(keep_mass * |g| * 2^48).
+                     Needs kv_block 1. */
+  int32_t residual_dtype;
+  float keep_mass;
   /* Tracing (no effect on the results): NULL, or an array of num_phase_events (0 to
      MCS_SELECT_PHASES) hipEvent_t handles created by the caller on the device of the call.  Event i
      is recorded on the stream when phase i of the selection has been launched: 0 grouping (hash and

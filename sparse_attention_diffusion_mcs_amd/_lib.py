@@ -18,7 +18,7 @@ MCS_ERROR_HIP = 6
 
 MCS_DTYPE_FP32 = 0
 MCS_DTYPE_BF16 = 1
-MCS_META_VERSION = 1
+MCS_META_VERSION = 2
 MCS_HASH_BITS = 8
 MCS_VERSION = 2
 MCS_SELECT_PHASES = 5
@@ -32,7 +32,8 @@ MCS_GROUPING_MORTON = 3
 
 EXPORTS = ("mcs_version", "mcs_status_string", "mcs_last_hip_error", "mcs_dense_attn", "mcs_meta_layout",
            "mcs_meta_bytes", "mcs_select_workspace_bytes", "mcs_meta_init", "mcs_select", "mcs_select_ex",
-           "mcs_sparse_attn", "mcs_select_noalloc")
+           "mcs_sparse_attn", "mcs_select_noalloc", "mcs_meta_layout_ex", "mcs_meta_init_ex",
+           "mcs_select_workspace_bytes_ex")
 
 
 class AttnDesc(ctypes.Structure):
@@ -43,15 +44,17 @@ class AttnDesc(ctypes.Structure):
 class Meta(ctypes.Structure):
     _fields_ = [("version", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("group_size", ctypes.c_int32),
-                ("num_groups", ctypes.c_int32), ("max_keep", ctypes.c_int32), ("total_idx", ctypes.c_int64),
+                ("num_groups", ctypes.c_int32), ("max_keep", ctypes.c_int32), ("residual_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("total_idx", ctypes.c_int64),
                 ("base", ctypes.c_void_p), ("bytes", ctypes.c_uint64), ("off_perm", ctypes.c_uint64),
                 ("off_keep", ctypes.c_uint64), ("off_idx_start", ctypes.c_uint64), ("off_sched", ctypes.c_uint64),
-                ("off_idx", ctypes.c_uint64), ("off_residual", ctypes.c_uint64)]
+                ("off_count", ctypes.c_uint64), ("off_idx", ctypes.c_uint64), ("off_residual", ctypes.c_uint64)]
 
 
 class SelectOptions(ctypes.Structure):
     _fields_ = [("grouping", ctypes.c_int32), ("kv_block", ctypes.c_int32), ("residual", ctypes.c_int32),
                 ("grid_t", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_x", ctypes.c_int32),
+                ("residual_dtype", ctypes.c_int32), ("keep_mass", ctypes.c_float),
                 ("phase_events", ctypes.POINTER(ctypes.c_void_p)), ("num_phase_events", ctypes.c_int32)]
 
 
@@ -108,6 +111,12 @@ def open_library(path):
     lib.mcs_select_ex.restype = ctypes.c_int
     lib.mcs_select_ex.argtypes = [DP, P, P, P, ctypes.c_int32, I32P, F32P, ctypes.POINTER(SelectOptions), P,
                                   ctypes.c_size_t, P, ctypes.c_size_t, P, MP, P]
+    lib.mcs_meta_layout_ex.restype = ctypes.c_int
+    lib.mcs_meta_layout_ex.argtypes = [DP, ctypes.c_int32, I32P, ctypes.c_int32, MP]
+    lib.mcs_meta_init_ex.restype = ctypes.c_int
+    lib.mcs_meta_init_ex.argtypes = [DP, ctypes.c_int32, I32P, ctypes.c_int32, P, ctypes.c_size_t, MP, P]
+    lib.mcs_select_workspace_bytes_ex.restype = ctypes.c_size_t
+    lib.mcs_select_workspace_bytes_ex.argtypes = [DP, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(SelectOptions)]
     lib.mcs_select_noalloc.restype = ctypes.c_int
     lib.mcs_select_noalloc.argtypes = [DP, P, P, P, ctypes.c_int32, I32P, F32P, ctypes.POINTER(SelectOptions), P,
                                        ctypes.c_size_t, P, MP, P]

@@ -86,8 +86,10 @@ class MetaCache:
     """Cached selection metadata: a device buffer plus its mcs_meta descriptor.
 
     Region views (all on the device): perm int32 [H, N], keep int32 [H],
-    idx_start int64 [H], sched int32 [H], idx int32 [total_idx] and residual
-    float32 [H, N, d] (rows in group order)."""
+    idx_start int64 [H], sched int32 [H], count int32 [H, num_groups] (keys
+    kept per group), idx int32 [total_idx] (per group a slot of keep[h]
+    indices, the first count[h, g] valid) and residual [H, N, d] (float32 or
+    bfloat16, rows in group order)."""
 
     def __init__(self, meta: L.Meta, buffer: torch.Tensor):
         self.meta = meta
@@ -134,6 +136,11 @@ class MetaCache:
         return self._region(m.off_sched, m.num_heads, torch.int32, (m.num_heads,))
 
     @property
+    def count(self):
+        m = self.meta
+        return self._region(m.off_count, m.num_heads * m.num_groups, torch.int32, (m.num_heads, m.num_groups))
+
+    @property
     def idx(self):
         m = self.meta
         return self._region(m.off_idx, m.total_idx, torch.int32, (m.total_idx,))
@@ -141,11 +148,13 @@ class MetaCache:
     @property
     def residual(self):
         m = self.meta
-        return self._region(m.off_residual, m.num_heads * m.seq_len * m.head_dim, torch.float32,
+        dt = torch.bfloat16 if m.residual_dtype == L.MCS_DTYPE_BF16 else torch.float32
+        return self._region(m.off_residual, m.num_heads * m.seq_len * m.head_dim, dt,
                             (m.num_heads, m.seq_len, m.head_dim))
 
     def head_idx(self, h: int, keep_h: int) -> torch.Tensor:
-        """Kept key indices of head h as [num_groups, keep_h]."""
+        """Index slots of head h as [num_groups, keep_h] (group g's first
+        count[h, g] entries are its kept keys)."""
         start = int(self.idx_start[h].item())
         return self.idx[start:start + self.num_groups * keep_h].view(self.num_groups, keep_h)
 
@@ -168,45 +177,55 @@ def dense_attn(q, k, v, out=None, scale=None, stream=None):
     return out
 
 
-def meta_layout(H, N, d, dtype_code, group_size, keep) -> L.Meta:
+_RESIDUAL_DTYPES = {"fp32": L.MCS_DTYPE_FP32, "bf16": L.MCS_DTYPE_BF16}
+
+
+def _residual_code(residual_dtype) -> int:
+    if residual_dtype not in _RESIDUAL_DTYPES:
+        raise ValueError(f"residual_dtype must be one of {sorted(_RESIDUAL_DTYPES)}")
+    return _RESIDUAL_DTYPES[residual_dtype]
+
+
+def meta_layout(H, N, d, dtype_code, group_size, keep, residual_dtype="fp32") -> L.Meta:
     desc = L.AttnDesc(H, N, d, dtype_code, 0.0)
     ka = _keep_array(keep, H)
     m = L.Meta()
-    L.check(L.lib().mcs_meta_layout(ctypes.byref(desc), group_size, _i32p(ka), ctypes.byref(m)), "mcs_meta_layout")
+    L.check(L.lib().mcs_meta_layout_ex(ctypes.byref(desc), group_size, _i32p(ka), _residual_code(residual_dtype),
+                                       ctypes.byref(m)), "mcs_meta_layout_ex")
     return m
 
 
-def workspace_bytes(q, group_size, heads_per_chunk=None) -> int:
+def workspace_bytes(q, group_size, heads_per_chunk=None, residual_dtype="fp32") -> int:
     desc = desc_for(q)
     hc = q.shape[0] if heads_per_chunk is None else heads_per_chunk
-    return int(L.lib().mcs_select_workspace_bytes(ctypes.byref(desc), group_size, hc))
+    opts = L.SelectOptions(L.MCS_GROUPING_HASH, 1, 1, 0, 0, 0, _residual_code(residual_dtype), 0.0, None, 0)
+    return int(L.lib().mcs_select_workspace_bytes_ex(ctypes.byref(desc), group_size, hc, ctypes.byref(opts)))
 
 
-def meta_init(q, group_size, keep, meta_buf=None, stream=None) -> MetaCache:
-    """Lays out an empty metadata buffer (keep/idx_start/sched written;
-    perm/idx/residual to be filled by the caller) (mcs_meta_init)."""
-    desc = desc_for(q)
-    H = q.shape[0]
-    ka = _keep_array(keep, H)
-    nbytes = int(L.lib().mcs_meta_bytes(ctypes.byref(desc), group_size, _i32p(ka)))
-    if nbytes == 0:
-        raise L.McsError(L.MCS_ERROR_INVALID_VALUE, "mcs_meta_bytes")
+def meta_init(q, group_size, keep, meta_buf=None, stream=None, residual_dtype="fp32") -> MetaCache:
+    """Lays out an empty metadata buffer (keep/idx_start/sched written, every
+    group's count set to keep[h]; perm/idx/residual to be filled by the
+    caller) (mcs_meta_init_ex)."""
     if not isinstance(q, torch.Tensor) or not q.is_cuda:
         raise ValueError("q must be a device tensor")
+    desc = desc_for(q)
+    H, N, d = q.shape
+    ka = _keep_array(keep, H)
+    layout = meta_layout(H, N, d, _dtype_code(q), group_size, keep, residual_dtype)
     if meta_buf is None:
-        meta_buf = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        meta_buf = torch.empty(max(int(layout.bytes), 256), dtype=torch.uint8, device=q.device)
     _check_bytes(meta_buf, "meta_buf", q.device)
     m = L.Meta()
     st = _stream(stream, q.device)
     with torch.cuda.device(q.device):
-        L.check(L.lib().mcs_meta_init(ctypes.byref(desc), group_size, _i32p(ka), _ptr(meta_buf), meta_buf.numel(),
-                                      ctypes.byref(m), st), "mcs_meta_init")
+        L.check(L.lib().mcs_meta_init_ex(ctypes.byref(desc), group_size, _i32p(ka), _residual_code(residual_dtype),
+                                         _ptr(meta_buf), meta_buf.numel(), ctypes.byref(m), st), "mcs_meta_init_ex")
     return MetaCache(m, meta_buf)
 
 
 def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace=None, heads_per_chunk=None,
            return_dense=False, stream=None, grouping="hash", kv_block=1, residual=True, grid=None, dense_out=None,
-           phase_events=None, noalloc=False):
+           phase_events=None, noalloc=False, residual_dtype="fp32", keep_mass=0.0):
     """Selection step (mcs_select; mcs_select_ex for the other groupings --
     "raster", "centred", "morton" with the (T, Y, X) `grid` -- the
     failure-mode ablations kv_block 64, residual False, and tracing).  The
@@ -216,7 +235,10 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
     as the grouping, dense pass, key scores, top-k and residual pass are
     launched.  With noalloc the call is mcs_select_noalloc: the workspace is
     the library's own per-device array (no `workspace` may be given).
-    Returns (MetaCache, dense output or None)."""
+    Extensions: residual_dtype "bf16" caches the residual in bfloat16;
+    keep_mass in (0, 1] keeps, per group, the fewest keys reaching that
+    retained probability mass, at most `keep` (their number is in the
+    metadata's count region).  Returns (MetaCache, dense output or None)."""
     _check_qkv(q, k, v)
     H, N, d = q.shape
     desc = desc_for(q, scale)
@@ -224,9 +246,12 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
     pj = np.ascontiguousarray(np.asarray(proj, dtype=np.float32))
     if pj.shape != (L.MCS_HASH_BITS, d):
         raise ValueError(f"proj must be [{L.MCS_HASH_BITS}, {d}]")
-    nbytes = int(L.lib().mcs_meta_bytes(ctypes.byref(desc), group_size, _i32p(ka)))
-    if nbytes == 0 and H * N > 0:
-        raise L.McsError(L.MCS_ERROR_INVALID_VALUE, "mcs_meta_bytes")
+    rcode = _residual_code(residual_dtype)
+    ml = L.Meta()
+    st_l = L.lib().mcs_meta_layout_ex(ctypes.byref(desc), group_size, _i32p(ka), rcode, ctypes.byref(ml))
+    if st_l != L.MCS_SUCCESS:
+        raise L.McsError(st_l, "mcs_meta_layout_ex")
+    nbytes = int(ml.bytes)
     if meta_buf is None:
         meta_buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     _check_bytes(meta_buf, "meta_buf", q.device)
@@ -235,8 +260,8 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
             raise ValueError("noalloc uses the library's own workspace")
     else:
         if workspace is None:
-            workspace = torch.empty(max(workspace_bytes(q, group_size, heads_per_chunk), 256), dtype=torch.uint8,
-                                    device=q.device)
+            workspace = torch.empty(max(workspace_bytes(q, group_size, heads_per_chunk, residual_dtype), 256),
+                                    dtype=torch.uint8, device=q.device)
         _check_bytes(workspace, "workspace", q.device)
     if dense_out is not None:
         _check_out(dense_out, q)
@@ -256,7 +281,8 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
                 ev.record(torch.cuda.current_stream(q.device))
             handles.append(ev.cuda_event)
         ev_arr = (ctypes.c_void_p * len(handles))(*handles)
-    if grouping == "hash" and kv_block == 1 and residual and ev_arr is None and not noalloc:
+    if (grouping == "hash" and kv_block == 1 and residual and ev_arr is None and not noalloc and rcode == 0
+            and keep_mass == 0):
         with torch.cuda.device(q.device):
             L.check(L.lib().mcs_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), group_size, _i32p(ka), pjp,
                                        _ptr(meta_buf), meta_buf.numel(), _ptr(workspace), workspace.numel(),
@@ -267,7 +293,8 @@ def select(q, k, v, group_size, keep, proj, scale=None, meta_buf=None, workspace
         if grouping not in codes:
             raise ValueError(f"unknown grouping {grouping!r}")
         gt, gy, gx = (int(x) for x in grid) if grouping == "morton" else (0, 0, 0)
-        opts = L.SelectOptions(codes[grouping], int(kv_block), 1 if residual else 0, gt, gy, gx,
+        opts = L.SelectOptions(codes[grouping], int(kv_block), 1 if residual else 0, gt, gy, gx, rcode,
+                               float(keep_mass),
                                ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr is not None else None,
                                len(phase_events) if ev_arr is not None else 0)
         with torch.cuda.device(q.device):

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   __amdgpu_buffer_rsrc_t ridx;  // the group's kept keys; reads past the end return 0 (row 0)
   if constexpr (SPARSE) {
     long long start;
-    group_keys(a.keep, a.idx_start, h, tile, N, a.total_idx, &start, &nkv);
+    group_keys(a.keep, a.idx_start, a.count, h, tile, N, a.ng, a.total_idx, &start, &nkv);
     ridx = __builtin_amdgcn_make_buffer_rsrc((void*)(a.idx + start), (short)0, nkv * 4, kBufferConfig);
   }
   const int nt = (nkv + BK - 1) / BK;
@@ -426,19 +426,37 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
           uint16_t* out = static_cast<uint16_t*>(a.o) + hoff + (size_t)p * D + col;
           *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         } else if constexpr (MODE == MODE_SELECT) {
-          *reinterpret_cast<f32x4*>(a.residual + hoff + (size_t)p * D + col) = o;
+          // the float32 dense output goes to the residual region, or (bf16
+          // residual) to the workspace until the sparse pass forms the residual
+          float* od = a.odense ? a.odense + (size_t)hs * N * D : static_cast<float*>(a.residual) + hoff;
+          *reinterpret_cast<f32x4*>(od + (size_t)p * D + col) = o;
           if (a.o) {
             uint16_t* out = static_cast<uint16_t*>(a.o) + hoff + (size_t)rtok[rb] * D + col;
             *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
           }
         } else if constexpr (MODE == MODE_REUSE) {
-          const f32x4 res = *reinterpret_cast<const f32x4*>(a.residual + hoff + (size_t)p * D + col);
+          f32x4 res;
+          if (a.residual_bf16) {
+            const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.residual) + hoff +
+                                                            (size_t)p * D + col);
+            res = f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                        __uint_as_float(r.y & 0xffff0000u)};
+          } else {
+            res = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.residual) + hoff + (size_t)p * D + col);
+          }
           const f32x4 y = o + res;
           uint16_t* out = static_cast<uint16_t*>(a.o) + hoff + (size_t)rtok[rb] * D + col;
           *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
         } else {  // MODE_RESINIT
-          f32x4* rp = reinterpret_cast<f32x4*>(a.residual + hoff + (size_t)p * D + col);
-          *rp = *rp - o;
+          if (a.residual_bf16) {
+            const f32x4 od = *reinterpret_cast<const f32x4*>(a.odense + (size_t)hs * N * D + (size_t)p * D + col);
+            const f32x4 r = od - o;
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.residual) + hoff + (size_t)p * D + col) =
+                make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+          } else {
+            f32x4* rp = reinterpret_cast<f32x4*>(static_cast<float*>(a.residual) + hoff + (size_t)p * D + col);
+            *rp = *rp - o;
+          }
         }
       }
     }

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
   const int32_t* kvidx = nullptr;
   if constexpr (SPARSE) {
     long long start;
-    group_keys(a.keep, a.idx_start, h, tile, N, a.total_idx, &start, &nkv);
+    group_keys(a.keep, a.idx_start, a.count, h, tile, N, a.ng, a.total_idx, &start, &nkv);
     kvidx = a.idx + start;
   }
 
@@ -100,7 +100,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
 
   const float inv = 1.0f / l;
   if (valid) {
-    float* resrow = a.residual ? a.residual + hoff + (size_t)p * D : nullptr;
+    // float32 problems keep a float32 residual
+    float* resrow = a.residual ? static_cast<float*>(a.residual) + hoff + (size_t)p * D : nullptr;
     if constexpr (MODE == MODE_PLAIN) {
       float* out = static_cast<float*>(a.o) + hoff + (size_t)p * D;
 #pragma unroll

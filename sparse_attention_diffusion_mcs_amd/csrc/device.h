@@ -31,9 +31,11 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks, int run) {
 // bounds.
 __device__ __forceinline__ int clamp_index(int i, int n) { return (unsigned)i < (unsigned)n ? i : (i < 0 ? 0 : n - 1); }
 
-// Start and length of one group's kept keys, kept inside [0, total).
-__device__ __forceinline__ void group_keys(const int32_t* keep, const int64_t* idx_start, int h, int g, int n,
-                                           long long total, long long* start, int* count) {
+// Start and length of one group's kept keys: the group's slot of keep[h]
+// indices starts at idx_start[h] + g * keep[h], and its first count[h][g]
+// (clamped to [1, keep[h]]) are the kept keys; both kept inside [0, total).
+__device__ __forceinline__ void group_keys(const int32_t* keep, const int64_t* idx_start, const int32_t* counts, int h,
+                                           int g, int n, int ng, long long total, long long* start, int* count) {
   int k = keep[h];
   k = k < 1 ? 1 : (k > n ? n : k);
   long long s = idx_start[h] + (long long)g * k;
@@ -41,8 +43,10 @@ __device__ __forceinline__ void group_keys(const int32_t* keep, const int64_t* i
     s = 0;
     if (k > total) k = (int)total;
   }
+  int c = counts ? counts[(size_t)h * ng + g] : k;
+  c = c < 1 ? 1 : (c > k ? k : c);
   *start = s;
-  *count = k;
+  *count = c;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

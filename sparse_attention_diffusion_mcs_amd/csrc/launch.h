@@ -20,7 +20,12 @@ struct AttnArgs {
   const void* k;
   const void* v;
   void* o;                   // PLAIN/REUSE: output; SELECT: optional dense output (original order)
-  float* residual;           // [H][N][d], sorted-position rows
+  void* residual;            // [H][N][d], sorted-position rows: float32, or bf16 when residual_bf16
+  int residual_bf16;         // REUSE/RESINIT: the residual region holds bf16
+  float* odense;             // SELECT out, RESINIT in: float32 dense output [nheads][N][d] (sorted rows), when
+                             // the residual is bf16 (else SELECT writes it into the float32 residual region)
+  const int32_t* count;      // [H][ng] kept keys per group (REUSE, RESINIT)
+  float keep_mass;           // selection: retained-mass target (0: fixed budgets)
   float* colsum;             // SCORE: [nheads][ng][ldc] key scores of the launched heads
   float* lse;                // SELECT out, SCORE in: [nheads][N] log2-sum-exp of the sorted rows
   const int32_t* perm;       // [H][N]
@@ -48,9 +53,14 @@ hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, const 
                             int N, int D, hipStream_t s);
 hipError_t launch_query_mean(const void* q, int dtype, double* mean, int H, int N, int D, hipStream_t s);
 hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hipStream_t s);
-hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, const int32_t* keep,
-                             const int64_t* idx_start, int head0, int nheads, int ng, int N, int block,
-                             hipStream_t s);
+// Writes each group's kept keys (idx) and their number (count[h][g]); with
+// keep_mass > 0 the number comes from the retained-mass target (groups of G
+// of the nq queries), else it is keep[h] / block blocks.
+hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, int32_t* count, const int32_t* keep,
+                             const int64_t* idx_start, int head0, int nheads, int ng, int N, int G, int nq, int block,
+                             float keep_mass, hipStream_t s);
+// count[h][g] = keep[h] for every group of every head (device tables)
+hipError_t launch_fill_counts(int32_t* count, const int32_t* keep, int H, int ng, hipStream_t s);
 // ablation helpers: 64-key block scores of score rows, raster-order
 // permutation, zero fill (residual off)
 hipError_t launch_block_scores(const float* colsum, int ldc, float* bs, int ldb, long long rows, int nb,

@@ -61,8 +61,9 @@ mcs_status check_group_keep(const mcs_attn_desc* d, int32_t G, const int32_t* ke
   return MCS_SUCCESS;
 }
 
-// Region offsets and size of a metadata buffer holding `total` kept indices.
-void place_regions(const mcs_attn_desc* d, int64_t total, mcs_meta* m) {
+// Region offsets and size of a metadata buffer holding `total` kept indices
+// and a residual of residual_dtype.
+void place_regions(const mcs_attn_desc* d, int32_t ng, int64_t total, int32_t residual_dtype, mcs_meta* m) {
   const uint64_t H = (uint64_t)d->num_heads, N = (uint64_t)d->seq_len, D = (uint64_t)d->head_dim;
   uint64_t off = 0;
   m->off_perm = off;
@@ -73,14 +74,16 @@ void place_regions(const mcs_attn_desc* d, int64_t total, mcs_meta* m) {
   off = align_up(off + H * 8, kAlign);
   m->off_sched = off;
   off = align_up(off + H * 4, kAlign);
+  m->off_count = off;
+  off = align_up(off + H * (uint64_t)ng * 4, kAlign);
   m->off_idx = off;
   off = align_up(off + (uint64_t)total * 4, kAlign);
   m->off_residual = off;
-  off = align_up(off + H * N * D * 4, kAlign);
+  off = align_up(off + H * N * D * (residual_dtype == MCS_DTYPE_BF16 ? 2 : 4), kAlign);
   m->bytes = off;
 }
 
-void make_layout(const mcs_attn_desc* d, int32_t G, const int32_t* keep, mcs_meta* m) {
+void make_layout(const mcs_attn_desc* d, int32_t G, const int32_t* keep, int32_t residual_dtype, mcs_meta* m) {
   const uint64_t H = (uint64_t)d->num_heads, N = (uint64_t)d->seq_len;
   std::memset(m, 0, sizeof(*m));
   m->version = MCS_META_VERSION;
@@ -90,6 +93,7 @@ void make_layout(const mcs_attn_desc* d, int32_t G, const int32_t* keep, mcs_met
   m->dtype = d->dtype;
   m->group_size = G;
   m->num_groups = (int32_t)((N + G - 1) / G);
+  m->residual_dtype = residual_dtype;
   int64_t total = 0;
   int32_t mk = 0;
   if (N > 0)
@@ -99,7 +103,12 @@ void make_layout(const mcs_attn_desc* d, int32_t G, const int32_t* keep, mcs_met
     }
   m->max_keep = mk;
   m->total_idx = total;
-  place_regions(d, total, m);
+  place_regions(d, m->num_groups, total, residual_dtype, m);
+}
+
+// The residual dtype of a problem: float32 always, bf16 for bf16 problems.
+bool residual_dtype_ok(const mcs_attn_desc* d, int32_t rd) {
+  return rd == MCS_DTYPE_FP32 || (rd == MCS_DTYPE_BF16 && d->dtype == MCS_DTYPE_BF16);
 }
 
 uint64_t colsum_ld(int N) { return align_up((uint64_t)N, 64); }
@@ -108,11 +117,14 @@ uint64_t colsum_ld(int N) { return align_up((uint64_t)N, 64); }
 uint64_t block_ld(int N) { return align_up((uint64_t)(N + 63) / 64, 64); }
 
 struct WsLayout {
-  uint64_t off_keys, off_proj, off_mean, off_colsum, per_head_colsum, per_head_block, per_head_lse, fixed;
+  uint64_t off_keys, off_proj, off_mean, off_colsum, per_head_colsum, per_head_block, per_head_lse, per_head_odense,
+      fixed;
+  uint64_t per_head() const { return per_head_colsum + per_head_block + per_head_lse + per_head_odense; }
 };
 
-// keys | projections | query means | key scores [hc][ng][ldc] | block scores [hc][ng][ldb] | row lse [hc][N]
-WsLayout ws_layout(const mcs_attn_desc* d, int32_t G) {
+// keys | projections | query means | key scores [hc][ng][ldc] | block scores [hc][ng][ldb] | row lse [hc][N] |
+// float32 dense output [hc][N][d] (bf16 residual only)
+WsLayout ws_layout(const mcs_attn_desc* d, int32_t G, bool bf16_residual) {
   const uint64_t H = (uint64_t)d->num_heads, N = (uint64_t)d->seq_len;
   const uint64_t ng = (N + G - 1) / G;
   WsLayout w;
@@ -123,6 +135,7 @@ WsLayout ws_layout(const mcs_attn_desc* d, int32_t G) {
   w.per_head_colsum = ng * colsum_ld((int)N) * 4;
   w.per_head_block = ng * block_ld((int)N) * 4;
   w.per_head_lse = align_up(N * 4, kAlign);
+  w.per_head_odense = bf16_residual ? align_up(N * (uint64_t)d->head_dim * 4, kAlign) : 0;
   w.fixed = w.off_colsum;
   return w;
 }
@@ -151,6 +164,10 @@ mcs_status upload_meta_tables(const mcs_meta* m, const int32_t* keep, hipStream_
       hipSuccess)
     return hip_fail(e);
   if ((e = mcs::launch_fill_bytes(at<void>(m->base, m->off_sched), sched.data(), (size_t)H * 4, s)) != hipSuccess)
+    return hip_fail(e);
+  // every group keeps k_h keys until a selection writes its own counts
+  if ((e = mcs::launch_fill_counts(at<int32_t>(m->base, m->off_count), at<int32_t>(m->base, m->off_keep), H,
+                                   m->num_groups, s)) != hipSuccess)
     return hip_fail(e);
   return MCS_SUCCESS;
 }
@@ -208,13 +225,18 @@ mcs_status mcs_dense_attn(const mcs_attn_desc* d, const void* q, const void* k, 
   return e == hipSuccess ? MCS_SUCCESS : hip_fail(e);
 }
 
-mcs_status mcs_meta_layout(const mcs_attn_desc* d, int32_t G, const int32_t* keep, mcs_meta* layout) {
+mcs_status mcs_meta_layout_ex(const mcs_attn_desc* d, int32_t G, const int32_t* keep, int32_t residual_dtype,
+                              mcs_meta* layout) {
   mcs_status st;
   if ((st = check_desc(d)) != MCS_SUCCESS) return st;
   if ((st = check_group_keep(d, G, keep)) != MCS_SUCCESS) return st;
-  if (!layout) return MCS_ERROR_INVALID_VALUE;
-  make_layout(d, G, keep, layout);
+  if (!layout || !residual_dtype_ok(d, residual_dtype)) return MCS_ERROR_INVALID_VALUE;
+  make_layout(d, G, keep, residual_dtype, layout);
   return MCS_SUCCESS;
+}
+
+mcs_status mcs_meta_layout(const mcs_attn_desc* d, int32_t G, const int32_t* keep, mcs_meta* layout) {
+  return mcs_meta_layout_ex(d, G, keep, MCS_DTYPE_FP32, layout);
 }
 
 size_t mcs_meta_bytes(const mcs_attn_desc* d, int32_t G, const int32_t* keep) {
@@ -223,22 +245,29 @@ size_t mcs_meta_bytes(const mcs_attn_desc* d, int32_t G, const int32_t* keep) {
   return (size_t)m.bytes;
 }
 
-size_t mcs_select_workspace_bytes(const mcs_attn_desc* d, int32_t G, int32_t heads_per_chunk) {
+size_t mcs_select_workspace_bytes_ex(const mcs_attn_desc* d, int32_t G, int32_t heads_per_chunk,
+                                     const mcs_select_options* opts) {
   if (check_desc(d) != MCS_SUCCESS) return 0;
   if (G != 64 && G != 128) return 0;
-  const WsLayout w = ws_layout(d, G);
+  const int32_t rd = opts ? opts->residual_dtype : MCS_DTYPE_FP32;
+  if (!residual_dtype_ok(d, rd)) return 0;
+  const WsLayout w = ws_layout(d, G, rd == MCS_DTYPE_BF16);
   const int64_t hc = std::max<int64_t>(1, std::min<int64_t>(heads_per_chunk, std::max(1, d->num_heads)));
-  return (size_t)(w.fixed + (uint64_t)hc * (w.per_head_colsum + w.per_head_block + w.per_head_lse));
+  return (size_t)(w.fixed + (uint64_t)hc * w.per_head());
 }
 
-mcs_status mcs_meta_init(const mcs_attn_desc* d, int32_t G, const int32_t* keep, void* meta_buf,
-                         size_t meta_bytes, mcs_meta* meta_out, void* stream) {
+size_t mcs_select_workspace_bytes(const mcs_attn_desc* d, int32_t G, int32_t heads_per_chunk) {
+  return mcs_select_workspace_bytes_ex(d, G, heads_per_chunk, nullptr);
+}
+
+mcs_status mcs_meta_init_ex(const mcs_attn_desc* d, int32_t G, const int32_t* keep, int32_t residual_dtype,
+                            void* meta_buf, size_t meta_bytes, mcs_meta* meta_out, void* stream) {
   mcs_status st;
   if ((st = check_desc(d)) != MCS_SUCCESS) return st;
   if ((st = check_group_keep(d, G, keep)) != MCS_SUCCESS) return st;
-  if (!meta_out) return MCS_ERROR_INVALID_VALUE;
+  if (!meta_out || !residual_dtype_ok(d, residual_dtype)) return MCS_ERROR_INVALID_VALUE;
   mcs_meta m;
-  make_layout(d, G, keep, &m);
+  make_layout(d, G, keep, residual_dtype, &m);
   if (!empty(d)) {
     if (!meta_buf) return MCS_ERROR_INVALID_VALUE;
     if (!aligned(meta_buf, kAlign)) return MCS_ERROR_MISALIGNED;
@@ -248,6 +277,11 @@ mcs_status mcs_meta_init(const mcs_attn_desc* d, int32_t G, const int32_t* keep,
   if (!empty(d) && (st = upload_meta_tables(&m, keep, static_cast<hipStream_t>(stream))) != MCS_SUCCESS) return st;
   *meta_out = m;
   return MCS_SUCCESS;
+}
+
+mcs_status mcs_meta_init(const mcs_attn_desc* d, int32_t G, const int32_t* keep, void* meta_buf,
+                         size_t meta_bytes, mcs_meta* meta_out, void* stream) {
+  return mcs_meta_init_ex(d, G, keep, MCS_DTYPE_FP32, meta_buf, meta_bytes, meta_out, stream);
 }
 
 mcs_status mcs_select(const mcs_attn_desc* d, const void* q, const void* k, const void* v, int32_t G,
@@ -270,8 +304,11 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
   if ((st = check_desc(d)) != MCS_SUCCESS) return st;
   if ((st = check_group_keep(d, G, keep)) != MCS_SUCCESS) return st;
   if (!meta_out) return MCS_ERROR_INVALID_VALUE;
-  mcs_select_options o{MCS_GROUPING_HASH, 1, 1, 0, 0, 0, nullptr, 0};
+  mcs_select_options o{MCS_GROUPING_HASH, 1, 1, 0, 0, 0, MCS_DTYPE_FP32, 0.f, nullptr, 0};
   if (opts) o = *opts;
+  if (!residual_dtype_ok(d, o.residual_dtype) || !std::isfinite(o.keep_mass) || o.keep_mass < 0.f ||
+      o.keep_mass > 1.f || (o.keep_mass > 0.f && o.kv_block != 1))
+    return MCS_ERROR_INVALID_VALUE;
   if ((o.grouping != MCS_GROUPING_HASH && o.grouping != MCS_GROUPING_RASTER &&
        o.grouping != MCS_GROUPING_CENTRED_HASH && o.grouping != MCS_GROUPING_MORTON) ||
       (o.kv_block != 1 && o.kv_block != 64) || (o.residual != 0 && o.residual != 1))
@@ -293,20 +330,21 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
       if (keep[h] % o.kv_block) return MCS_ERROR_UNSUPPORTED_SHAPE;
   }
   mcs_meta m;
-  make_layout(d, G, keep, &m);
+  make_layout(d, G, keep, o.residual_dtype, &m);
   m.base = meta_buf;
   if (empty(d)) {
     *meta_out = m;
     return MCS_SUCCESS;
   }
+  const bool bf16_res = o.residual_dtype == MCS_DTYPE_BF16;
   for (const void* p : {q, k, v})
     if ((st = check_tensor(p)) != MCS_SUCCESS) return st;
   if (o_dense_out && !aligned(o_dense_out, 16)) return MCS_ERROR_MISALIGNED;
   if (!proj || !meta_buf || (!ws && !scratch)) return MCS_ERROR_INVALID_VALUE;
   if (!aligned(meta_buf, kAlign) || (!scratch && !aligned(ws, kAlign))) return MCS_ERROR_MISALIGNED;
   if (meta_bytes < m.bytes) return MCS_ERROR_BUFFER_TOO_SMALL;
-  const WsLayout wl = ws_layout(d, G);
-  const uint64_t per_head = wl.per_head_colsum + wl.per_head_block + wl.per_head_lse;
+  const WsLayout wl = ws_layout(d, G, bf16_res);
+  const uint64_t per_head = wl.per_head();
   if (scratch) ws_bytes = MCS_NOALLOC_SCRATCH_BYTES;
   if (ws_bytes < wl.fixed + per_head) return MCS_ERROR_BUFFER_TOO_SMALL;
   if (scratch) {
@@ -326,6 +364,9 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
   float* colsum = at<float>(ws, wl.off_colsum);
   float* bscore = at<float>(ws, wl.off_colsum + (uint64_t)hc * wl.per_head_colsum);
   float* lse = at<float>(ws, wl.off_colsum + (uint64_t)hc * (wl.per_head_colsum + wl.per_head_block));
+  float* odense = bf16_res ? at<float>(ws, wl.off_colsum + (uint64_t)hc * (wl.per_head_colsum + wl.per_head_block +
+                                                                          wl.per_head_lse))
+                           : nullptr;
   int32_t* perm = at<int32_t>(meta_buf, m.off_perm);
   if (o.grouping == MCS_GROUPING_HASH || o.grouping == MCS_GROUPING_CENTRED_HASH) {
     double* mean = nullptr;
@@ -349,7 +390,11 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
   if ((e = mark(0)) != hipSuccess) return hip_fail(e);
 
   mcs::AttnArgs a = base_args(d, q, k, v);
-  a.residual = at<float>(meta_buf, m.off_residual);
+  a.residual = at<void>(meta_buf, m.off_residual);
+  a.residual_bf16 = bf16_res ? 1 : 0;
+  a.odense = odense;
+  a.count = at<int32_t>(meta_buf, m.off_count);
+  a.keep_mass = o.keep_mass;
   a.colsum = colsum;
   a.lse = lse;
   a.perm = perm;
@@ -371,21 +416,24 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
       return hip_fail(e);
     if ((e = mark(2)) != hipSuccess) return hip_fail(e);
     if (o.kv_block == 1) {
-      e = mcs::launch_group_topk(colsum, a.ldc, at<int32_t>(meta_buf, m.off_idx), a.keep, a.idx_start, h0,
-                                 a.nheads, a.ng, N, 1, s);
+      e = mcs::launch_group_topk(colsum, a.ldc, at<int32_t>(meta_buf, m.off_idx), at<int32_t>(meta_buf, m.off_count),
+                                 a.keep, a.idx_start, h0, a.nheads, a.ng, N, G, N, 1, o.keep_mass, s);
     } else {
       const int nb = N / o.kv_block, ldb = (int)block_ld(N);
       e = mcs::launch_block_scores(colsum, a.ldc, bscore, ldb, (long long)a.nheads * a.ng, nb, s);
       if (e == hipSuccess)
-        e = mcs::launch_group_topk(bscore, ldb, at<int32_t>(meta_buf, m.off_idx), a.keep, a.idx_start, h0,
-                                   a.nheads, a.ng, nb, o.kv_block, s);
+        e = mcs::launch_group_topk(bscore, ldb, at<int32_t>(meta_buf, m.off_idx),
+                                   at<int32_t>(meta_buf, m.off_count), a.keep, a.idx_start, h0, a.nheads, a.ng, nb,
+                                   G, N, o.kv_block, 0.f, s);
     }
     if (e != hipSuccess || (e = mark(3)) != hipSuccess) return hip_fail(e);
     a.o = nullptr;
     if (o.residual)
       e = launch_attn(d->dtype, mcs::MODE_RESINIT, a, s);
     else
-      e = mcs::launch_zero_floats(a.residual + (size_t)h0 * N * D, (long long)a.nheads * N * D, s);
+      e = mcs::launch_zero_floats(reinterpret_cast<float*>(static_cast<char*>(a.residual) +
+                                                           (size_t)h0 * N * D * (bf16_res ? 2 : 4)),
+                                  (long long)a.nheads * N * D / (bf16_res ? 2 : 1), s);
     if (e != hipSuccess || (e = mark(4)) != hipSuccess) return hip_fail(e);
   }
   *meta_out = m;
@@ -409,7 +457,7 @@ mcs_status mcs_select_noalloc(const mcs_attn_desc* d, const void* q, const void*
   // Shapes whose fixed workspace and one head's scores exceed the array are
   // refused first (a zero size is an invalid descriptor or group size, which
   // the ordinary validation reports).
-  if (mcs_select_workspace_bytes(d, G, 1) > MCS_NOALLOC_SCRATCH_BYTES) return MCS_ERROR_BUFFER_TOO_SMALL;
+  if (mcs_select_workspace_bytes_ex(d, G, 1, opts) > MCS_NOALLOC_SCRATCH_BYTES) return MCS_ERROR_BUFFER_TOO_SMALL;
   return select_impl(d, q, k, v, G, keep, proj, opts, meta_buf, meta_bytes, nullptr, 0, o_dense_out, meta_out,
                      stream, true);
 }
@@ -421,17 +469,17 @@ mcs_status mcs_sparse_attn(const mcs_attn_desc* d, const void* q, const void* k,
   if (!m) return MCS_ERROR_INVALID_VALUE;
   if (m->version != MCS_META_VERSION || m->num_heads != d->num_heads || m->seq_len != d->seq_len ||
       m->head_dim != d->head_dim || m->dtype != d->dtype || (m->group_size != 64 && m->group_size != 128) ||
-      m->num_groups != (d->seq_len + m->group_size - 1) / m->group_size)
+      m->num_groups != (d->seq_len + m->group_size - 1) / m->group_size || !residual_dtype_ok(d, m->residual_dtype))
     return MCS_ERROR_META_MISMATCH;
   // the regions must sit where this layout version puts them for the
   // struct's own index count (at most every head keeping every key)
   if (m->total_idx < 0 || (double)m->total_idx > (double)m->num_groups * d->seq_len * d->num_heads)
     return MCS_ERROR_META_MISMATCH;
   mcs_meta ref;
-  place_regions(d, m->total_idx, &ref);
+  place_regions(d, m->num_groups, m->total_idx, m->residual_dtype, &ref);
   if (m->off_perm != ref.off_perm || m->off_keep != ref.off_keep || m->off_idx_start != ref.off_idx_start ||
-      m->off_sched != ref.off_sched || m->off_idx != ref.off_idx || m->off_residual != ref.off_residual ||
-      m->bytes != ref.bytes)
+      m->off_sched != ref.off_sched || m->off_count != ref.off_count || m->off_idx != ref.off_idx ||
+      m->off_residual != ref.off_residual || m->bytes != ref.bytes)
     return MCS_ERROR_META_MISMATCH;
   if (empty(d)) return MCS_SUCCESS;
   for (const void* p : {q, k, v, (const void*)o})
@@ -440,7 +488,9 @@ mcs_status mcs_sparse_attn(const mcs_attn_desc* d, const void* q, const void* k,
   if (!aligned(m->base, kAlign)) return MCS_ERROR_MISALIGNED;
   mcs::AttnArgs a = base_args(d, q, k, v);
   a.o = o;
-  a.residual = at<float>(m->base, m->off_residual);
+  a.residual = at<void>(m->base, m->off_residual);
+  a.residual_bf16 = m->residual_dtype == MCS_DTYPE_BF16 ? 1 : 0;
+  a.count = at<int32_t>(m->base, m->off_count);
   a.perm = at<int32_t>(m->base, m->off_perm);
   a.keep = at<int32_t>(m->base, m->off_keep);
   a.idx_start = at<int64_t>(m->base, m->off_idx_start);

@@ -226,23 +226,150 @@ __device__ __forceinline__ void block_excl_scan2(int a, int b, int* ea, int* eb,
   *tb = tot_b;
 }
 
+// Fixed-point value of a score for the retained-mass budget: floor(x * 2^48)
+// for the non-negative float32 with bit pattern x (x = m * 2^(e - 150) with
+// the 24-bit significand m of a normal number; zero and subnormals give 0).
+__device__ __forceinline__ unsigned long long mass_units(uint32_t x) {
+  const int e = (int)(x >> 23);
+  if (e == 0) return 0ull;
+  const unsigned long long m = (x & 0x7fffffu) | 0x800000u;
+  const int sft = e - 102;
+  if (sft >= 0) return sft < 40 ? (m << sft) : ~0ull;
+  return -sft >= 64 ? 0ull : (m >> -sft);
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int src = (lane - off) << 2;
+    const uint32_t lo = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(x >> 32));
+    if (lane >= off) x += ((unsigned long long)hi << 32) | lo;
+  }
+  return x;
+}
+
+// The budget of one group under a retained-mass target: the fewest keys, in
+// the top-k order (score descending, index ascending), whose fixed-point
+// scores sum to at least ceil(mass * glen * 2^48), at most cap, at least 1.
+// Three histogram passes (counts and sums per bin, the same bit fields as the
+// top-k) find the score T* at which the running sum from the top reaches the
+// target; the keys above T* and just enough of those equal to T* make the
+// count.  Reads the row three times.
+__device__ __forceinline__ int topk_mass_count(const uint32_t* __restrict__ row, int N, float mass, int glen, int cap,
+                                               int* hist, unsigned long long* hsum, unsigned long long* shq, int* sh,
+                                               int* found) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NW = TK_NT / 64;
+  const unsigned long long target =
+      (unsigned long long)ceil((double)mass * (double)glen * 281474976710656.0);  // * 2^48
+  unsigned long long rem = target;
+  int above = 0;
+  uint32_t prefix = 0, pmask = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    for (int b = tid; b < 2048; b += TK_NT) {
+      hist[b] = 0;
+      hsum[b] = 0ull;
+    }
+    __syncthreads();
+    for (int j0 = 4 * tid; j0 < N; j0 += 4 * TK_NT) {
+      uint32_t u[4];
+      if (j0 + 4 <= N) {
+        const uint4 x = *reinterpret_cast<const uint4*>(row + j0);
+        u[0] = x.x;
+        u[1] = x.y;
+        u[2] = x.z;
+        u[3] = x.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = (j0 + e < N) ? row[j0 + e] : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + e < N && (u[e] & pmask) == prefix) {
+          const int b = (u[e] >> shift) & (nb - 1);
+          atomicAdd(&hist[b], 1);
+          atomicAdd(&hsum[b], mass_units(u[e]));
+        }
+    }
+    __syncthreads();
+    // thread t owns bins [t*per, (t+1)*per); sums above a thread = total - inclusive
+    const int per = nb / TK_NT;
+    unsigned long long msum = 0ull;
+    int mcnt = 0;
+    for (int b = 0; b < per; ++b) {
+      msum += hsum[tid * per + b];
+      mcnt += hist[tid * per + b];
+    }
+    const unsigned long long incl = wave_incl_scan_u64(msum);
+    if (lane == 63) shq[w] = incl;
+    int ecnt, unused_e, tcnt, unused_t;
+    block_excl_scan2(mcnt, 0, &ecnt, &unused_e, &tcnt, &unused_t, sh);  // synchronises shq too
+    unsigned long long wbefore = 0ull, total = 0ull;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      if (ww < w) wbefore += shq[ww];
+      total += shq[ww];
+    }
+    if (tid == 0) found[0] = -1;
+    __syncthreads();
+    unsigned long long asum = total - (wbefore + incl);   // sums of the bins above this thread's
+    int acnt = tcnt - ecnt - mcnt;
+    if (asum < rem && asum + msum >= rem) {
+      for (int b = per - 1; b >= 0; --b) {
+        const int bin = tid * per + b;
+        if (asum + hsum[bin] >= rem) {
+          found[0] = bin;
+          found[1] = acnt;
+          shq[NW] = asum;
+          break;
+        }
+        asum += hsum[bin];
+        acnt += hist[bin];
+      }
+    }
+    __syncthreads();
+    if (found[0] < 0) return cap;  // even every key falls short: all are needed
+    prefix |= (uint32_t)found[0] << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    above += found[1];
+    rem -= shq[NW];
+    __syncthreads();
+  }
+  const unsigned long long unit = mass_units(prefix);
+  const long long need = unit ? (long long)((rem + unit - 1) / unit) : 1;
+  const long long n = (long long)above + need;
+  return (int)(n < 1 ? 1 : (n > cap ? cap : n));
+}
+
 // One workgroup per (head, group) row of N scores: the keep[h] / block
-// largest (ties to the lower index), written ascending.  With block > 1 the
-// row holds scores of whole key blocks and every kept block b is written as
-// its keys b*block .. b*block + block - 1.
+// largest (ties to the lower index), written ascending, and their number
+// (in keys) to count[h][g].  With block > 1 the row holds scores of whole key
+// blocks and every kept block b is written as its keys b*block .. b*block +
+// block - 1.  With MASS the number kept is the retained-mass budget of the
+// group (capped at keep[h]); groups are runs of G of the nq queries.
+template <bool MASS>
 __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restrict__ colsum, int ldc,
-                                                           int32_t* __restrict__ idx, const int32_t* __restrict__ keep,
+                                                           int32_t* __restrict__ idx, int32_t* __restrict__ count,
+                                                           const int32_t* __restrict__ keep,
                                                            const int64_t* __restrict__ idx_start, int head0, int ng,
-                                                           int N, int block) {
+                                                           int N, int G, int nq, int block, float keep_mass) {
   __shared__ int hist[2048];
   __shared__ uint32_t cand[TK_CAP];
+  __shared__ unsigned long long hsum[MASS ? 2048 : 1];
+  __shared__ unsigned long long shq[TK_NT / 64 + 1];
   __shared__ int sh[8];
   __shared__ int found[3];
   const int tid = threadIdx.x;
   const int g = blockIdx.x, hl = blockIdx.y, h = head0 + hl;
   const uint32_t* row = reinterpret_cast<const uint32_t*>(colsum + ((size_t)hl * ng + g) * ldc);
-  const int k = keep[h] / block;
+  int k = keep[h] / block;
   int32_t* out = idx + idx_start[h] + (int64_t)g * keep[h];
+  if constexpr (MASS) k = topk_mass_count(row, N, keep_mass, min(G, nq - g * G), k, hist, hsum, shq, sh, found);
+  if (tid == 0) count[(size_t)h * ng + g] = k * block;
 
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
@@ -426,6 +553,13 @@ __global__ void morton_perm_kernel(int32_t* __restrict__ perm, int H, int N, int
   for (int h = 0; h < H; ++h) perm[(size_t)h * N + rank] = tok;
 }
 
+// count[h][g] = keep[h]: every group keeps its head's full budget.
+__global__ void fill_counts_kernel(int32_t* __restrict__ count, const int32_t* __restrict__ keep, long long total,
+                                   int ng) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long long)gridDim.x * blockDim.x)
+    count[i] = keep[i / ng];
+}
+
 __global__ void zero_floats_kernel(float* __restrict__ p, long long n) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
     p[i] = 0.f;
@@ -501,12 +635,24 @@ hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hi
   return hipGetLastError();
 }
 
-hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, const int32_t* keep,
-                             const int64_t* idx_start, int head0, int nheads, int ng, int N, int block,
-                             hipStream_t s) {
+hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, int32_t* count, const int32_t* keep,
+                             const int64_t* idx_start, int head0, int nheads, int ng, int N, int G, int nq, int block,
+                             float keep_mass, hipStream_t s) {
   if (nheads == 0 || ng == 0) return hipSuccess;
-  hipLaunchKernelGGL(group_topk_kernel, dim3(ng, nheads), dim3(TK_NT), 0, s, colsum, ldc, idx, keep, idx_start,
-                     head0, ng, N, block);
+  if (keep_mass > 0.f)
+    hipLaunchKernelGGL(group_topk_kernel<true>, dim3(ng, nheads), dim3(TK_NT), 0, s, colsum, ldc, idx, count, keep,
+                       idx_start, head0, ng, N, G, nq, block, keep_mass);
+  else
+    hipLaunchKernelGGL(group_topk_kernel<false>, dim3(ng, nheads), dim3(TK_NT), 0, s, colsum, ldc, idx, count, keep,
+                       idx_start, head0, ng, N, G, nq, block, keep_mass);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_counts(int32_t* count, const int32_t* keep, int H, int ng, hipStream_t s) {
+  const long long total = (long long)H * ng;
+  if (total == 0) return hipSuccess;
+  const long long blocks = std::min<long long>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(fill_counts_kernel, dim3((unsigned)blocks), dim3(256), 0, s, count, keep, total, ng);
   return hipGetLastError();
 }
 

@@ -46,16 +46,29 @@ int main(void) {
   CHECK(m.max_keep == 100);
   CHECK(m.total_idx == 16 * (64 + 100 + 7));
   CHECK(m.base == NULL);
-  CHECK(m.off_perm % 256 == 0 && m.off_idx % 256 == 0 && m.off_residual % 256 == 0);
+  CHECK(m.off_perm % 256 == 0 && m.off_count % 256 == 0 && m.off_idx % 256 == 0 && m.off_residual % 256 == 0);
+  CHECK(m.residual_dtype == MCS_DTYPE_FP32);
   end = m.off_residual + (uint64_t)3 * 1000 * 64 * 4; /* float32 residual [H][N][d] */
   CHECK(m.bytes >= end);
   bytes = mcs_meta_bytes(&d, 64, keep);
   CHECK(bytes == m.bytes);
+  /* the same layout with a bf16 residual */
+  CHECK(mcs_meta_layout_ex(&d, 64, keep, MCS_DTYPE_BF16, &m) == MCS_SUCCESS);
+  CHECK(m.residual_dtype == MCS_DTYPE_BF16 && m.bytes == end - (uint64_t)3 * 1000 * 64 * 2);
 
   ws1 = mcs_select_workspace_bytes(&d, 64, 1);
   ws3 = mcs_select_workspace_bytes(&d, 64, 3);
   CHECK(ws1 > 0 && ws3 > ws1);
   CHECK(mcs_select_workspace_bytes(&d, 64, 99) == ws3); /* clamped to H */
+  {
+    mcs_select_options o;
+    memset(&o, 0, sizeof o);
+    o.kv_block = 1;
+    o.residual = 1;
+    o.residual_dtype = MCS_DTYPE_BF16;
+    CHECK(mcs_select_workspace_bytes_ex(&d, 64, 1, &o) == ws1 + (size_t)1000 * 64 * 4);
+    CHECK(mcs_select_workspace_bytes_ex(&d, 64, 1, NULL) == ws1);
+  }
 
   /* argument checks that fail before any device work */
   CHECK(mcs_meta_layout(&d, 32, keep, &m) == MCS_ERROR_UNSUPPORTED_SHAPE);

@@ -147,13 +147,36 @@ def sample_groups(ng, extra=4, seed=0):
     return sorted(base | {int(x) for x in pick})
 
 
+MASS_EPS = 2e-4   # retained-mass comparisons: allowance per query of the group (score rounding)
+
+
+def check_mass_group(slot, n, scores, mass, glen, cap, what):
+    """A group's kept keys under a retained-mass target: n keys (1 <= n <=
+    cap) that are a top-n set by the kept-key rule, and n is where the
+    oracle's scores, sorted, first reach mass * glen (within MASS_EPS * glen
+    either way: the GPU's float32 scores round differently), or the cap.
+    Returns (set equal to the oracle's top-n, n equal to the oracle's)."""
+    assert 1 <= n <= cap, f"{what}: count {n} outside [1, {cap}]"
+    gi = np.asarray(slot[:n])
+    exact = check_idx(gi, scores, n, len(scores), what)
+    srt = np.sort(np.asarray(scores, np.float64).astype(np.float32).astype(np.float64))[::-1]
+    prefix = np.cumsum(srt)
+    target, eps = mass * glen, MASS_EPS * glen
+    if n < cap:
+        assert prefix[n - 1] >= target - eps, f"{what}: {n} keys hold {prefix[n - 1]:.6f} < {target:.6f}"
+    assert n == 1 or prefix[n - 2] < target + eps, f"{what}: {n - 1} keys already hold {prefix[n - 2]:.6f}"
+    return exact, n == orc.mass_keep_count(scores, mass, glen, cap)
+
+
 def check_units(p: Problem, meta, od, outs, sc, heads, groups, label="", grouping="hash", kv_block=1,
-                residual=True):
+                residual=True, keep_mass=0.0):
     """Compares the sampled (head, group) units of a GPU run with the oracle:
-    perm of the whole head, kept keys, dense rows, residual and the reuse
-    outputs of every generated step.  Returns the number of kept-key sets
-    equal to the oracle's and the number checked."""
+    perm of the whole head, kept keys (and their number under a retained-mass
+    target), dense rows, residual and the reuse outputs of every generated
+    step.  Returns the number of kept-key sets equal to the oracle's and the
+    number checked."""
     exact = total = 0
+    counts = meta.count.cpu().numpy()
     for h in heads:
         q, k, v = p.heads_np[(h, 0)]
         perm_o = orc.select_head(q, k, v, p.proj(), p.G, int(p.keeps[h]), sc, groups=[], grouping=grouping,
@@ -163,13 +186,21 @@ def check_units(p: Problem, meta, od, outs, sc, heads, groups, label="", groupin
         kh = int(p.keeps[h])
         gidx = meta.head_idx(h, kh)
         ranges = orc.group_ranges(p.N, p.G)
+        if keep_mass == 0:
+            assert np.all(counts[h] == kh), f"{label} head {h}: group counts differ from the budget {kh}"
         for g in groups:
             s, e = ranges[g]
             rows = perm_o[s:e]
             rows_t = torch.from_numpy(rows.astype(np.int64)).to("cuda")
             sel = orc.select_group(q, k, v, rows, kh, sc, kv_block=kv_block, residual=residual)
             gi = gidx[g].cpu().numpy()
-            if kv_block == 1:
+            if keep_mass > 0:
+                n = int(counts[h, g])
+                same_set, _ = check_mass_group(gi, n, sel.scores, keep_mass, e - s, kh,
+                                               f"{label} head {h} group {g}")
+                exact += same_set
+                gi = gi[:n]
+            elif kv_block == 1:
                 exact += check_idx(gi, sel.scores, kh, p.N, f"{label} head {h} group {g}")
             else:
                 exact += check_blocks(gi, sel.scores, kh, p.N, kv_block, f"{label} head {h} group {g}")
@@ -179,6 +210,8 @@ def check_units(p: Problem, meta, od, outs, sc, heads, groups, label="", groupin
                              f"{label} head {h} group {g} dense rows")
             if residual:
                 res_c = sel.o_dense - orc.sparse_attention(q[rows], k, v, gi, sc)
+                if meta.meta.residual_dtype == 1:   # cached in bf16 (the oracle's rounding of the same difference)
+                    res_c = orc.round_bf16(res_c)
                 assert_close(to_np(meta.residual[h, s:e]), res_c, p.dtype, f"{label} head {h} group {g} residual",
                              ref_norm=np.linalg.norm(sel.o_dense))
             else:
@@ -242,14 +275,17 @@ def check_every_unit(p: Problem, meta, sc, outs, heads, label="", dense=(), dens
     perm_all = meta.perm.cpu().numpy()
     idx_all = meta.idx.cpu().numpy()
     starts = meta.idx_start.cpu().numpy()
-    res_all = meta.residual.cpu().numpy()
+    res_all = meta.residual.float().cpu().numpy()
     outs_h = {t: to_np(o) for t, o in outs.items()}
     dense_h = [(name, to_np(x)) for name, x in dense]
     ranges = orc.group_ranges(p.N, p.G)
 
+    counts = meta.count.cpu().numpy()
+
     def kept(h):
         kh = int(p.keeps[h])
-        return idx_all[starts[h]:starts[h] + p.ng * kh].reshape(p.ng, kh).astype(np.int64)
+        slots = idx_all[starts[h]:starts[h] + p.ng * kh].reshape(p.ng, kh).astype(np.int64)
+        return [slots[g, :counts[h, g]] for g in range(p.ng)]
 
     def head_job(h):
         kh = int(p.keeps[h])
@@ -257,8 +293,10 @@ def check_every_unit(p: Problem, meta, sc, outs, heads, label="", dense=(), dens
         perm_o = orc.select_head(q0, k0, v0, p.proj(), p.G, kh, sc, groups=[], grouping=grouping, grid=p.grid).perm
         assert np.array_equal(perm_all[h], perm_o), f"{label} head {h}: perm differs"
         gidx = kept(h)
-        assert np.all(np.diff(gidx, axis=1) > 0), f"{label} head {h}: kept keys not strictly ascending"
-        assert gidx.min() >= 0 and gidx.max() < p.N, f"{label} head {h}: kept key out of range"
+        assert np.all(counts[h] == kh), f"{label} head {h}: group counts differ from the budget {kh}"
+        for g, gi in enumerate(gidx):
+            assert np.all(np.diff(gi) > 0), f"{label} head {h} group {g}: kept keys not strictly ascending"
+            assert gi.min() >= 0 and gi.max() < p.N, f"{label} head {h} group {g}: kept key out of range"
         for t, o in outs_h.items():
             qt, kt, vt = p.heads_np[(h, t)]
             for g, (s, e) in enumerate(ranges):
@@ -289,6 +327,8 @@ def check_every_unit(p: Problem, meta, sc, outs, heads, label="", dense=(), dens
                 exact += check_idx(gidx[g], orc.group_scores(pr[a:b]), kh, p.N, f"{label} head {h} group {g}")
                 total += 1
                 res_c = o_d[a:b] - orc.sparse_attention(q0[rows[a:b]], k0, v0, gidx[g], sc)
+                if meta.meta.residual_dtype == 1:
+                    res_c = orc.round_bf16(res_c)
                 assert_close(res_all[h, ranges[g][0]:ranges[g][1]], res_c, p.dtype,
                              f"{label} head {h} group {g} residual", ref_norm=np.linalg.norm(o_d[a:b]))
     return exact, total

@@ -1,0 +1,146 @@
+"""GPU parity of the two extensions of the method against their oracle
+readings: the residual cached in bfloat16, and per-group keep budgets from a
+retained probability-mass target (the group counts live in the metadata's
+count region)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.mcs_oracle as orc
+from mcs_inputs import WORKLOADS
+from parity import (assert_close, build_problem, check_every_unit, check_mass_group, check_units, sample_groups,
+                    scale_for, to_np)
+
+pytestmark = pytest.mark.gpu
+
+mcs = pytest.importorskip("sparse_attention_diffusion_mcs_amd")
+
+SMALL = {
+    # name: (grid, H, d, G, keeps, drift, steps, wid)
+    "d128_g64_ragged": ((5, 8, 25), 2, 128, 64, [128, 100], 0.02, [1, 4], 121),
+    "d64_g128_keep1_keepN": ((4, 10, 30), 3, 64, 128, [64, 1200, 1], 0.02, [2], 122),
+    "d128_g128_ragged": ((3, 17, 21), 2, 128, 128, [333, 1071], 0.01, [1], 123),
+}
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_bf16_residual_every_group(name):
+    """Every group: the bf16 residual against the oracle's (dense minus
+    sparse on the GPU's kept keys, rounded to bf16), reuse on that residual,
+    the same kept keys and permutation as the float32-residual selection, and
+    metadata whose residual region is half as large."""
+    _need_gpu()
+    grid, H, d, G, keeps, drift, steps, wid = SMALL[name]
+    print(f"[ext] bf16 residual {name}: grid={grid} H={H} d={d} G={G} keeps={keeps}", flush=True)
+    p = build_problem(grid, H, d, "bf16", G, keeps, drift, steps, wid=wid)
+    sc = scale_for(d)
+    m32, _ = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc)
+    m16, od = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc, return_dense=True, residual_dtype="bf16")
+    outs = {t: mcs.sparse_attn(*p.dev[t], m16, scale=sc) for t in steps}
+    torch.cuda.synchronize()
+    assert m16.meta.residual_dtype == 1 and m16.residual.dtype == torch.bfloat16
+    assert m32.meta.bytes - m16.meta.bytes == H * p.N * d * 2
+    for region in ("perm", "count", "idx"):
+        assert torch.equal(getattr(m16, region), getattr(m32, region)), region
+    exact, total = check_units(p, m16, od, outs, sc, range(H), range(p.ng), f"bf16 residual {name}")
+    # the cached values are the bf16 rounding of the float32 residual
+    r16 = m16.residual.float().cpu().numpy()
+    r32 = orc.round_bf16(m32.residual.cpu().numpy())
+    assert np.max(np.abs(r16 - r32)) <= 2 ** -7 * max(np.max(np.abs(r32)), 1e-30)
+    print(f"[ext] {name}: {exact}/{total} kept-key sets equal to the oracle's", flush=True)
+
+
+def test_bf16_residual_workload2_every_unit():
+    """The full video layer with a bf16 residual: every unit's reuse output at
+    step 10 against the oracle on the GPU's own metadata, and one head's
+    residuals and dense rows in full."""
+    _need_gpu()
+    w = WORKLOADS[2]
+    print(f"[ext] bf16 residual, workload 2: H={w.heads} N={w.seq_len}", flush=True)
+    p = build_problem(w.grid, w.heads, w.head_dim, w.dtype, w.group, w.keeps(), w.drift, [10], wid=w.wid)
+    sc = scale_for(w.head_dim)
+    meta, od = mcs.select(*p.dev[0], w.group, p.keeps, p.proj(), scale=sc, return_dense=True, residual_dtype="bf16")
+    out = mcs.sparse_attn(*p.dev[10], meta, scale=sc)
+    torch.cuda.synchronize()
+    check_every_unit(p, meta, sc, {10: out}, range(w.heads), "bf16 residual workload 2",
+                     dense=[("selection dense output", od)], dense_heads=(0,))
+
+
+@pytest.mark.parametrize("mass", [0.5, 0.9, 0.99])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_mass_budget_every_group(name, mass):
+    """Every group: its count and kept keys under the retained-mass target
+    (the count where the sorted oracle scores reach the target, within the
+    score-rounding allowance, or the head's budget), then the residual and
+    reuse on those keys."""
+    _need_gpu()
+    grid, H, d, G, keeps, drift, steps, wid = SMALL[name]
+    print(f"[ext] mass {mass} {name}: grid={grid} H={H} d={d} G={G} caps={keeps}", flush=True)
+    p = build_problem(grid, H, d, "bf16", G, keeps, drift, steps, wid=wid)
+    sc = scale_for(d)
+    meta, od = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc, return_dense=True, keep_mass=mass)
+    outs = {t: mcs.sparse_attn(*p.dev[t], meta, scale=sc) for t in steps}
+    torch.cuda.synchronize()
+    exact, total = check_units(p, meta, od, outs, sc, range(H), range(p.ng), f"mass {mass} {name}", keep_mass=mass)
+    counts = meta.count.cpu().numpy()
+    print(f"[ext] mass {mass} {name}: {exact}/{total} kept-key sets equal to the oracle's; counts per head "
+          f"{[sorted(set(c.tolist()))[:6] for c in counts]}", flush=True)
+
+
+def test_mass_budget_workload2_sampled_groups():
+    """The full video layer with a 0.95 mass target capped at 25% of the keys:
+    sampled groups against the oracle, the counts of every group within the
+    cap, and counts that differ from group to group."""
+    _need_gpu()
+    w = WORKLOADS[2].with_(keep_frac=(0.25,))
+    print(f"[ext] mass 0.95, workload 2: H={w.heads} N={w.seq_len} cap={w.keeps()[0]}", flush=True)
+    p = build_problem(w.grid, w.heads, w.head_dim, w.dtype, w.group, w.keeps(), w.drift, [5], wid=w.wid,
+                      keep_heads={0, w.heads - 1})
+    sc = scale_for(w.head_dim)
+    meta, od = mcs.select(*p.dev[0], w.group, p.keeps, p.proj(), scale=sc, return_dense=True, keep_mass=0.95)
+    outs = {5: mcs.sparse_attn(*p.dev[5], meta, scale=sc)}
+    torch.cuda.synchronize()
+    counts = meta.count.cpu().numpy()
+    assert counts.min() >= 1 and counts.max() <= int(p.keeps[0])
+    assert len(np.unique(counts)) > 10
+    exact, total = check_units(p, meta, od, outs, sc, [0, w.heads - 1], sample_groups(p.ng), "mass 0.95 workload 2",
+                               keep_mass=0.95)
+    print(f"[ext] mass 0.95 workload 2: counts {counts.min()}..{counts.max()} (mean {counts.mean():.0f}); "
+          f"{exact}/{total} sampled sets equal to the oracle's", flush=True)
+
+
+def test_reuse_reads_the_count_region():
+    """Reuse on metadata laid out by mcs_meta_init with counts written by the
+    caller: each group attends over only its first count keys."""
+    _need_gpu()
+    grid, H, d, G, keep = (4, 6, 25), 2, 128, 64, 200
+    p = build_problem(grid, H, d, "bf16", G, [keep, keep], 0.02, [2], wid=124)
+    sc = scale_for(d)
+    meta = mcs.meta_init(p.dev[0][0], G, p.keeps)
+    torch.cuda.synchronize()
+    assert torch.equal(meta.count, torch.full((H, p.ng), keep, dtype=torch.int32, device="cuda"))
+    r = np.random.default_rng(3)
+    perm = np.stack([r.permutation(p.N) for _ in range(H)]).astype(np.int32)
+    counts = r.integers(1, keep + 1, size=(H, p.ng)).astype(np.int32)
+    slots = np.zeros((H, p.ng, keep), np.int32)
+    for h in range(H):
+        for g in range(p.ng):
+            slots[h, g, :counts[h, g]] = np.sort(r.choice(p.N, counts[h, g], replace=False))
+    resid = (0.05 * r.standard_normal((H, p.N, d))).astype(np.float32)
+    meta.perm.copy_(torch.from_numpy(perm))
+    meta.count.copy_(torch.from_numpy(counts))
+    meta.idx.copy_(torch.from_numpy(slots.reshape(-1)))
+    meta.residual.copy_(torch.from_numpy(resid))
+    out = to_np(mcs.sparse_attn(*p.dev[2], meta, scale=sc))
+    for h in range(H):
+        q, k, v = p.heads_np[(h, 2)]
+        for g, (s, e) in enumerate(orc.group_ranges(p.N, G)):
+            rows = perm[h, s:e]
+            ref = orc.reuse_group(q, k, v, rows, slots[h, g, :counts[h, g]], resid[h, s:e].astype(np.float64), sc)
+            assert_close(out[h, rows], ref, "bf16", f"head {h} group {g} (count {counts[h, g]})")

@@ -77,14 +77,25 @@ def test_meta_layout(lib):
     m = L.Meta()
     assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), G, kp, ctypes.byref(m)) == L.MCS_SUCCESS
     ng = -(-N // G)
-    assert (m.version, m.num_heads, m.seq_len, m.head_dim, m.group_size, m.num_groups) == (1, H, N, d, G, ng)
+    assert (m.version, m.num_heads, m.seq_len, m.head_dim, m.group_size, m.num_groups) == (2, H, N, d, G, ng)
     assert m.total_idx == ng * keep.sum() and m.max_keep == 1000 and m.base is None
-    offs = [m.off_perm, m.off_keep, m.off_idx_start, m.off_sched, m.off_idx, m.off_residual]
-    sizes = [H * N * 4, H * 4, H * 8, H * 4, m.total_idx * 4, H * N * d * 4]
+    assert m.residual_dtype == L.MCS_DTYPE_FP32 and m.reserved == 0
+    offs = [m.off_perm, m.off_keep, m.off_idx_start, m.off_sched, m.off_count, m.off_idx, m.off_residual]
+    sizes = [H * N * 4, H * 4, H * 8, H * 4, H * ng * 4, m.total_idx * 4, H * N * d * 4]
     assert all(o % 256 == 0 for o in offs)
     for (o, s), o2 in zip(zip(offs, sizes), offs[1:] + [m.bytes]):
         assert o + s <= o2
     assert lib.mcs_meta_bytes(ctypes.byref(_desc(H, N, d)), G, kp) == m.bytes
+    # a bf16 residual: the same regions, the residual region half as large
+    mb16 = L.Meta()
+    assert lib.mcs_meta_layout_ex(ctypes.byref(_desc(H, N, d)), G, kp, L.MCS_DTYPE_BF16,
+                                  ctypes.byref(mb16)) == L.MCS_SUCCESS
+    assert mb16.residual_dtype == L.MCS_DTYPE_BF16 and mb16.off_residual == m.off_residual
+    assert mb16.bytes == m.off_residual + H * N * d * 2
+    # bf16 residuals exist for bf16 problems only; other codes are refused
+    assert lib.mcs_meta_layout_ex(ctypes.byref(_desc(H, N, d, dt=0)), G, kp, L.MCS_DTYPE_BF16,
+                                  ctypes.byref(mb16)) == L.MCS_ERROR_INVALID_VALUE
+    assert lib.mcs_meta_layout_ex(ctypes.byref(_desc(H, N, d)), G, kp, 7, ctypes.byref(mb16)) == L.MCS_ERROR_INVALID_VALUE
     # invalid keep / group
     bad, bp = _i32([64, 0, 5])
     assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), G, bp, ctypes.byref(m)) == L.MCS_ERROR_INVALID_VALUE
@@ -105,6 +116,14 @@ def test_workspace_bytes(lib):
     assert lib.mcs_select_workspace_bytes(ctypes.byref(d), 64, 99) == lib.mcs_select_workspace_bytes(
         ctypes.byref(d), 64, 4)
     assert lib.mcs_select_workspace_bytes(ctypes.byref(d), 48, 1) == 0
+    # a bf16 residual adds each head's float32 dense output [N][d]
+    opts = L.SelectOptions(0, 1, 1, 0, 0, 0, L.MCS_DTYPE_BF16, 0.0, None, 0)
+    one16 = lib.mcs_select_workspace_bytes_ex(ctypes.byref(d), 64, 1, ctypes.byref(opts))
+    two16 = lib.mcs_select_workspace_bytes_ex(ctypes.byref(d), 64, 2, ctypes.byref(opts))
+    assert two16 - one16 == per + 1000 * 64 * 4 and one16 == one + 1000 * 64 * 4
+    assert lib.mcs_select_workspace_bytes_ex(ctypes.byref(d), 64, 1, None) == one
+    opts.residual_dtype = 5
+    assert lib.mcs_select_workspace_bytes_ex(ctypes.byref(d), 64, 1, ctypes.byref(opts)) == 0
 
 
 def test_select_validation(lib):
@@ -135,7 +154,7 @@ def test_select_validation(lib):
     m0 = L.Meta()
     D0 = ctypes.byref(_desc(0, N, d))
     assert sel(D0, NULL, NULL, NULL, 64, kp, pp, NULL, 0, NULL, 0, NULL, ctypes.byref(m0), NULL) == L.MCS_SUCCESS
-    assert m0.version == 1 and m0.num_heads == 0 and m0.bytes == 0
+    assert m0.version == L.MCS_META_VERSION == 2 and m0.num_heads == 0 and m0.bytes == 0
 
 
 def test_select_ex_options_validation(lib):
@@ -171,11 +190,20 @@ def test_select_ex_options_validation(lib):
     # tracing events: at most MCS_SELECT_PHASES, an array when any, no null handle
     evs = (ctypes.c_void_p * 6)(*([FAKE.value] * 6))
     ep = ctypes.cast(evs, ctypes.POINTER(ctypes.c_void_p))
-    assert call(O(0, 1, 1, 0, 0, 0, ep, L.MCS_SELECT_PHASES + 1)) == L.MCS_ERROR_INVALID_VALUE
-    assert call(O(0, 1, 1, 0, 0, 0, None, 1)) == L.MCS_ERROR_INVALID_VALUE
-    assert call(O(0, 1, 1, 0, 0, 0, ep, -1)) == L.MCS_ERROR_INVALID_VALUE
+    assert call(O(0, 1, 1, 0, 0, 0, 0, 0.0, ep, L.MCS_SELECT_PHASES + 1)) == L.MCS_ERROR_INVALID_VALUE
+    assert call(O(0, 1, 1, 0, 0, 0, 0, 0.0, None, 1)) == L.MCS_ERROR_INVALID_VALUE
+    assert call(O(0, 1, 1, 0, 0, 0, 0, 0.0, ep, -1)) == L.MCS_ERROR_INVALID_VALUE
     evs[1] = None
-    assert call(O(0, 1, 1, 0, 0, 0, ep, 2)) == L.MCS_ERROR_INVALID_VALUE
+    assert call(O(0, 1, 1, 0, 0, 0, 0, 0.0, ep, 2)) == L.MCS_ERROR_INVALID_VALUE
+    # extensions: residual dtype, retained-mass target in [0, 1] with single-token selection
+    assert call(O(0, 1, 1, 0, 0, 0, 3)) == L.MCS_ERROR_INVALID_VALUE
+    assert call(O(0, 1, 1, 0, 0, 0, 0, -0.5)) == L.MCS_ERROR_INVALID_VALUE
+    assert call(O(0, 1, 1, 0, 0, 0, 0, 1.5)) == L.MCS_ERROR_INVALID_VALUE
+    assert call(O(0, 1, 1, 0, 0, 0, 0, float("nan"))) == L.MCS_ERROR_INVALID_VALUE
+    d64 = ctypes.byref(_desc(H, 128, d))
+    assert call(O(1, 64, 1, 0, 0, 0, 0, 0.9), desc=d64) == L.MCS_ERROR_INVALID_VALUE
+    # bf16 residual of a float32 problem
+    assert call(O(0, 1, 1, 0, 0, 0, 1), desc=ctypes.byref(_desc(H, N, d, dt=0))) == L.MCS_ERROR_INVALID_VALUE
 
 
 def test_sparse_validation(lib):
@@ -188,8 +216,13 @@ def test_sparse_validation(lib):
     for bad in (_desc(H + 1, N, d), _desc(H, N + 1, d), _desc(H, N, 128), _desc(H, N, d, dt=0)):
         assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, ctypes.byref(m), FAKE, NULL) == L.MCS_ERROR_META_MISMATCH
     m2 = L.Meta.from_buffer_copy(m)
-    m2.version = 2
+    m2.version = 1
     assert f(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, ctypes.byref(m2), FAKE, NULL) == L.MCS_ERROR_META_MISMATCH
+    m5 = L.Meta.from_buffer_copy(m)
+    m5.residual_dtype = L.MCS_DTYPE_BF16   # the regions of an fp32 layout under a bf16 label
+    assert f(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, ctypes.byref(m5), FAKE, NULL) == L.MCS_ERROR_META_MISMATCH
+    m5.residual_dtype = 9
+    assert f(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, ctypes.byref(m5), FAKE, NULL) == L.MCS_ERROR_META_MISMATCH
     assert f(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, None, FAKE, NULL) == L.MCS_ERROR_INVALID_VALUE
     assert f(ctypes.byref(_desc(H, N, d)), FAKE, FAKE, FAKE, ctypes.byref(m), NULL, NULL) == L.MCS_ERROR_INVALID_VALUE
     m3 = L.Meta.from_buffer_copy(m)
@@ -235,7 +268,7 @@ def test_sparse_attn_rejects_edited_layouts(lib):
     good = L.Meta()
     assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), G, kp, ctypes.byref(good)) == L.MCS_SUCCESS
     for field, delta in (("off_residual", 256), ("off_idx", -256), ("off_perm", 256), ("bytes", 256),
-                         ("total_idx", 64), ("total_idx", -good.total_idx - 1)):
+                         ("off_count", 256), ("total_idx", 64), ("total_idx", -good.total_idx - 1)):
         m = L.Meta()
         ctypes.pointer(m)[0] = good
         m.base = FAKE

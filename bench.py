@@ -97,6 +97,10 @@ def parse():
                     help="add the failure-mode ablations (raster groups, 64-key blocks, no residual)")
     ap.add_argument("--sweep", action="store_true",
                     help="workload 5 only: add the keep x group denoising-loop sweep to the result")
+    ap.add_argument("--extensions", action="store_true",
+                    help="add the extensions: bf16 residual, retained-mass budgets against fixed budgets of the "
+                         "same mean size, and (with a re-selection interval, workload 5) the error-triggered "
+                         "re-selection policy against the fixed interval")
     return ap.parse_args()
 
 
@@ -314,6 +318,141 @@ def sweep(w, X, threads, scale, grouping, seed=0):
             del ws, mb, out, meta
             torch.cuda.empty_cache()
     return {"steps": S, "reselect_every": R, "dense_ms": round(dense_med, 4), "points": points}
+
+
+def _timed(stream, fn):
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    r = fn()
+    e1.record(stream)
+    return r, (e0, e1)
+
+
+def extensions(w, X, keeps, scale, grouping, seed):
+    """The method's extensions on the workload's inputs:
+    * bf16 residual: the segment (selection on step 0, reuse on steps 1..T)
+      with the residual cached in bfloat16 against the float32 one;
+    * retained-mass budgets: for each mass target (capped at 25% of the keys)
+      the segment's reuse time, the mean kept keys per group and the
+      per-step fidelity, next to a fixed budget of the same mean size;
+    * re-selection policy (a workload with a re-selection interval R over S
+      steps): the fixed interval against an error-triggered policy that
+      measures, after every reuse step, the relative L2 error of one probe
+      head against exact attention (one head's dense pass) and re-selects on
+      the next step when it exceeds a threshold.
+    Fidelity is the relative L2 error of each step's output against dense
+    attention on that step (computed outside the timed calls)."""
+    import torch
+
+    import sparse_attention_diffusion_mcs_amd as mcs
+    from mcs_inputs import keep_count
+
+    H, N, d, G, T = w.heads, w.seq_len, w.head_dim, w.group, w.reuse_steps
+    stream = torch.cuda.current_stream()
+    proj = hash_projections(seed, w.wid, d)
+    gkw = grouping_kw(w, grouping)
+    steps = sorted(X)
+    dense = {t: mcs.dense_attn(*X[t], scale=scale) for t in steps}
+    torch.cuda.synchronize()
+    out = torch.empty_like(X[0][0])
+    res = {}
+
+    def segment(keep_arr, **kw):
+        """Selection on step 0 and reuse on steps 1..T, each call timed."""
+        ws = torch.empty(mcs.workspace_bytes(X[0][0], G, residual_dtype=kw.get("residual_dtype", "fp32")),
+                         dtype=torch.uint8, device="cuda")
+        meta, _ = mcs.select(*X[0], G, keep_arr, proj, scale=scale, workspace=ws, **gkw, **kw)  # warm-up
+        torch.cuda.synchronize()
+        meta, sel_ev = _timed(stream, lambda: mcs.select(*X[0], G, keep_arr, proj, scale=scale, meta_buf=meta.buffer,
+                                                          workspace=ws, **gkw, **kw)[0])
+        ev, err = [], []
+        for t in range(1, T + 1):
+            _, e = _timed(stream, lambda t=t: mcs.sparse_attn(*X[t], meta, out=out, scale=scale))
+            ev.append(e)
+            err.append(rel_l2(out, dense[t]))
+        torch.cuda.synchronize()
+        counts = meta.count.float()
+        r = {"select_ms": round(sel_ev[0].elapsed_time(sel_ev[1]), 3),
+             "reuse_ms": round(float(np.mean([a.elapsed_time(b) for a, b in ev])), 4),
+             "mean_keys_per_group": round(float(counts.mean()), 1),
+             "keys_per_group_p10_p90": [int(torch.quantile(counts, 0.1)), int(torch.quantile(counts, 0.9))],
+             "meta_bytes": int(meta.nbytes),
+             "rel_l2_step1": round(err[0], 6), "rel_l2_mean": round(float(np.mean(err)), 6),
+             "rel_l2_final": round(err[-1], 6)}
+        del meta, ws
+        torch.cuda.empty_cache()
+        return r
+
+    log("extensions: float32 vs bf16 residual")
+    res["residual"] = {"fp32": segment(keeps), "bf16": segment(keeps, residual_dtype="bf16")}
+    log(f"extensions: {res['residual']}")
+
+    cap = np.full(H, keep_count(0.25, N), dtype=np.int32)
+    mass_rows = []
+    for mass in (0.9, 0.95, 0.98, 0.99):
+        r = segment(cap, keep_mass=mass)
+        kfix = int(max(64, round(r["mean_keys_per_group"] / 64) * 64))
+        f = segment(np.full(H, min(kfix, N), dtype=np.int32))
+        mass_rows.append({"mass": mass, "cap": int(cap[0]), "mass_budget": r, "fixed_budget_same_mean": f,
+                          "fixed_keep": kfix})
+        log(f"extensions: mass {mass}: {mass_rows[-1]}")
+    res["retained_mass_budgets"] = mass_rows
+
+    if w.reselect and len(steps) > w.reselect + 1:
+        S = len(steps)
+        ws = torch.empty(mcs.workspace_bytes(X[0][0], G), dtype=torch.uint8, device="cuda")
+        mb = torch.empty(int(mcs.meta_layout(H, N, d, 1, G, keeps).bytes), dtype=torch.uint8, device="cuda")
+        od = torch.empty_like(X[0][0])
+        probe_out = torch.empty_like(X[0][0][:1])
+        mcs.select(*X[0], G, keeps, proj, scale=scale, meta_buf=mb, workspace=ws, **gkw)  # warm-up
+        torch.cuda.synchronize()
+
+        def run(policy, arg):
+            total_ms, probe_ms, errs, selected = 0.0, 0.0, [], []
+            meta, pending = None, True
+            for t in range(S):
+                if pending or (policy == "interval" and t % arg == 0):
+                    meta, e = _timed(stream, lambda t=t: mcs.select(*X[t], G, keeps, proj, scale=scale, meta_buf=mb,
+                                                                     workspace=ws, dense_out=od, **gkw)[0])
+                    torch.cuda.synchronize()
+                    total_ms += e[0].elapsed_time(e[1])
+                    errs.append(rel_l2(od, dense[t]))
+                    selected.append(t)
+                    pending = False
+                    continue
+                _, e = _timed(stream, lambda t=t: mcs.sparse_attn(*X[t], meta, out=out, scale=scale))
+                if policy == "error":
+                    # the measured quantity: one probe head's error against exact attention
+                    _, e2 = _timed(stream, lambda t=t: mcs.dense_attn(X[t][0][:1], X[t][1][:1], X[t][2][:1],
+                                                                      out=probe_out, scale=scale))
+                    torch.cuda.synchronize()
+                    total_ms += e2[0].elapsed_time(e2[1])
+                    probe_ms += e2[0].elapsed_time(e2[1])
+                    pending = rel_l2(out[:1], probe_out) > arg
+                torch.cuda.synchronize()
+                total_ms += e[0].elapsed_time(e[1])
+                errs.append(rel_l2(out, dense[t]))
+            return {"policy": policy, "parameter": arg, "selections_at": selected, "n_selections": len(selected),
+                    "total_ms": round(total_ms, 3), "probe_ms": round(probe_ms, 3),
+                    "ms_per_step": round(total_ms / S, 4),
+                    "rel_l2_mean": round(float(np.mean(errs)), 6), "rel_l2_max": round(float(np.max(errs)), 6),
+                    "rel_l2_final": round(errs[-1], 6), "rel_l2_per_step": [round(x, 4) for x in errs]}
+
+        dense_ms = []
+        for t in steps[1:6]:
+            _, e = _timed(stream, lambda t=t: mcs.dense_attn(*X[t], out=out, scale=scale))
+            torch.cuda.synchronize()
+            dense_ms.append(e[0].elapsed_time(e[1]))
+        rows = [run("interval", r) for r in (5, w.reselect, 15)]
+        rows += [run("error", th) for th in (0.01, 0.02, 0.04)]
+        for r in rows:
+            r["speedup_vs_dense"] = round(float(np.median(dense_ms)) * S / r["total_ms"], 3)
+            log(f"extensions: policy {r}")
+        res["reselection_policy"] = {"steps": S, "dense_ms": round(float(np.median(dense_ms)), 4),
+                                     "probe": "head 0, relative L2 against its exact attention", "runs": rows}
+        del ws, mb
+    return res
 
 
 def ablations(base):
@@ -648,7 +787,7 @@ def main():
         print("--sweep needs a workload with a sweep (workload 5)", file=sys.stderr)
         sys.exit(2)
     t0 = time.time()
-    n_steps = max(T + 1, w.sweep["steps"] if args.sweep else 0)
+    n_steps = max(T + 1, w.sweep["steps"] if (args.sweep or (args.extensions and w.reselect)) else 0)
     X = generate(w, range(0, n_steps), args.threads, args.seed)
     torch.cuda.synchronize()
     if args.copy_probe:
@@ -713,6 +852,7 @@ def main():
 
     sweep_res = sweep(w, X, args.threads, scale, args.grouping, args.seed) if args.sweep else None
     ablation_res = ablation(w, X, keeps, scale, args.grouping, args.seed) if args.ablation else None
+    ext_res = extensions(w, X, keeps, scale, args.grouping, args.seed) if args.extensions else None
     peak_mem = int(torch.cuda.max_memory_allocated())
 
     achieved = flops_reuse / (reuse_mean * 1e-3) / 1e12
@@ -778,6 +918,8 @@ def main():
         result["sweep"] = sweep_res
     if ablation_res is not None:
         result["ablation"] = ablation_res
+    if ext_res is not None:
+        result["extensions"] = ext_res
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w, keeps, T, scale, args.cpu_groups, args.seed)

@@ -67,6 +67,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "reuse-step sparse attn ms + speedup vs dense; % bf16 MFMA peak (1 GPU)"
 ATTN_SRC = os.path.join(ROOT, "sparse_attention_diffusion_mcs_amd", "csrc", "attn_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_reuse_workload2.json")
+SELECT_SRC = os.path.join(ROOT, "sparse_attention_diffusion_mcs_amd", "csrc", "select.hip")
 
 
 def log(msg):
@@ -546,14 +547,20 @@ def traffic_summary(fetch_db, write_db, out, grouping):
     counter reads for the plain 1 GiB device copy of --copy-probe."""
     import sqlite3
 
-    def per_kernel(db):
+    def rows_of(db):
         cur = sqlite3.connect(db).cursor()
         cols = [c[1] for c in cur.execute("pragma table_info(counters_collection)")]
-        rows = [dict(zip(cols, r)) for r in cur.execute("select * from counters_collection")]
-        reuse = [r["value"] for r in rows if "attn_bf16_kernel<128, 2, 2, 32>" in r["kernel_name"]]
+        return [dict(zip(cols, r)) for r in cur.execute("select * from counters_collection")]
+
+    def per_kernel(db, name="attn_bf16_kernel<128, 2, 2, 32>"):
+        rows = rows_of(db)
+        reuse = [r["value"] for r in rows if name in r["kernel_name"]]
+        if not reuse:
+            reuse = [float("nan")]
         copies = [r for r in rows if "copy" in r["kernel_name"] and "bfloat16" not in r["kernel_name"]]
         cp = max(copies, key=lambda r: r["value"])
-        return float(np.mean(reuse)), len(reuse), float(cp["value"]), cp["kernel_name"][:80]
+        n = sum(1 for x in reuse if np.isfinite(x))
+        return float(np.mean(reuse)), n, float(cp["value"]), cp["kernel_name"][:80]
 
     f_reuse, n1, f_copy, cname = per_kernel(fetch_db)
     w_reuse, n2, w_copy, _ = per_kernel(write_db)
@@ -561,8 +568,23 @@ def traffic_summary(fetch_db, write_db, out, grouping):
     fs, ws = gib / 1024 / f_copy, gib / 1024 / w_copy
     H, N, d, ng, k = 24, 24960, 128, 390, 2496
     compulsory = 3 * H * N * d * 2 + H * N * d * 4 + H * ng * k * 4 + H * N * d * 2 + H * N * 4
+    # the selection's index-gather kernels from the same two runs, against
+    # their algorithmic bytes (score rows read once + kept indices written;
+    # Q read once + keys written; keys read + permutation written)
+    others = {}
+    for label, name, alg in (("topk", "group_topk_kernel", H * ng * N * 4 + H * ng * k * 4),
+                             ("hash", "hash_keys_kernel", H * N * d * 2 + H * N),
+                             ("sort", "perm_sort_kernel", H * N + H * N * 4)):
+        fk, nk, _, _ = per_kernel(fetch_db, name)
+        wk, _, _, _ = per_kernel(write_db, name)
+        if nk == 0 or not (np.isfinite(fk) and np.isfinite(wk)):
+            continue  # not in these runs (another grouping)
+        others[label] = {"kernel": name, "fetch_bytes": int(round(fk * 1024 * fs)),
+                         "write_bytes": int(round(wk * 1024 * ws)), "algorithmic_bytes": int(alg),
+                         "launches_averaged": nk}
     cmd = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c} -o pmc -- python3 bench.py --steps 1 --warmup 0 "
-           "--no-cpu-baseline --copy-probe --grouping " + grouping)
+           "--no-cpu-baseline --copy-probe --no-zcurve --no-cold-cache" +
+           ("" if grouping == "hash" else " --grouping " + grouping))
     res = {
         "kernel": "attn_bf16_kernel<128,2,REUSE,32> (reuse step)", "workload": 2, "grouping": grouping,
         "source_sha": src_hash(ATTN_SRC),
@@ -572,6 +594,7 @@ def traffic_summary(fetch_db, write_db, out, grouping):
         "bytes_per_launch": int(round(f_reuse * 1024 * fs + w_reuse * 1024 * ws)),
         "fetch_bytes": int(round(f_reuse * 1024 * fs)), "write_bytes": int(round(w_reuse * 1024 * ws)),
         "launches_averaged": min(n1, n2), "compulsory_bytes": compulsory,
+        "selection_kernels": others,
         "commands": [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE"),
                      f"python3 bench.py --traffic-summary {fetch_db} {write_db} {out} {grouping}"],
         "note": "FETCH_SIZE counts L2 misses served by the fabric (MALL or HBM); each counter is scaled by what it "
@@ -655,10 +678,11 @@ def counter_summary(out, *args):
          vals.get("SQ_LDS_BANK_CONFLICT", float("nan")) / vals.get("SQ_LDS_IDX_ACTIVE", float("nan"))),
     ]
     cmd = ("rocprofv3 --pmc {c} -d gpurun_out/cnt_{i} -o cnt -- python3 bench.py --steps 1 --warmup 0 "
-           "--no-cpu-baseline")
+           "--no-cpu-baseline --no-zcurve --no-cold-cache")
     what = "reuse launch" if kernel == REUSE_KERNEL else "launch"
+    src = ATTN_SRC if "attn_bf16" in kernel else SELECT_SRC
     lines = [f"# Counters of the workload-2 {what} (`{kernel}`)", "",
-             f"Source hash of `attn_bf16.hip`: `{src_hash(ATTN_SRC)}`. Mean over the launch's dispatches in each pass; "
+             f"Source hash of `{os.path.basename(src)}`: `{src_hash(src)}`. Mean over the launch's dispatches in each pass; "
              f"median dispatch time under counter collection {dur * 1e3:.3f} ms.", "", "Commands:", ""]
     lines += [f"- `{cmd.format(c=c, i=i + 1)}`" for i, c in enumerate(COUNTER_PASSES)]
     sel = "" if kernel == REUSE_KERNEL else f' --kernel "{kernel}"'

@@ -32,7 +32,11 @@
  *    into H.
  *  - All calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Results are valid once the stream reaches the call.  No call
- *    synchronises the device.  The device work of every call is kernel
+ *    synchronises the device, except in the debug mode: with the environment
+ *    variable MCS_DEBUG set to a value other than 0 when the library first
+ *    launches, every launch is followed by a synchronisation of the stream
+ *    and a status check, so that a fault is returned (MCS_ERROR_HIP) by the
+ *    call whose kernel caused it.  That mode is not for graph capture.  The device work of every call is kernel
  *    launches only (no allocation, memset or copy; host tables travel as
  *    kernel arguments), so a call can be captured in a HIP graph and
  *    replayed; a replay reads the buffers and host values of the capture.

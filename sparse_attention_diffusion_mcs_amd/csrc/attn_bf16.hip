@@ -587,7 +587,7 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_bf16_kernel<D, NW, MODE, tile_tokens<D>()>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
                      s, b);
-  return hipGetLastError();
+  return launched(s);
 }
 
 template <int D>

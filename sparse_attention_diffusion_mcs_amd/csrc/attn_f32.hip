@@ -156,7 +156,7 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   if (nblocks == 0) return hipSuccess;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_f32_kernel<D, MODE>), dim3((unsigned)nblocks), dim3(bm), 0, s, a);
-  return hipGetLastError();
+  return launched(s);
 }
 
 template <int D>

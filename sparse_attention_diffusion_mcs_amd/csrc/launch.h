@@ -76,4 +76,11 @@ hipError_t noalloc_scratch(void** out);
 // arguments (asynchronous on s, safe for pageable and stack host memory).
 hipError_t launch_fill_bytes(void* dst, const void* src, size_t nbytes, hipStream_t s);
 
+// Status of the launch just made on s: the launch error; with MCS_DEBUG set
+// to a value other than 0 in the environment, the stream is also synchronised
+// and a fault of the kernel is returned here, at the launch that caused it
+// (mcs_api.cpp; not for use under graph capture).
+hipError_t launched(hipStream_t s);
+bool debug_sync();
+
 }  // namespace mcs

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <numeric>
 #include <vector>
@@ -192,6 +193,25 @@ hipError_t launch_attn(int dtype, int mode, const mcs::AttnArgs& a, hipStream_t 
 }
 
 }  // namespace
+
+namespace mcs {
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("MCS_DEBUG");
+    return e && *e && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+hipError_t launched(hipStream_t s) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !debug_sync()) return e;
+  e = hipStreamSynchronize(s);
+  return e == hipSuccess ? hipGetLastError() : e;
+}
+
+}  // namespace mcs
 
 extern "C" {
 

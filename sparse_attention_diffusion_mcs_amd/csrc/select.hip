@@ -36,15 +36,18 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return
 // projection is exact in float64 and one fused multiply-add per term gives
 // the same sum.
 //
-// A workgroup hashes HT consecutive tokens (rows of the flattened [H*N]
-// queries).  The rows are first copied to LDS with 16-byte loads that
-// consecutive threads issue for consecutive addresses, then each thread sums
-// its own row in dimension order, 8 dimensions per 16-byte LDS read.  The
-// LDS rows are padded by 16 bytes: the row stride in 4-byte banks is then
-// odd in units of four banks, so the 16-byte reads of 32 lanes of different
-// rows fall into distinct bank groups.  The projections are read with uniform
-// addresses (scalar loads).
+// A workgroup hashes tiles of HT consecutive tokens (rows of the flattened
+// [H*N] queries), tile blockIdx.x, then every gridDim.x-th tile after it.  A
+// tile's rows are copied with 16-byte loads that consecutive threads issue
+// for consecutive addresses; the loads of the next tile go out into
+// registers before the current tile is hashed, so the copy overlaps the
+// float64 arithmetic.  Each thread sums its own row from LDS in dimension
+// order, 8 dimensions per 16-byte LDS read.  The LDS rows are padded by 16
+// bytes: the row stride in 4-byte banks is then odd in units of four banks,
+// so the 16-byte reads of 32 lanes of different rows fall into distinct bank
+// groups.  The projections are read with uniform addresses (scalar loads).
 constexpr int HT = 128;
+constexpr int HASH_BLOCKS_PER_CU = 4;
 
 template <typename T, int D, bool CENTRED>
 __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, const double* __restrict__ proj,
@@ -54,45 +57,76 @@ __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, 
   constexpr int STRIDE = ROWB + 16;          // padded LDS row
   constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
   constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
+  constexpr int LPT = CPR;                   // 16-byte loads per thread per tile (HT rows * CPR chunks / HT)
   __shared__ __attribute__((aligned(16))) unsigned char rows[HT * STRIDE];
-  const long long t0 = (long long)blockIdx.x * HT;
-  const int nrows = (int)min((long long)HT, total - t0);
-  const unsigned char* src = reinterpret_cast<const unsigned char*>(q + t0 * D);
-  for (int e = threadIdx.x; e < nrows * CPR; e += HT) {
-    const int r = e / CPR, c = e % CPR;
-    *reinterpret_cast<uint4*>(rows + r * STRIDE + 16 * c) = *reinterpret_cast<const uint4*>(src + 16 * e);
-  }
-  __syncthreads();
-  const int r = threadIdx.x;
-  if (r >= nrows) return;
-  const long long i = t0 + r;
-  const double* mu = CENTRED ? mean + (i / N) * D : nullptr;
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int c = 0; c < CPR; ++c) {
-    const uint4 u = *reinterpret_cast<const uint4*>(rows + r * STRIDE + 16 * c);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  const long long tiles = (total + HT - 1) / HT;
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(q);
+  // chunk e = threadIdx.x + HT * l of a tile: row e / CPR, chunk e % CPR;
+  // chunks past the last row of a ragged last tile load nothing (zeros)
+  uint4 buf[LPT];
+  long long tile = blockIdx.x;
+  if (tile < tiles) {
+    const int lim = (int)min((long long)HT, total - tile * HT) * CPR;
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      double x;
-      if constexpr (sizeof(T) == 2)
-        x = (double)bf16_to_f32((uint16_t)(w[e / 2] >> (16 * (e % 2))));
-      else
-        x = (double)__uint_as_float(w[e]);
-      const int dim = c * EPC + e;
-      if constexpr (CENTRED) {
-        const double xc = x - mu[dim];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) acc[b] = __dadd_rn(acc[b], __dmul_rn(xc, proj[b * D + dim]));
-      } else {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) acc[b] = __fma_rn(x, proj[b * D + dim], acc[b]);
-      }
+    for (int l = 0; l < LPT; ++l) {
+      const int e = threadIdx.x + HT * l;
+      buf[l] = e < lim ? *reinterpret_cast<const uint4*>(base + (size_t)tile * HT * ROWB + 16 * (size_t)e)
+                       : make_uint4(0, 0, 0, 0);
     }
   }
-  uint32_t key = 0;
+  for (; tile < tiles; tile += gridDim.x) {
+    const long long t0 = tile * HT;
+    const int nrows = (int)min((long long)HT, total - t0);
 #pragma unroll
-  for (int b = 0; b < 8; ++b) key |= (acc[b] > 0.0 ? 1u : 0u) << b;
-  keys[i] = (uint8_t)key;
+    for (int l = 0; l < LPT; ++l) {
+      const int e = threadIdx.x + HT * l;
+      if (e < nrows * CPR) *reinterpret_cast<uint4*>(rows + (e / CPR) * STRIDE + 16 * (e % CPR)) = buf[l];
+    }
+    __syncthreads();
+    const long long nxt = tile + gridDim.x;
+    if (nxt < tiles) {
+      const int lim = (int)min((long long)HT, total - nxt * HT) * CPR;
+#pragma unroll
+      for (int l = 0; l < LPT; ++l) {
+        const int e = threadIdx.x + HT * l;
+        buf[l] = e < lim ? *reinterpret_cast<const uint4*>(base + (size_t)nxt * HT * ROWB + 16 * (size_t)e)
+                         : make_uint4(0, 0, 0, 0);
+      }
+    }
+    const int r = threadIdx.x;
+    if (r < nrows) {
+      const long long i = t0 + r;
+      const double* mu = CENTRED ? mean + (i / N) * D : nullptr;
+      double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 4
+      for (int c = 0; c < CPR; ++c) {
+        const uint4 u = *reinterpret_cast<const uint4*>(rows + r * STRIDE + 16 * c);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          double x;
+          if constexpr (sizeof(T) == 2)
+            x = (double)bf16_to_f32((uint16_t)(w[e / 2] >> (16 * (e % 2))));
+          else
+            x = (double)__uint_as_float(w[e]);
+          const int dim = c * EPC + e;
+          if constexpr (CENTRED) {
+            const double xc = x - mu[dim];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) acc[b] = __dadd_rn(acc[b], __dmul_rn(xc, proj[b * D + dim]));
+          } else {
+#pragma unroll
+            for (int b = 0; b < 8; ++b) acc[b] = __fma_rn(x, proj[b * D + dim], acc[b]);
+          }
+        }
+      }
+      uint32_t key = 0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) key |= (acc[b] > 0.0 ? 1u : 0u) << b;
+      keys[i] = (uint8_t)key;
+    }
+    __syncthreads();  // the rows are rewritten by the next tile
+  }
 }
 
 // Per-dimension mean of each head's queries: one thread per (head, dim),
@@ -581,7 +615,10 @@ namespace {
 template <typename T, int D>
 void hash_launch(const void* q, const double* proj, const double* mean, uint8_t* keys, long long total, int N,
                  hipStream_t s) {
-  const dim3 grid((unsigned)((total + HT - 1) / HT));
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const long long tiles = (total + HT - 1) / HT;
+  const dim3 grid((unsigned)std::min<long long>(tiles, (long long)std::max(cus, 1) * HASH_BLOCKS_PER_CU));
   if (mean)
     hipLaunchKernelGGL((hash_keys_kernel<T, D, true>), grid, dim3(HT), 0, s, static_cast<const T*>(q), proj, mean,
                        keys, total, N);
@@ -606,7 +643,7 @@ hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, const 
     else
       hash_launch<float, 128>(q, proj, mean, keys, total, N, s);
   }
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_query_mean(const void* q, int dtype, double* mean, int H, int N, int D, hipStream_t s) {
@@ -626,13 +663,13 @@ hipError_t launch_query_mean(const void* q, int dtype, double* mean, int H, int 
       hipLaunchKernelGGL((query_mean_kernel<float, 128>), dim3(H), dim3(128), 0, s, static_cast<const float*>(q),
                          mean, N);
   }
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hipStream_t s) {
   if (H == 0 || N == 0) return hipSuccess;
   hipLaunchKernelGGL(perm_sort_kernel, dim3(H), dim3(SORT_NT), 0, s, keys, perm, N);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, int32_t* count, const int32_t* keep,
@@ -645,7 +682,7 @@ hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, int32_t
   else
     hipLaunchKernelGGL(group_topk_kernel<false>, dim3(ng, nheads), dim3(TK_NT), 0, s, colsum, ldc, idx, count, keep,
                        idx_start, head0, ng, N, G, nq, block, keep_mass);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_fill_counts(int32_t* count, const int32_t* keep, int H, int ng, hipStream_t s) {
@@ -653,7 +690,7 @@ hipError_t launch_fill_counts(int32_t* count, const int32_t* keep, int H, int ng
   if (total == 0) return hipSuccess;
   const long long blocks = std::min<long long>((total + 255) / 256, 65536);
   hipLaunchKernelGGL(fill_counts_kernel, dim3((unsigned)blocks), dim3(256), 0, s, count, keep, total, ng);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_block_scores(const float* colsum, int ldc, float* bs, int ldb, long long rows, int nb,
@@ -662,7 +699,7 @@ hipError_t launch_block_scores(const float* colsum, int ldc, float* bs, int ldb,
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(block_scores_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, colsum, ldc, bs,
                      ldb, rows, nb);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_iota_perm(int32_t* perm, int H, int N, hipStream_t s) {
@@ -670,20 +707,20 @@ hipError_t launch_iota_perm(int32_t* perm, int H, int N, hipStream_t s) {
   if (total == 0) return hipSuccess;
   const long long blocks = std::min<long long>((total + 255) / 256, 65536);
   hipLaunchKernelGGL(iota_perm_kernel, dim3((unsigned)blocks), dim3(256), 0, s, perm, total, N);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_morton_perm(int32_t* perm, int H, int N, int T, int Y, int X, hipStream_t s) {
   if (H == 0 || N == 0) return hipSuccess;
   hipLaunchKernelGGL(morton_perm_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, perm, H, N, T, Y, X);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_zero_floats(float* p, long long n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const long long blocks = std::min<long long>((n + 255) / 256, 65536);
   hipLaunchKernelGGL(zero_floats_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
-  return hipGetLastError();
+  return launched(s);
 }
 
 hipError_t launch_fill_bytes(void* dst, const void* src, size_t nbytes, hipStream_t s) {
@@ -697,7 +734,7 @@ hipError_t launch_fill_bytes(void* dst, const void* src, size_t nbytes, hipStrea
     __builtin_memcpy(p.w, in + done, chunk);
     hipLaunchKernelGGL(fill_words_kernel, dim3(1), dim3(256), 0, s, reinterpret_cast<uint32_t*>(out + done), p,
                        (int)(chunk / 4));
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launched(s);
     if (e != hipSuccess) return e;
     done += chunk;
   }

@@ -75,9 +75,10 @@ def test_traffic_summary_scales_by_the_copy_probe(tmp_path):
     b = _bench()
     reuse = f"void mcs::(anonymous namespace)::{b.REUSE_KERNEL}(mcs::AttnArgs)"
     copy = "__amd_rocclr_copyBuffer"
+    topk = "void mcs::(anonymous namespace)::group_topk_kernel<false>(float const*)"
     for name, reuse_kib, copy_kib in (("f.db", 1000.0, 524288.0), ("w.db", 300.0, 1048576.0)):
         _counter_db(str(tmp_path / name), [(reuse, "X", reuse_kib, 0, 1), (reuse, "X", reuse_kib, 2, 3),
-                                           (copy, "X", copy_kib, 4, 5)])
+                                           (copy, "X", copy_kib, 4, 5), (topk, "X", reuse_kib / 10, 6, 7)])
     out = tmp_path / "t.json"
     b.traffic_summary(str(tmp_path / "f.db"), str(tmp_path / "w.db"), str(out), "morton")
     import json
@@ -86,6 +87,10 @@ def test_traffic_summary_scales_by_the_copy_probe(tmp_path):
     assert res["fetch_bytes"] == 1000 * 1024 * 2 and res["write_bytes"] == 300 * 1024
     assert res["bytes_per_launch"] == res["fetch_bytes"] + res["write_bytes"]
     assert res["launches_averaged"] == 2 and res["source_sha"] == b.src_hash(b.ATTN_SRC)
+    # the selection's index-gather kernels present in the runs, scaled the same way
+    assert set(res["selection_kernels"]) == {"topk"}
+    assert res["selection_kernels"]["topk"]["fetch_bytes"] == 100 * 1024 * 2
+    assert res["selection_kernels"]["topk"]["write_bytes"] == 30 * 1024
 
 
 def test_trace_summary_tables(tmp_path):

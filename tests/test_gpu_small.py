@@ -163,6 +163,50 @@ def test_deterministic():
         assert torch.equal(a.contiguous().view(-1).view(torch.uint8), b.contiguous().view(-1).view(torch.uint8))
 
 
+_DEBUG_CHILD = """
+import sys, numpy as np, torch
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import sparse_attention_diffusion_mcs_amd as mcs
+from parity import build_problem, scale_for
+p = build_problem((4, 8, 20), 2, 64, "bf16", 128, [100, 300], 0.02, [1], wid=110)
+sc = scale_for(64)
+meta, od = mcs.select(*p.dev[0], 128, p.keeps, p.proj(), scale=sc, return_dense=True)
+out = mcs.sparse_attn(*p.dev[1], meta, scale=sc)
+dense = mcs.dense_attn(*p.dev[1], scale=sc)
+torch.cuda.synchronize()
+np.savez({path!r}, idx=meta.idx.cpu().numpy(), res=meta.residual.cpu().numpy(), od=od.float().cpu().numpy(),
+         out=out.float().cpu().numpy(), dense=dense.float().cpu().numpy())
+"""
+
+
+def test_debug_mode_gives_the_same_results(tmp_path):
+    """With MCS_DEBUG=1 (a synchronisation and status check after every
+    launch) a child process computes bit-identical metadata and outputs."""
+    import os
+    import subprocess
+    import sys
+
+    _need_gpu()
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = str(tmp_path / "debug.npz")
+    code = _DEBUG_CHILD.format(root=os.path.dirname(here), tests=here, path=path)
+    print("[case] MCS_DEBUG=1 child: select + reuse + dense", flush=True)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       env=dict(os.environ, MCS_DEBUG="1"))
+    assert r.returncode == 0, r.stderr[-3000:]
+    got = np.load(path)
+    p = build_problem((4, 8, 20), 2, 64, "bf16", 128, [100, 300], 0.02, [1], wid=110)
+    sc = scale_for(64)
+    meta, od = mcs.select(*p.dev[0], 128, p.keeps, p.proj(), scale=sc, return_dense=True)
+    out = mcs.sparse_attn(*p.dev[1], meta, scale=sc)
+    dense = mcs.dense_attn(*p.dev[1], scale=sc)
+    torch.cuda.synchronize()
+    want = dict(idx=meta.idx.cpu().numpy(), res=meta.residual.cpu().numpy(), od=od.float().cpu().numpy(),
+                out=out.float().cpu().numpy(), dense=dense.float().cpu().numpy())
+    for k, v in want.items():
+        assert np.array_equal(got[k], v), k
+
+
 def test_empty_problems():
     _need_gpu()
     for shape in [(0, 64, 64), (2, 0, 64)]:

@@ -277,11 +277,14 @@ def test_sparse_attn_rejects_edited_layouts(lib):
         assert st == L.MCS_ERROR_META_MISMATCH, (field, delta, st)
 
 
-def test_valid_call_without_a_device_reports_the_hip_error():
+@pytest.mark.parametrize("debug", ["0", "1"])
+def test_valid_call_without_a_device_reports_the_hip_error(debug):
     """On a host with no GPU a valid call passes validation, its launch fails
     and the call returns MCS_ERROR_HIP with the HIP code kept for
-    mcs_last_hip_error (hipErrorNoDevice).  Run in a child process; skipped
-    where a device exists, since the pointers are fake."""
+    mcs_last_hip_error (hipErrorNoDevice), also in the debug mode
+    (MCS_DEBUG=1) that synchronises after every launch.  Run in a child
+    process; skipped where a device exists, since the pointers are fake."""
+    import os
     import subprocess
     import sys
 
@@ -297,7 +300,8 @@ def test_valid_call_without_a_device_reports_the_hip_error():
         "f = ctypes.c_void_p(0x7f0000000000)\n"
         "st = lib.mcs_dense_attn(ctypes.byref(d), f, f, f, f, None)\n"
         "print(st, lib.mcs_last_hip_error())\n")
-    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       env=dict(os.environ, MCS_DEBUG=debug))
     assert r.returncode == 0, r.stderr[-2000:]
     st, err = (int(x) for x in r.stdout.split()[-2:])
     assert st == L.MCS_ERROR_HIP and err == 100

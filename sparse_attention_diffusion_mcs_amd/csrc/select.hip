@@ -98,7 +98,6 @@ __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, 
       const long long i = t0 + r;
       const double* mu = CENTRED ? mean + (i / N) * D : nullptr;
       double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
       for (int c = 0; c < CPR; ++c) {
         const uint4 u = *reinterpret_cast<const uint4*>(rows + r * STRIDE + 16 * c);
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};

@@ -144,3 +144,36 @@ def test_reuse_reads_the_count_region():
             rows = perm[h, s:e]
             ref = orc.reuse_group(q, k, v, rows, slots[h, g, :counts[h, g]], resid[h, s:e].astype(np.float64), sc)
             assert_close(out[h, rows], ref, "bf16", f"head {h} group {g} (count {counts[h, g]})")
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_bf16_residual_and_mass_budgets_other_workloads(wid):
+    """The 3D-asset layer (d = 64, G = 128, per-head budgets) and the
+    denoising-loop layer (ragged last group of 56 queries): a bf16 residual
+    and, on its own selection, a 0.95 retained-mass target capped by each
+    head's budget; sampled groups of the first and last heads (and, for the
+    asset layer, one head of every budget) against the oracle."""
+    _need_gpu()
+    w = WORKLOADS[wid]
+    keeps = w.keeps()
+    heads = sorted({0, w.heads - 1} | {int(np.nonzero(keeps == kv)[0][0]) for kv in np.unique(keeps)})
+    print(f"[ext] workload {wid}: H={w.heads} N={w.seq_len} d={w.head_dim} G={w.group} heads={heads}", flush=True)
+    p = build_problem(w.grid, w.heads, w.head_dim, w.dtype, w.group, keeps, w.drift, [1], wid=w.wid,
+                      keep_heads=set(heads))
+    sc = scale_for(w.head_dim)
+    groups = sample_groups(p.ng)
+    m16, od = mcs.select(*p.dev[0], w.group, p.keeps, p.proj(), scale=sc, return_dense=True, residual_dtype="bf16")
+    outs = {1: mcs.sparse_attn(*p.dev[1], m16, scale=sc)}
+    torch.cuda.synchronize()
+    assert m16.meta.residual_dtype == 1
+    exact, total = check_units(p, m16, od, outs, sc, heads, groups, f"bf16 residual workload {wid}")
+    print(f"[ext] workload {wid} bf16 residual: {exact}/{total} kept-key sets equal to the oracle's", flush=True)
+    del m16, outs
+    mm, od = mcs.select(*p.dev[0], w.group, p.keeps, p.proj(), scale=sc, return_dense=True, keep_mass=0.95)
+    outs = {1: mcs.sparse_attn(*p.dev[1], mm, scale=sc)}
+    torch.cuda.synchronize()
+    counts = mm.count.cpu().numpy()
+    assert np.all(counts >= 1) and np.all(counts <= keeps[:, None])
+    exact, total = check_units(p, mm, od, outs, sc, heads, groups, f"mass 0.95 workload {wid}", keep_mass=0.95)
+    print(f"[ext] workload {wid} mass 0.95: counts {counts.min()}..{counts.max()}; {exact}/{total} sets equal",
+          flush=True)

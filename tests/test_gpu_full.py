@@ -50,7 +50,7 @@ def test_workload2_video_layer():
 
 
 def test_workload2_zcurve_groups():
-    """The benchmark's grouping: Z-curve order over the 16 x 30 x 52 grid."""
+    """The secondary grouping the benchmark also times: Z-curve order over the 16 x 30 x 52 grid."""
     _need_gpu()
     w = WORKLOADS[2]
     run_workload(w, [1, 10], [0, w.heads - 1], "workload 2 z-curve", grouping="morton")

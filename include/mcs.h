@@ -148,9 +148,9 @@ int mcs_last_hip_error(void);
 
 /*
  * Exact dense attention, the method's selection-time computation and the
- * speed baseline every sparse speedup is measured against ("Relative to dense
- * attention", abstract of "MC-Sparse: Deconstructing and Closing the
- * Dense-Sparse Attention Gap in Diffusion Transformers").
+ * speed baseline every sparse speedup is measured against (the abstract of
+ * "MC-Sparse: Deconstructing and Closing the Dense-Sparse Attention Gap in
+ * Diffusion Transformers" states its speedups against dense attention).
  *   o[h][i] = sum_j softmax_j(scale * q[h][i] . k[h][j]) v[h][j]
  * q, k, v: [H][N][d] inputs; o: [H][N][d] output (must not alias the inputs).
  */

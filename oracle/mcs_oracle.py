@@ -54,8 +54,9 @@ Two extensions beyond the pages: a per-group keep budget from a retained
 probability-mass target (the fewest keys whose group scores reach a fraction
 of the group's mass, capped by the head's budget -- per-head budgets
 generalised, as the benchmark's 3D-asset workload draws them per head), and
-a residual cached in bfloat16 instead of float32 (half the cache, the
-"metadata cache per step" the pages count as MC-Sparse's extra cost).
+a residual cached in bfloat16 instead of float32 (half the cache; the
+per-step metadata cache is the extra cost the table "Three approaches at a
+glance" of "The quality cliff nobody admits to" charges to MC-Sparse).
 
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
@@ -156,7 +157,8 @@ def group_ranges(n: int, group: int):
 
 
 # ---------------------------------------------------------------------------
-# Exact attention ([ABS]: "exact attention probabilities").
+# Exact attention ([ABS]: the kept KV indices are chosen from the exact
+# softmax probabilities).
 # ---------------------------------------------------------------------------
 
 def softmax_rows(s: np.ndarray):

@@ -63,8 +63,8 @@
 extern "C" {
 #endif
 
-#define MCS_VERSION 2
-#define MCS_META_VERSION 2
+#define MCS_VERSION 3
+#define MCS_META_VERSION 3
 #define MCS_HASH_BITS 8
 #define MCS_MAX_SEQ_LEN (1 << 22)
 
@@ -107,6 +107,19 @@ typedef struct mcs_attn_desc {
  *                              reuse launches the costliest heads first
  *   count     int32 [H][ng]    keys kept by group g of head h, 1 <= count <= k_h
  *                              (k_h unless a retained-mass target chose fewer)
+ *   order     int32 [H][ng]    launch order of head h's groups in the sparse
+ *                              passes: work item t computes group order[h][t].
+ *                              Results do not depend on it, but it must be a
+ *                              permutation of [0, ng) (a group left out is not
+ *                              written).  For hash groups the selection
+ *                              writes the groups stably sorted by
+ *                              floor(m * 256 / N), m the group's median kept
+ *                              key (entry count / 2 of its ascending list), so
+ *                              that groups whose kept keys lie in the same part
+ *                              of the sequence run side by side and share the
+ *                              L2; raster and Z-curve groups, already in
+ *                              sequence order, and mcs_meta_init get
+ *                              0, 1, ..., ng - 1
  *   idx       int32 [total_idx] head h, group g: the slot of k_h indices at
  *                              idx[idx_start[h] + g*k_h ...]; its first count[h][g]
  *                              entries are the kept keys, ascending
@@ -133,6 +146,7 @@ typedef struct mcs_meta {
   uint64_t off_idx_start;
   uint64_t off_sched;
   uint64_t off_count;
+  uint64_t off_order;
   uint64_t off_idx;
   uint64_t off_residual;
 } mcs_meta;
@@ -209,8 +223,9 @@ size_t mcs_select_workspace_bytes_ex(const mcs_attn_desc* desc, int32_t group_si
 
 /*
  * Lays out metadata in meta_buf (device, 256-byte aligned, meta_bytes long)
- * and writes its keep, idx_start and sched regions; perm, idx and residual
- * are left for the caller to fill (to restore saved metadata or to supply
+ * and writes its keep, idx_start and sched regions, every group's count
+ * (k_h) and the launch order 0, 1, ..., ng - 1; perm, idx and residual are
+ * left for the caller to fill (to restore saved metadata or to supply
  * metadata built elsewhere).  *meta_out receives the descriptor.
  */
 mcs_status mcs_meta_init(const mcs_attn_desc* desc, int32_t group_size, const int32_t* keep_host,

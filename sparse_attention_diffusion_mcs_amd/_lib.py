@@ -18,9 +18,9 @@ MCS_ERROR_HIP = 6
 
 MCS_DTYPE_FP32 = 0
 MCS_DTYPE_BF16 = 1
-MCS_META_VERSION = 2
+MCS_META_VERSION = 3
 MCS_HASH_BITS = 8
-MCS_VERSION = 2
+MCS_VERSION = 3
 MCS_SELECT_PHASES = 5
 MCS_NOALLOC_SCRATCH_BYTES = 128 << 20
 MCS_MAX_SEQ_LEN = 1 << 22
@@ -48,7 +48,8 @@ class Meta(ctypes.Structure):
                 ("reserved", ctypes.c_int32), ("total_idx", ctypes.c_int64),
                 ("base", ctypes.c_void_p), ("bytes", ctypes.c_uint64), ("off_perm", ctypes.c_uint64),
                 ("off_keep", ctypes.c_uint64), ("off_idx_start", ctypes.c_uint64), ("off_sched", ctypes.c_uint64),
-                ("off_count", ctypes.c_uint64), ("off_idx", ctypes.c_uint64), ("off_residual", ctypes.c_uint64)]
+                ("off_count", ctypes.c_uint64), ("off_order", ctypes.c_uint64), ("off_idx", ctypes.c_uint64),
+                ("off_residual", ctypes.c_uint64)]
 
 
 class SelectOptions(ctypes.Structure):

@@ -87,7 +87,8 @@ class MetaCache:
 
     Region views (all on the device): perm int32 [H, N], keep int32 [H],
     idx_start int64 [H], sched int32 [H], count int32 [H, num_groups] (keys
-    kept per group), idx int32 [total_idx] (per group a slot of keep[h]
+    kept per group), order int32 [H, num_groups] (launch order of the groups
+    in the sparse passes), idx int32 [total_idx] (per group a slot of keep[h]
     indices, the first count[h, g] valid) and residual [H, N, d] (float32 or
     bfloat16, rows in group order)."""
 
@@ -139,6 +140,11 @@ class MetaCache:
     def count(self):
         m = self.meta
         return self._region(m.off_count, m.num_heads * m.num_groups, torch.int32, (m.num_heads, m.num_groups))
+
+    @property
+    def order(self):
+        m = self.meta
+        return self._region(m.off_order, m.num_heads * m.num_groups, torch.int32, (m.num_heads, m.num_groups))
 
     @property
     def idx(self):
@@ -204,8 +210,8 @@ def workspace_bytes(q, group_size, heads_per_chunk=None, residual_dtype="fp32") 
 
 def meta_init(q, group_size, keep, meta_buf=None, stream=None, residual_dtype="fp32") -> MetaCache:
     """Lays out an empty metadata buffer (keep/idx_start/sched written, every
-    group's count set to keep[h]; perm/idx/residual to be filled by the
-    caller) (mcs_meta_init_ex)."""
+    group's count set to keep[h], the launch order 0 .. num_groups-1;
+    perm/idx/residual to be filled by the caller) (mcs_meta_init_ex)."""
     if not isinstance(q, torch.Tensor) or not q.is_cuda:
         raise ValueError("q must be a device tensor")
     desc = desc_for(q)

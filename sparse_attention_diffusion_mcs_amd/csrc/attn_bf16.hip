@@ -120,8 +120,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   // the items in flight on an XCD share a key range of one head.
   const int kchunks = (MODE == MODE_SCORE && a.kchunks > 1) ? a.kchunks : 1;
   const int L = xcd_remap(blockIdx.x, a.nheads * tiles * kchunks, a.run);
-  const int hs = L / (tiles * kchunks), tile = L % tiles, kc = (L / tiles) % kchunks;
+  const int hs = L / (tiles * kchunks), wt = L % tiles, kc = (L / tiles) % kchunks;
   const int h = (MODE == MODE_REUSE) ? clamp_index(a.sched[hs], a.H) : a.head0 + hs;
+  // the sparse passes take a head's groups in the metadata's launch order
+  const int tile = (SPARSE && a.order) ? clamp_index(a.order[(size_t)h * a.ng + wt], a.ng) : wt;
   const int row0 = tile * BM;
   const size_t hoff = (size_t)h * N * D;
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + hoff;

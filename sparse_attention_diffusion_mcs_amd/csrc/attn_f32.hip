@@ -26,8 +26,10 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
   const int N = a.N;
   const int tiles = (MODE == MODE_PLAIN) ? (N + BM - 1) / BM : a.ng;
   const int L = xcd_remap(blockIdx.x, a.nheads * tiles, a.run);
-  const int hs = L / tiles, tile = L % tiles;
+  const int hs = L / tiles, wt = L % tiles;
   const int h = (MODE == MODE_REUSE) ? clamp_index(a.sched[hs], a.H) : a.head0 + hs;
+  // the sparse passes take a head's groups in the metadata's launch order
+  const int tile = (SPARSE && a.order) ? clamp_index(a.order[(size_t)h * a.ng + wt], a.ng) : wt;
   const size_t hoff = (size_t)h * N * D;
   const float* qh = static_cast<const float*>(a.q) + hoff;
   const float* kh = static_cast<const float*>(a.k) + hoff;

@@ -25,6 +25,7 @@ struct AttnArgs {
   float* odense;             // SELECT out, RESINIT in: float32 dense output [nheads][N][d] (sorted rows), when
                              // the residual is bf16 (else SELECT writes it into the float32 residual region)
   const int32_t* count;      // [H][ng] kept keys per group (REUSE, RESINIT)
+  const int32_t* order;      // [H][ng] launch order of the groups (REUSE, RESINIT; null: index order)
   float keep_mass;           // selection: retained-mass target (0: fixed budgets)
   float* colsum;             // SCORE: [nheads][ng][ldc] key scores of the launched heads
   float* lse;                // SELECT out, SCORE in: [nheads][N] log2-sum-exp of the sorted rows
@@ -61,6 +62,13 @@ hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, int32_t
                              float keep_mass, hipStream_t s);
 // count[h][g] = keep[h] for every group of every head (device tables)
 hipError_t launch_fill_counts(int32_t* count, const int32_t* keep, int H, int ng, hipStream_t s);
+// Launch order of the groups of heads head0 .. head0+nheads-1 for the sparse
+// passes: each group's sort key floor(m * 256 / N), m its median kept key
+// (entry count/2 of its ascending list), goes to bucket[h][g] (bytes,
+// [H][ng]); order[h] is then the stable order of the keys.
+hipError_t launch_group_order(const int32_t* idx, const int32_t* count, const int32_t* keep,
+                              const int64_t* idx_start, uint8_t* bucket, int32_t* order, int head0, int nheads, int ng,
+                              int N, long long total_idx, hipStream_t s);
 // ablation helpers: 64-key block scores of score rows, raster-order
 // permutation, zero fill (residual off)
 hipError_t launch_block_scores(const float* colsum, int ldc, float* bs, int ldb, long long rows, int nb,

@@ -77,6 +77,8 @@ void place_regions(const mcs_attn_desc* d, int32_t ng, int64_t total, int32_t re
   off = align_up(off + H * 4, kAlign);
   m->off_count = off;
   off = align_up(off + H * (uint64_t)ng * 4, kAlign);
+  m->off_order = off;
+  off = align_up(off + H * (uint64_t)ng * 4, kAlign);
   m->off_idx = off;
   off = align_up(off + (uint64_t)total * 4, kAlign);
   m->off_residual = off;
@@ -166,9 +168,12 @@ mcs_status upload_meta_tables(const mcs_meta* m, const int32_t* keep, hipStream_
     return hip_fail(e);
   if ((e = mcs::launch_fill_bytes(at<void>(m->base, m->off_sched), sched.data(), (size_t)H * 4, s)) != hipSuccess)
     return hip_fail(e);
-  // every group keeps k_h keys until a selection writes its own counts
+  // every group keeps k_h keys until a selection writes its own counts, and
+  // the groups run in index order until a selection writes its launch order
   if ((e = mcs::launch_fill_counts(at<int32_t>(m->base, m->off_count), at<int32_t>(m->base, m->off_keep), H,
                                    m->num_groups, s)) != hipSuccess)
+    return hip_fail(e);
+  if ((e = mcs::launch_iota_perm(at<int32_t>(m->base, m->off_order), H, m->num_groups, s)) != hipSuccess)
     return hip_fail(e);
   return MCS_SUCCESS;
 }
@@ -422,6 +427,7 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
   a.idx_start = at<int64_t>(meta_buf, m.off_idx_start);
   a.sched = at<int32_t>(meta_buf, m.off_sched);
   a.idx = at<int32_t>(meta_buf, m.off_idx);
+  a.order = at<int32_t>(meta_buf, m.off_order);
   a.G = G;
   a.ng = m.num_groups;
   a.total_idx = m.total_idx;
@@ -446,6 +452,12 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
                                    at<int32_t>(meta_buf, m.off_count), a.keep, a.idx_start, h0, a.nheads, a.ng, nb,
                                    G, N, o.kv_block, 0.f, s);
     }
+    // launch order of the chunk's hash groups for the sparse passes (the
+    // hash keys are no longer needed: their region holds the order's sort
+    // keys); raster and Z-curve groups keep their sequence order
+    if (e == hipSuccess && (o.grouping == MCS_GROUPING_HASH || o.grouping == MCS_GROUPING_CENTRED_HASH))
+      e = mcs::launch_group_order(a.idx, a.count, a.keep, a.idx_start, keys, at<int32_t>(meta_buf, m.off_order), h0,
+                                  a.nheads, a.ng, N, m.total_idx, s);
     if (e != hipSuccess || (e = mark(3)) != hipSuccess) return hip_fail(e);
     a.o = nullptr;
     if (o.residual)
@@ -498,7 +510,8 @@ mcs_status mcs_sparse_attn(const mcs_attn_desc* d, const void* q, const void* k,
   mcs_meta ref;
   place_regions(d, m->num_groups, m->total_idx, m->residual_dtype, &ref);
   if (m->off_perm != ref.off_perm || m->off_keep != ref.off_keep || m->off_idx_start != ref.off_idx_start ||
-      m->off_sched != ref.off_sched || m->off_count != ref.off_count || m->off_idx != ref.off_idx ||
+      m->off_sched != ref.off_sched || m->off_count != ref.off_count || m->off_order != ref.off_order ||
+      m->off_idx != ref.off_idx ||
       m->off_residual != ref.off_residual || m->bytes != ref.bytes)
     return MCS_ERROR_META_MISMATCH;
   if (empty(d)) return MCS_SUCCESS;
@@ -516,6 +529,7 @@ mcs_status mcs_sparse_attn(const mcs_attn_desc* d, const void* q, const void* k,
   a.idx_start = at<int64_t>(m->base, m->off_idx_start);
   a.sched = at<int32_t>(m->base, m->off_sched);
   a.idx = at<int32_t>(m->base, m->off_idx);
+  a.order = at<int32_t>(m->base, m->off_order);
   a.G = m->group_size;
   a.ng = m->num_groups;
   a.total_idx = m->total_idx;

@@ -625,6 +625,24 @@ void hash_launch(const void* q, const double* proj, const double* mean, uint8_t*
     hipLaunchKernelGGL((hash_keys_kernel<T, D, false>), grid, dim3(HT), 0, s, static_cast<const T*>(q), proj,
                        mean, keys, total, N);
 }
+// Sort key of each group's launch order: floor(m * 256 / N) for its median
+// kept key m (entry count/2 of the ascending list), one thread per group.
+__global__ __launch_bounds__(256) void group_bucket_kernel(const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ count,
+                                                           const int32_t* __restrict__ keep,
+                                                           const int64_t* __restrict__ idx_start,
+                                                           uint8_t* __restrict__ bucket, int head0, int nheads, int ng,
+                                                           int N, long long total_idx) {
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (long long)nheads * ng) return;
+  const int h = head0 + (int)(t / ng), g = (int)(t % ng);
+  long long start;
+  int n;
+  group_keys(keep, idx_start, count, h, g, N, ng, total_idx, &start, &n);
+  const int m = clamp_index(idx[start + n / 2], N);
+  bucket[(size_t)h * ng + g] = (uint8_t)(((long long)m * 256) / N);
+}
+
 }  // namespace
 
 hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, const double* mean, uint8_t* keys, int H,
@@ -681,6 +699,21 @@ hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, int32_t
   else
     hipLaunchKernelGGL(group_topk_kernel<false>, dim3(ng, nheads), dim3(TK_NT), 0, s, colsum, ldc, idx, count, keep,
                        idx_start, head0, ng, N, G, nq, block, keep_mass);
+  return launched(s);
+}
+
+hipError_t launch_group_order(const int32_t* idx, const int32_t* count, const int32_t* keep,
+                              const int64_t* idx_start, uint8_t* bucket, int32_t* order, int head0, int nheads, int ng,
+                              int N, long long total_idx, hipStream_t s) {
+  const long long total = (long long)nheads * ng;
+  if (total == 0 || N == 0) return hipSuccess;
+  hipLaunchKernelGGL(group_bucket_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, idx, count, keep,
+                     idx_start, bucket, head0, nheads, ng, N, total_idx);
+  const hipError_t e = launched(s);
+  if (e != hipSuccess) return e;
+  // the stable counting sort of the grouping, over ng keys per head
+  hipLaunchKernelGGL(perm_sort_kernel, dim3(nheads), dim3(SORT_NT), 0, s, bucket + (size_t)head0 * ng,
+                     order + (size_t)head0 * ng, ng);
   return launched(s);
 }
 

@@ -46,7 +46,9 @@ int main(void) {
   CHECK(m.max_keep == 100);
   CHECK(m.total_idx == 16 * (64 + 100 + 7));
   CHECK(m.base == NULL);
-  CHECK(m.off_perm % 256 == 0 && m.off_count % 256 == 0 && m.off_idx % 256 == 0 && m.off_residual % 256 == 0);
+  CHECK(m.off_perm % 256 == 0 && m.off_count % 256 == 0 && m.off_order % 256 == 0 && m.off_idx % 256 == 0 &&
+        m.off_residual % 256 == 0);
+  CHECK(m.off_order >= m.off_count + (uint64_t)3 * 16 * 4 && m.off_idx >= m.off_order + (uint64_t)3 * 16 * 4);
   CHECK(m.residual_dtype == MCS_DTYPE_FP32);
   end = m.off_residual + (uint64_t)3 * 1000 * 64 * 4; /* float32 residual [H][N][d] */
   CHECK(m.bytes >= end);

@@ -317,3 +317,57 @@ def test_binding_rejects_bad_buffers():
     with pytest.raises(ValueError):
         mcs.dense_attn(q, k.cpu(), v, scale=sc)
     torch.cuda.synchronize()
+
+
+def test_launch_order_region():
+    """The selection writes each head's hash groups in the launch order of
+    the sparse passes: a permutation of the groups, stably sorted by
+    floor(m * 256 / N) of each group's median kept key m; Z-curve groups and
+    metadata laid out by mcs_meta_init run in index order; and reuse on
+    metadata whose whole groups (perm rows, residual rows, kept keys) were
+    permuted, with a caller-written launch order, gives bit-identical
+    outputs."""
+    _need_gpu()
+    grid, H, d, G = (5, 8, 25), 3, 128, 64
+    keeps = [100, 333, 64]
+    print(f"[case] launch order: grid={grid} H={H} G={G} keeps={keeps}", flush=True)
+    p = build_problem(grid, H, d, "bf16", G, keeps, 0.02, [1], wid=130)
+    sc = scale_for(d)
+    meta, _ = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc)
+    out = mcs.sparse_attn(*p.dev[1], meta, scale=sc)
+    torch.cuda.synchronize()
+    ng, N = p.ng, p.N
+    order = meta.order.cpu().numpy()
+    counts = meta.count.cpu().numpy()
+    for h in range(H):
+        slots = meta.head_idx(h, keeps[h]).cpu().numpy()
+        med = np.array([slots[g, counts[h, g] // 2] for g in range(ng)], np.int64)
+        want = np.argsort((med * 256) // N, kind="stable")
+        assert np.array_equal(order[h], want), f"head {h}: launch order"
+    init = mcs.meta_init(p.dev[0][0], G, p.keeps)
+    zc, _ = mcs.select(*p.dev[0], G, p.keeps, p.proj(), scale=sc, grouping="morton", grid=grid)
+    torch.cuda.synchronize()
+    iota = np.tile(np.arange(ng, dtype=np.int32), (H, 1))
+    assert np.array_equal(init.order.cpu().numpy(), iota)
+    assert np.array_equal(zc.order.cpu().numpy(), iota)  # Z-curve groups keep their sequence order
+    # the same groups stored in another order, run in yet another order
+    r = np.random.default_rng(5)
+    moved = mcs.meta_init(p.dev[0][0], G, p.keeps)
+    full = ng - 1 if N % G else ng
+    for h in range(H):
+        pi = np.concatenate([r.permutation(full), np.arange(full, ng)])
+        k = keeps[h]
+        src_perm = meta.perm[h].cpu().numpy()
+        src_res = meta.residual[h].cpu().numpy()
+        src_slots = meta.head_idx(h, k).cpu().numpy()
+        dst_perm = src_perm.copy()
+        dst_res = src_res.copy()
+        dst_perm[:full * G] = src_perm[:full * G].reshape(full, G)[pi[:full]].reshape(-1)
+        dst_res[:full * G] = src_res[:full * G].reshape(full, G, d)[pi[:full]].reshape(-1, d)
+        moved.perm[h].copy_(torch.from_numpy(dst_perm))
+        moved.residual[h].copy_(torch.from_numpy(dst_res))
+        moved.head_idx(h, k).copy_(torch.from_numpy(src_slots[pi]))
+        moved.order[h].copy_(torch.from_numpy(r.permutation(ng).astype(np.int32)))
+    out2 = mcs.sparse_attn(*p.dev[1], moved, scale=sc)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mcs_version() == L.MCS_VERSION == 2
+    assert lib.mcs_version() == L.MCS_VERSION == 3
     assert lib.mcs_status_string(0) == b"MCS_SUCCESS"
     assert lib.mcs_status_string(6) == b"MCS_ERROR_HIP"
     assert lib.mcs_status_string(99) == b"MCS_UNKNOWN_STATUS"
@@ -77,11 +77,12 @@ def test_meta_layout(lib):
     m = L.Meta()
     assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), G, kp, ctypes.byref(m)) == L.MCS_SUCCESS
     ng = -(-N // G)
-    assert (m.version, m.num_heads, m.seq_len, m.head_dim, m.group_size, m.num_groups) == (2, H, N, d, G, ng)
+    assert (m.version, m.num_heads, m.seq_len, m.head_dim, m.group_size, m.num_groups) == (3, H, N, d, G, ng)
     assert m.total_idx == ng * keep.sum() and m.max_keep == 1000 and m.base is None
     assert m.residual_dtype == L.MCS_DTYPE_FP32 and m.reserved == 0
-    offs = [m.off_perm, m.off_keep, m.off_idx_start, m.off_sched, m.off_count, m.off_idx, m.off_residual]
-    sizes = [H * N * 4, H * 4, H * 8, H * 4, H * ng * 4, m.total_idx * 4, H * N * d * 4]
+    offs = [m.off_perm, m.off_keep, m.off_idx_start, m.off_sched, m.off_count, m.off_order, m.off_idx,
+            m.off_residual]
+    sizes = [H * N * 4, H * 4, H * 8, H * 4, H * ng * 4, H * ng * 4, m.total_idx * 4, H * N * d * 4]
     assert all(o % 256 == 0 for o in offs)
     for (o, s), o2 in zip(zip(offs, sizes), offs[1:] + [m.bytes]):
         assert o + s <= o2
@@ -154,7 +155,7 @@ def test_select_validation(lib):
     m0 = L.Meta()
     D0 = ctypes.byref(_desc(0, N, d))
     assert sel(D0, NULL, NULL, NULL, 64, kp, pp, NULL, 0, NULL, 0, NULL, ctypes.byref(m0), NULL) == L.MCS_SUCCESS
-    assert m0.version == L.MCS_META_VERSION == 2 and m0.num_heads == 0 and m0.bytes == 0
+    assert m0.version == L.MCS_META_VERSION == 3 and m0.num_heads == 0 and m0.bytes == 0
 
 
 def test_select_ex_options_validation(lib):
@@ -268,7 +269,8 @@ def test_sparse_attn_rejects_edited_layouts(lib):
     good = L.Meta()
     assert lib.mcs_meta_layout(ctypes.byref(_desc(H, N, d)), G, kp, ctypes.byref(good)) == L.MCS_SUCCESS
     for field, delta in (("off_residual", 256), ("off_idx", -256), ("off_perm", 256), ("bytes", 256),
-                         ("off_count", 256), ("total_idx", 64), ("total_idx", -good.total_idx - 1)):
+                         ("off_count", 256), ("off_order", 256), ("total_idx", 64),
+                         ("total_idx", -good.total_idx - 1)):
         m = L.Meta()
         ctypes.pointer(m)[0] = good
         m.base = FAKE

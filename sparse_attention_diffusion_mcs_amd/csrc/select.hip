@@ -219,9 +219,14 @@ __global__ __launch_bounds__(SORT_NT) void perm_sort_kernel(const uint8_t* __res
 // (k - #greater) indices with score == T, in ascending index order.  When
 // the first pass's bin of T holds at most TK_CAP scores, a second read copies
 // them into LDS and the last two passes run there: three reads of the row
-// instead of four.
+// instead of four.  When the bin holds at most TK_CAP / 2 scores and the row
+// at most TK_MASK_KEYS keys, the second read is also the last: it sets one
+// LDS bit per key above the bin and keeps the bin's (score, index) pairs;
+// once T is known the bin's winners join the bits, and the ordered output
+// comes from the bits: two reads of the row.
 constexpr int TK_NT = 256;
 constexpr int TK_CAP = 4096;
+constexpr int TK_MASK_KEYS = 1 << 17;  // longest row of the mask path (16 KB of LDS)
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = __lane_id();
@@ -389,9 +394,16 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
                                                            int32_t* __restrict__ idx, int32_t* __restrict__ count,
                                                            const int32_t* __restrict__ keep,
                                                            const int64_t* __restrict__ idx_start, int head0, int ng,
-                                                           int N, int G, int nq, int block, float keep_mass) {
+                                                           int N, int G, int nq, int block, float keep_mass,
+                                                           int mask_words) {
   __shared__ int hist[2048];
-  __shared__ uint32_t cand[TK_CAP];
+  // candidates of the first pass's bin: TK_CAP scores, or (mask path) up
+  // to TK_CAP / 2 (score, index) pairs
+  __shared__ unsigned long long cand64[TK_CAP / 2];
+  uint32_t* cand = reinterpret_cast<uint32_t*>(cand64);
+  // one bit per key of the row (dynamic, mask_words words; 0 if the row is
+  // too long for the mask path)
+  extern __shared__ uint32_t mask[];
   __shared__ unsigned long long hsum[MASS ? 2048 : 1];
   __shared__ unsigned long long shq[TK_NT / 64 + 1];
   __shared__ int sh[8];
@@ -409,7 +421,7 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
   // Reads the row 16 consecutive scores per thread and step (four 16-byte
   // loads in flight; rows start 256-byte aligned) and hands each in-range
   // score to f.
-  auto scan_row = [&](auto f) {
+  auto scan_row = [&](auto f) {  // f(score bits, key index)
     for (int j0 = 16 * tid; j0 < N; j0 += 16 * TK_NT) {
       uint32_t u[16];
       if (j0 + 16 <= N) {
@@ -427,21 +439,22 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        if (j0 + e < N) f(u[e]);
+        if (j0 + e < N) f(u[e], j0 + e);
     }
   };
-  bool in_lds = false;
+  bool in_lds = false, mask_mode = false;
   int ncand = 0;
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = pass == 2 ? 1024 : 2048;
     for (int b = tid; b < 2048; b += TK_NT) hist[b] = 0;
     __syncthreads();
-    auto count = [&](uint32_t x) {
+    auto count = [&](uint32_t x, int) {
       if ((x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & (nb - 1)], 1);
     };
     if (in_lds) {
-      for (int c = tid; c < ncand; c += TK_NT) count(cand[c]);
+      for (int c = tid; c < ncand; c += TK_NT)
+        count(mask_mode ? (uint32_t)(cand64[c] >> 32) : cand[c], 0);
     } else {
       scan_row(count);
     }
@@ -471,11 +484,26 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
     krem -= found[1];
     const int in_bin = found[2];
     __syncthreads();
-    if (pass == 0 && in_bin <= TK_CAP) {
+    if (pass == 0 && in_bin <= TK_CAP / 2 && N <= 32 * mask_words) {
+      // second (and last) read of the row: the keys above T's bin are kept,
+      // one bit each; the (score, index) pairs of the bin go to LDS
+      for (int wd = tid; wd < mask_words; wd += TK_NT) mask[wd] = 0u;
+      if (tid == 0) sh[0] = 0;
+      __syncthreads();
+      scan_row([&](uint32_t x, int j) {
+        if ((x & pmask) > prefix)
+          atomicOr(&mask[j >> 5], 1u << (j & 31));
+        else if ((x & pmask) == prefix)
+          cand64[atomicAdd(&sh[0], 1)] = ((unsigned long long)x << 32) | (uint32_t)j;
+      });
+      __syncthreads();
+      ncand = in_bin;
+      in_lds = mask_mode = true;
+    } else if (pass == 0 && in_bin <= TK_CAP) {
       // second read: the scores in T's bin, to LDS (exactly in_bin of them)
       if (tid == 0) sh[0] = 0;
       __syncthreads();
-      scan_row([&](uint32_t x) {
+      scan_row([&](uint32_t x, int) {
         if ((x & pmask) == prefix) cand[atomicAdd(&sh[0], 1)] = x;
       });
       __syncthreads();
@@ -484,6 +512,55 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
     }
   }
   const uint32_t T = prefix;
+
+  if (mask_mode) {
+    // the bin's winners join the mask: scores above T, and of the scores
+    // equal to T the krem with the lowest indices
+    for (int c = tid; c < ncand; c += TK_NT) {
+      const unsigned long long e = cand64[c];
+      const uint32_t x = (uint32_t)(e >> 32);
+      const int j = (int)(uint32_t)e;
+      bool win = x > T;
+      if (x == T) {
+        int rank = 0;
+        for (int c2 = 0; c2 < ncand; ++c2) {
+          const unsigned long long e2 = cand64[c2];
+          rank += ((uint32_t)(e2 >> 32) == T && (int)(uint32_t)e2 < j);
+        }
+        win = rank < krem;
+      }
+      if (win) atomicOr(&mask[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    // ordered compaction of the mask: thread t owns words [t*wpt, (t+1)*wpt)
+    const int nwords = (N + 31) / 32;
+    const int wpt = (nwords + TK_NT - 1) / TK_NT;
+    int mine = 0;
+    for (int i = 0; i < wpt; ++i) {
+      const int wd = tid * wpt + i;
+      if (wd < nwords) mine += __popc(mask[wd]);
+    }
+    int excl, unused_e, total, unused_t;
+    block_excl_scan2(mine, 0, &excl, &unused_e, &total, &unused_t, sh);
+    int pos = excl;
+    for (int i = 0; i < wpt; ++i) {
+      const int wd = tid * wpt + i;
+      if (wd >= nwords) break;
+      uint32_t bits = mask[wd];
+      while (bits) {
+        const int j = 32 * wd + __ffs(bits) - 1;
+        bits &= bits - 1;
+        if (pos < k) {
+          if (block == 1)
+            out[pos] = j;
+          else
+            for (int t = 0; t < block; ++t) out[(int64_t)pos * block + t] = j * block + t;
+        }
+        ++pos;
+      }
+    }
+    return;
+  }
 
   // ordered compaction, 4 consecutive elements per thread per step
   int gt_base = 0, eq_base = 0;
@@ -693,12 +770,16 @@ hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, int32_t
                              const int64_t* idx_start, int head0, int nheads, int ng, int N, int G, int nq, int block,
                              float keep_mass, hipStream_t s) {
   if (nheads == 0 || ng == 0) return hipSuccess;
+  // the mask path of the top-k holds one bit per key in LDS (rows up to
+  // TK_MASK_KEYS keys); longer rows take the three-read path
+  const int mask_words = N <= TK_MASK_KEYS ? (N + 31) / 32 : 0;
+  const size_t lds = (size_t)mask_words * 4;
   if (keep_mass > 0.f)
-    hipLaunchKernelGGL(group_topk_kernel<true>, dim3(ng, nheads), dim3(TK_NT), 0, s, colsum, ldc, idx, count, keep,
-                       idx_start, head0, ng, N, G, nq, block, keep_mass);
+    hipLaunchKernelGGL(group_topk_kernel<true>, dim3(ng, nheads), dim3(TK_NT), lds, s, colsum, ldc, idx, count, keep,
+                       idx_start, head0, ng, N, G, nq, block, keep_mass, mask_words);
   else
-    hipLaunchKernelGGL(group_topk_kernel<false>, dim3(ng, nheads), dim3(TK_NT), 0, s, colsum, ldc, idx, count, keep,
-                       idx_start, head0, ng, N, G, nq, block, keep_mass);
+    hipLaunchKernelGGL(group_topk_kernel<false>, dim3(ng, nheads), dim3(TK_NT), lds, s, colsum, ldc, idx, count, keep,
+                       idx_start, head0, ng, N, G, nq, block, keep_mass, mask_words);
   return launched(s);
 }
 

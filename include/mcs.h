@@ -172,6 +172,29 @@ mcs_status mcs_dense_attn(const mcs_attn_desc* desc, const void* q, const void* 
                           void* o, void* stream);
 
 /*
+ * The selection's per-group top-k on caller score rows (the "Individual KV
+ * selection" item of "MC-Sparse Narrows the Dense-Sparse Attention Gap in
+ * Diffusion Transformers": each group keeps the single KV tokens with the
+ * highest scores; mcs_select runs the same kernel on the group key scores it
+ * computes).  For each row r < rows of n float32 scores at scores + r * ld,
+ * writes the indices of its k largest scores, ties to the lower index, in
+ * ascending order to idx[r * k .. r * k + k - 1].  Scores are ranked by their
+ * bit patterns as unsigned integers, which is the value order for
+ * non-negative floats (the selection's scores are sums of probabilities);
+ * other patterns give k distinct indices in that order.  The result is exact
+ * for every input: it does not depend on how the rows are read.
+ *   scores  device, 16-byte aligned; ld a multiple of 4 with n <= ld; the
+ *           buffer holds (rows - 1) * ld + n floats rounded up to a multiple
+ *           of 4 (the kernel reads whole 16-byte chunks)
+ *   idx     device int32 [rows][k], 4-byte aligned, must not alias scores
+ *   n in [1, MCS_MAX_SEQ_LEN], k in [1, n], rows in [0, 2^31 - 1]
+ * Errors: MCS_ERROR_INVALID_VALUE for a size or stride outside these
+ * ranges or a NULL buffer, MCS_ERROR_MISALIGNED for misaligned buffers.
+ */
+mcs_status mcs_topk_rows(const float* scores, int64_t ld, int64_t rows, int32_t n, int32_t k, int32_t* idx,
+                         void* stream);
+
+/*
  * Host-only: computes the metadata layout (the cached query groups, kept KV
  * indices and residual that the abstract of "MC-Sparse: Deconstructing and
  * Closing the Dense-Sparse Attention Gap in Diffusion Transformers" names)

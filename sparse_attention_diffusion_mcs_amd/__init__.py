@@ -9,4 +9,5 @@ fallback implementation.
 """
 
 from ._lib import LIB_PATH, McsError, lib  # noqa: F401
-from .api import MetaCache, dense_attn, desc_for, meta_init, meta_layout, select, sparse_attn, workspace_bytes  # noqa: F401
+from .api import (MetaCache, dense_attn, desc_for, meta_init, meta_layout, select, sparse_attn,  # noqa: F401
+                  topk_rows, workspace_bytes)

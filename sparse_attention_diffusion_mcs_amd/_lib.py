@@ -33,7 +33,7 @@ MCS_GROUPING_MORTON = 3
 EXPORTS = ("mcs_version", "mcs_status_string", "mcs_last_hip_error", "mcs_dense_attn", "mcs_meta_layout",
            "mcs_meta_bytes", "mcs_select_workspace_bytes", "mcs_meta_init", "mcs_select", "mcs_select_ex",
            "mcs_sparse_attn", "mcs_select_noalloc", "mcs_meta_layout_ex", "mcs_meta_init_ex",
-           "mcs_select_workspace_bytes_ex")
+           "mcs_select_workspace_bytes_ex", "mcs_topk_rows")
 
 
 class AttnDesc(ctypes.Structure):
@@ -121,6 +121,9 @@ def open_library(path):
     lib.mcs_select_noalloc.restype = ctypes.c_int
     lib.mcs_select_noalloc.argtypes = [DP, P, P, P, ctypes.c_int32, I32P, F32P, ctypes.POINTER(SelectOptions), P,
                                        ctypes.c_size_t, P, MP, P]
+    lib.mcs_topk_rows.restype = ctypes.c_int
+    lib.mcs_topk_rows.argtypes = [F32P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_void_p, P]
     lib.mcs_sparse_attn.restype = ctypes.c_int
     lib.mcs_sparse_attn.argtypes = [DP, P, P, P, MP, P, P]
     return lib

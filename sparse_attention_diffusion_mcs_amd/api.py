@@ -183,6 +183,33 @@ def dense_attn(q, k, v, out=None, scale=None, stream=None):
     return out
 
 
+def topk_rows(scores, k, out=None, stream=None):
+    """The selection's top-k on caller score rows (mcs_topk_rows): for each
+    row of the float32 [rows, n] CUDA tensor `scores` (unit column stride,
+    row stride a multiple of 4), the ascending indices of its k largest
+    scores, ties to the lower index, as int32 [rows, k]."""
+    if not isinstance(scores, torch.Tensor) or scores.dtype != torch.float32 or scores.dim() != 2:
+        raise TypeError("scores must be a float32 tensor [rows, n]")
+    if not scores.is_cuda or scores.stride(1) != 1:
+        raise ValueError("scores must be a CUDA tensor with unit column stride")
+    rows, n = scores.shape
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    if out.dtype != torch.int32 or tuple(out.shape) != (rows, k) or not out.is_contiguous() or \
+            out.device != scores.device:
+        raise ValueError(f"out must be a contiguous int32 [{rows}, {k}] tensor on {scores.device}")
+    ld = scores.stride(0)
+    need = (scores.storage_offset() + (rows - 1) * ld + -(-n // 4) * 4) * 4
+    if rows and (ld % 4 or ld < n or need > scores.untyped_storage().nbytes()):
+        raise ValueError("scores needs a row stride that is a multiple of 4 and at least n, and storage for the "
+                         "last row's n scores rounded up to 4")
+    st = _stream(stream, scores.device)
+    fp = ctypes.cast(ctypes.c_void_p(scores.data_ptr()), ctypes.POINTER(ctypes.c_float))
+    with torch.cuda.device(scores.device):
+        L.check(L.lib().mcs_topk_rows(fp, ld, rows, n, k, _ptr(out), st), "mcs_topk_rows")
+    return out
+
+
 _RESIDUAL_DTYPES = {"fp32": L.MCS_DTYPE_FP32, "bf16": L.MCS_DTYPE_BF16}
 
 

@@ -60,6 +60,10 @@ hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hi
 hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, int32_t* count, const int32_t* keep,
                              const int64_t* idx_start, int head0, int nheads, int ng, int N, int G, int nq, int block,
                              float keep_mass, hipStream_t s);
+// Top-k of `rows` plain score rows (row r at scores + r * ld, n scores; ld a
+// multiple of 4, at least n): the k largest of each row, ties to the lower
+// index, written ascending to idx + r * k.
+hipError_t launch_topk_rows(const float* scores, int ld, int rows, int n, int k, int32_t* idx, hipStream_t s);
 // count[h][g] = keep[h] for every group of every head (device tables)
 hipError_t launch_fill_counts(int32_t* count, const int32_t* keep, int H, int ng, hipStream_t s);
 // Launch order of the groups of heads head0 .. head0+nheads-1 for the sparse

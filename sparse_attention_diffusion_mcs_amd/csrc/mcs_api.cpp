@@ -250,6 +250,19 @@ mcs_status mcs_dense_attn(const mcs_attn_desc* d, const void* q, const void* k, 
   return e == hipSuccess ? MCS_SUCCESS : hip_fail(e);
 }
 
+mcs_status mcs_topk_rows(const float* scores, int64_t ld, int64_t rows, int32_t n, int32_t k, int32_t* idx,
+                         void* stream) {
+  if (rows < 0 || rows > INT32_MAX || n < 1 || n > MCS_MAX_SEQ_LEN || k < 1 || k > n) return MCS_ERROR_INVALID_VALUE;
+  if (ld < n || ld % 4 != 0 || ld > INT32_MAX) return MCS_ERROR_INVALID_VALUE;
+  if (rows == 0) return MCS_SUCCESS;
+  mcs_status st;
+  if ((st = check_tensor(scores)) != MCS_SUCCESS) return st;
+  if (!idx) return MCS_ERROR_INVALID_VALUE;
+  if (!aligned(idx, 4)) return MCS_ERROR_MISALIGNED;
+  const hipError_t e = mcs::launch_topk_rows(scores, (int)ld, (int)rows, n, k, idx, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MCS_SUCCESS : hip_fail(e);
+}
+
 mcs_status mcs_meta_layout_ex(const mcs_attn_desc* d, int32_t G, const int32_t* keep, int32_t residual_dtype,
                               mcs_meta* layout) {
   mcs_status st;

@@ -213,28 +213,53 @@ __global__ __launch_bounds__(SORT_NT) void perm_sort_kernel(const uint8_t* __res
 
 // ---------------------------------------------------------------- top-k ----
 // One workgroup per (head, group) score row.  Scores are non-negative floats,
-// so their bit patterns order like the values.  Three histogram passes over
-// bits [31:21], [20:10], [9:0] find the k-th largest pattern T exactly; a
-// final ordered pass writes every index with score > T and the lowest-index
-// (k - #greater) indices with score == T, in ascending index order.  When
-// the first pass's bin of T holds at most TK_CAP scores, a second read copies
-// them into LDS and the last two passes run there: three reads of the row
-// instead of four.  When the bin holds at most TK_CAP / 2 scores and the row
-// at most TK_MASK_KEYS keys, the second read is also the last: it sets one
-// LDS bit per key above the bin and keeps the bin's (score, index) pairs;
-// once T is known the bin's winners join the bits, and the ordered output
-// comes from the bits: two reads of the row.
+// so their bit patterns order like the values, and the k-th largest pattern T
+// is found exactly by radix passes over bits [31:21], [20:10], [9:0]; the
+// output is every index with score > T and the lowest-index (k - #greater)
+// indices with score == T, in ascending index order.
+//
+// The usual case reads the row once.  A sample of whole 32-key lines (one
+// line drawn at a hashed position in each of up to 128 equal strata of the
+// row) gives two of its order statistics around the rank k * s / N, wide
+// enough that about 0.7 * CAP / 2 keys of the row are expected between them
+// (CAP, the LDS capacity in scores, is TK_CAP or, for short rows,
+// TK_CAP_SHORT).  The read of the rest of the row then keeps one LDS bit per
+// key above the upper one and the (score, index) pairs of the keys between
+// the two.  When fewer than k keys lie above the band, at least k above its
+// lower end, and the pairs fit, T lies in the band and is found among the
+// pairs in LDS; the winners join the bits and the ordered output comes from
+// the bits.  The band only decides which keys are looked at again, never
+// which are kept, so a row whose band misses T (the sample is a spatially
+// clustered one) is still exact: it falls back to the passes below.
+//
+// The fallback (and the retained-mass variant, whose k comes from its own
+// passes) reads the row for the first pass; when T's first-pass bin holds at
+// most CAP / 2 scores the second read is also the last (bits for the keys
+// above the bin, pairs for the bin); when it holds at most CAP scores they
+// are copied to LDS and the ordered output takes a third read; otherwise
+// every pass reads the row.  Rows longer than TK_MASK_KEYS keys skip the
+// band and the bits.
 constexpr int TK_NT = 256;
 constexpr int TK_CAP = 4096;
+// Rows of at most TK_SHORT_WORDS * 32 keys use TK_CAP_SHORT: 2.25 KB less of
+// LDS for the pairs, with the row's bits, keeps a workgroup within a sixth of
+// the CU's 160 KB (in 512-byte granules), and the kernel is compiled for six
+// waves per SIMD, so six workgroups share a CU instead of five.
+constexpr int TK_CAP_SHORT = 3520;
+constexpr int TK_SHORT_WORDS = 1074;
 constexpr int TK_MASK_KEYS = 1 << 17;  // longest row of the mask path (16 KB of LDS)
+constexpr int TK_SAMPLE_LINES = 128;   // 32-key lines of the band's sample (16 keys per thread)
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __builtin_amdgcn_ds_bpermute((lane - off) << 2, x);
-    if (lane >= off) x += y;
-  }
+  // DPP: shifts by 1, 2, 4, 8 within each row of 16 lanes (a lane whose
+  // source lies before its row adds 0), then lane 15 of rows 0 and 2 is added
+  // to rows 1 and 3, and lane 31 to rows 2 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
 
@@ -262,6 +287,81 @@ __device__ __forceinline__ void block_excl_scan2(int a, int b, int* ea, int* eb,
   *eb = off_b + packed_b - b;
   *ta = tot_a;
   *tb = tot_b;
+}
+
+// The bin of a radix pass that holds the krem-th largest counted element:
+// found[0] = bin, found[1] = elements in higher bins, found[2] = its count.
+// Thread t owns bins [t * nb / TK_NT, (t + 1) * nb / TK_NT).
+__device__ __forceinline__ void radix_find_bin(int nb, int krem, const int* hist, int* sh, int* found) {
+  const int tid = threadIdx.x;
+  const int per = nb / TK_NT;
+  int mine = 0;
+  for (int b = 0; b < per; ++b) mine += hist[tid * per + b];
+  int excl, unused_e, total, unused_t;
+  block_excl_scan2(mine, 0, &excl, &unused_e, &total, &unused_t, sh);
+  int above = total - excl - mine;
+  if (above < krem && above + mine >= krem) {
+    for (int b = per - 1; b >= 0; --b) {
+      const int bin = tid * per + b;
+      if (above + hist[bin] >= krem) {
+        found[0] = bin;
+        found[1] = above;
+        found[2] = hist[bin];
+        break;
+      }
+      above += hist[bin];
+    }
+  }
+  __syncthreads();
+}
+
+// The same for two ranks at once: rank rA over histogram hA and rank rB over
+// hB (each thread owning `per` bins of each; hB may equal hA).  A rank
+// outside [1, count] finds nothing.  found[0..2] for A, found[3..5] for B.
+__device__ __forceinline__ void radix_find_bin2(const int* hA, const int* hB, int per, int rA, int rB, int* sh,
+                                                int* found) {
+  const int tid = threadIdx.x;
+  int a = 0, b = 0;
+  for (int i = 0; i < per; ++i) {
+    a += hA[tid * per + i];
+    b += hB[tid * per + i];
+  }
+  int ea, eb, ta, tb;
+  block_excl_scan2(a, b, &ea, &eb, &ta, &tb, sh);
+  int above_a = ta - ea - a, above_b = tb - eb - b;
+  if (above_a < rA && above_a + a >= rA) {
+    for (int i = per - 1; i >= 0; --i) {
+      const int bin = tid * per + i;
+      if (above_a + hA[bin] >= rA) {
+        found[0] = bin;
+        found[1] = above_a;
+        found[2] = hA[bin];
+        break;
+      }
+      above_a += hA[bin];
+    }
+  }
+  if (above_b < rB && above_b + b >= rB) {
+    for (int i = per - 1; i >= 0; --i) {
+      const int bin = tid * per + i;
+      if (above_b + hB[bin] >= rB) {
+        found[3] = bin;
+        found[4] = above_b;
+        found[5] = hB[bin];
+        break;
+      }
+      above_b += hB[bin];
+    }
+  }
+  __syncthreads();
+}
+
+// Line of stratum i of the band's sample: strata split the row's nlines
+// 32-key lines into nls runs of equal length (+-1); the line is drawn from
+// its run by a multiplicative hash of i.
+__device__ __forceinline__ int sample_line(int i, int nls, int nlines) {
+  const int a = i * nlines / nls, b = (i + 1) * nlines / nls;
+  return a + (int)(((uint32_t)i * 2654435761u) >> 7) % (b - a);
 }
 
 // Fixed-point value of a score for the retained-mass budget: floor(x * 2^48)
@@ -388,63 +488,205 @@ __device__ __forceinline__ int topk_mass_count(const uint32_t* __restrict__ row,
 // (in keys) to count[h][g].  With block > 1 the row holds scores of whole key
 // blocks and every kept block b is written as its keys b*block .. b*block +
 // block - 1.  With MASS the number kept is the retained-mass budget of the
-// group (capped at keep[h]); groups are runs of G of the nq queries.
-template <bool MASS>
-__global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restrict__ colsum, int ldc,
+// group (capped at keep[h]); groups are runs of G of the nq queries.  Plain
+// score rows (keep, idx_start and count null): every row keeps kfix, row g
+// writes idx + g * kfix.
+template <bool MASS, int CAP, int WAVES>
+__global__ __launch_bounds__(TK_NT, WAVES) void group_topk_kernel(const float* __restrict__ colsum, int ldc,
                                                            int32_t* __restrict__ idx, int32_t* __restrict__ count,
                                                            const int32_t* __restrict__ keep,
                                                            const int64_t* __restrict__ idx_start, int head0, int ng,
                                                            int N, int G, int nq, int block, float keep_mass,
-                                                           int mask_words) {
+                                                           int mask_words, int kfix) {
   __shared__ int hist[2048];
-  // candidates of the first pass's bin: TK_CAP scores, or (mask path) up
-  // to TK_CAP / 2 (score, index) pairs
-  __shared__ unsigned long long cand64[TK_CAP / 2];
+  // candidates: CAP scores, or (band and mask paths) up to CAP / 2
+  // (score, index) pairs
+  __shared__ unsigned long long cand64[CAP / 2];
   uint32_t* cand = reinterpret_cast<uint32_t*>(cand64);
   // one bit per key of the row (dynamic, mask_words words; 0 if the row is
   // too long for the mask path)
   extern __shared__ uint32_t mask[];
+  // one bit per 32-key line: lines read by the band's sample
+  __shared__ uint32_t sampled[TK_MASK_KEYS / 32 / 32];
   __shared__ unsigned long long hsum[MASS ? 2048 : 1];
   __shared__ unsigned long long shq[TK_NT / 64 + 1];
   __shared__ int sh[8];
-  __shared__ int found[3];
+  __shared__ int found[6];
+  __shared__ int nband;
   const int tid = threadIdx.x;
   const int g = blockIdx.x, hl = blockIdx.y, h = head0 + hl;
   const uint32_t* row = reinterpret_cast<const uint32_t*>(colsum + ((size_t)hl * ng + g) * ldc);
-  int k = keep[h] / block;
-  int32_t* out = idx + idx_start[h] + (int64_t)g * keep[h];
+  const int kh = keep ? keep[h] : kfix;
+  int k = kh / block;
+  int32_t* out = idx + (idx_start ? idx_start[h] : 0) + (int64_t)g * kh;
   if constexpr (MASS) k = topk_mass_count(row, N, keep_mass, min(G, nq - g * G), k, hist, hsum, shq, sh, found);
-  if (tid == 0) count[(size_t)h * ng + g] = k * block;
+  if (tid == 0 && count) count[(size_t)h * ng + g] = k * block;
 
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
-  // Reads the row 16 consecutive scores per thread and step (four 16-byte
-  // loads in flight; rows start 256-byte aligned) and hands each in-range
-  // score to f.
-  auto scan_row = [&](auto f) {  // f(score bits, key index)
-    for (int j0 = 16 * tid; j0 < N; j0 += 16 * TK_NT) {
-      uint32_t u[16];
-      if (j0 + 16 <= N) {
+  const bool band = !MASS && N <= 32 * mask_words;
+  // Reads the row in steps of 16 * TK_NT keys and hands each score to f.
+  // Load v of a step covers 4 * TK_NT consecutive keys, four per thread, so
+  // each wave reads whole 128-byte lines, and the next step's loads are in
+  // flight while this step's scores are handed over.  Keys past the row (and,
+  // with skip_sampled, keys of the band's sample lines) are not handed over;
+  // their loads read the row's first 16 bytes instead, which stay cached.
+  // The row stride is at least N rounded up to 4, so a 16-byte read at any
+  // key j < N (j a multiple of 4) stays inside the row.
+  // A thread's chunk j = 1024 q + 4 tid lies in line 32 q + tid / 8, so its
+  // sample bit is bit tid / 8 of sampled[q]; skipm caches it for q < 64.
+  uint64_t skipm = 0;
+  // Chunks whose four scores all lie below floor_bits are not handed over.
+  auto scan_row = [&](auto f, bool skip_sampled, uint32_t floor_bits) {  // f(score bits, key index)
+    constexpr int STEP = 16 * TK_NT;
+    auto live = [&](int j) {
+      if (!skip_sampled) return j < N;
+      const int q = j >> 10;
+      const uint32_t smp = q < 64 ? (uint32_t)(skipm >> q) : sampled[q] >> (tid >> 3);
+      return j < N && !(smp & 1u);
+    };
+    auto load = [&](uint4* x, int base) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 x = *reinterpret_cast<const uint4*>(row + j0 + 4 * v);
-          u[4 * v] = x.x;
-          u[4 * v + 1] = x.y;
-          u[4 * v + 2] = x.z;
-          u[4 * v + 3] = x.w;
+      for (int v = 0; v < 4; ++v) {
+        const int j = base + 4 * (TK_NT * v + tid);
+        x[v] = *reinterpret_cast<const uint4*>(row + (live(j) ? j : 0));
+      }
+    };
+    uint4 cur[4], nxt[4];
+    load(cur, 0);
+    for (int base = 0; base < N; base += STEP) {
+      load(nxt, base + STEP);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = base + 4 * (TK_NT * v + tid);
+        if (live(j) && max(max(cur[v].x, cur[v].y), max(cur[v].z, cur[v].w)) >= floor_bits) {
+          f(cur[v].x, j);
+          if (j + 1 < N) f(cur[v].y, j + 1);
+          if (j + 2 < N) f(cur[v].z, j + 2);
+          if (j + 3 < N) f(cur[v].w, j + 3);
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) u[e] = (j0 + e < N) ? row[j0 + e] : 0u;
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (j0 + e < N) f(u[e], j0 + e);
+      for (int v = 0; v < 4; ++v) cur[v] = nxt[v];
     }
   };
   bool in_lds = false, mask_mode = false;
-  int ncand = 0;
-  for (int pass = 0; pass < 3; ++pass) {
+  int ncand = 0, first_pass = 0;
+
+  if (band) {
+    // ---- the band: sample, two of its order statistics, one read of the rest
+    const int nlines = (N + 31) >> 5;
+    const int nls = min(TK_SAMPLE_LINES, nlines);
+    for (int wd = tid; wd < (nlines + 31) >> 5; wd += TK_NT) sampled[wd] = 0u;
+    for (int wd = tid; wd < mask_words; wd += TK_NT) mask[wd] = 0u;
+    if (tid == 0) nband = 0;
+    __syncthreads();
+    // 16 sample keys per thread: 16-byte chunk c = tid + TK_NT * v is quarter
+    // c & 7 of sample line c >> 3; sv has a bit per slot that holds a key
+    uint32_t su[16];
+    uint32_t sv = 0u;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int c = tid + TK_NT * v, i = c >> 3;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (i < nls) {
+        const int line = sample_line(i, nls, nlines);
+        const int j0 = 32 * line + 4 * (c & 7);
+        if (j0 < N) x = *reinterpret_cast<const uint4*>(row + j0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j0 + e < N) sv |= 1u << (4 * v + e);
+        if ((c & 7) == 0) atomicOr(&sampled[line >> 5], 1u << (line & 31));
+      }
+      su[4 * v] = x.x;
+      su[4 * v + 1] = x.y;
+      su[4 * v + 2] = x.z;
+      su[4 * v + 3] = x.w;
+    }
+    // keys in the sample: only the row's last line can be short
+    const int ns = 32 * nls - (sample_line(nls - 1, nls, nlines) == nlines - 1 ? 32 * nlines - N : 0);
+    // the expected rank of T in the sample, +- a margin of about
+    // 0.35 * CAP / 2 keys of the row.  hi and lo bracket the sample's
+    // r_hi-th and r_lo-th largest to 21 bits: a pass over bits [31:21] finds
+    // both ranks' bins, a pass over bits [20:11] (one 1024-bin half of the
+    // histogram per rank) their sub-bins; hi is the top of its sub-bin, lo
+    // the bottom of its own, so the band only grows.
+    const float rs = (float)k * (float)ns / (float)N;
+    const float dm = 0.35f * (float)(CAP / 2) * (float)ns / (float)N;
+    const int r_hi = (int)floorf(rs - dm), r_lo = (int)ceilf(rs + dm);
+    const bool has_hi = r_hi >= 1, has_lo = r_lo <= ns;
+    for (int b = tid; b < 2048; b += TK_NT) hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if ((sv >> e) & 1u) atomicAdd(&hist[su[e] >> 21], 1);
+    __syncthreads();
+    radix_find_bin2(hist, hist, 2048 / TK_NT, has_hi ? r_hi : 0, has_lo ? r_lo : 0, sh, found);
+    const uint32_t top_hi = (uint32_t)found[0], top_lo = (uint32_t)found[3];
+    const int rh = r_hi - found[1], rl = r_lo - found[4];
+    __syncthreads();
+    for (int b = tid; b < 2048; b += TK_NT) hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if ((sv >> e) & 1u) {
+        const int sub = (su[e] >> 11) & 1023;
+        if (has_hi && (su[e] >> 21) == top_hi) atomicAdd(&hist[sub], 1);
+        if (has_lo && (su[e] >> 21) == top_lo) atomicAdd(&hist[1024 + sub], 1);
+      }
+    __syncthreads();
+    radix_find_bin2(hist, hist + 1024, 1024 / TK_NT, has_hi ? rh : 0, has_lo ? rl : 0, sh, found);
+    const uint32_t hi = has_hi ? (top_hi << 21) | ((uint32_t)found[0] << 11) | 0x7ffu : 0xffffffffu;
+    const uint32_t lo = has_lo ? (top_lo << 21) | ((uint32_t)found[3] << 11) : 0u;
+    __syncthreads();
+    int nab = 0;
+    auto classify = [&](uint32_t x, int j) {
+      if (x > hi) {
+        atomicOr(&mask[j >> 5], 1u << (j & 31));
+        ++nab;
+      } else if (x >= lo) {
+        const int slot = atomicAdd(&nband, 1);
+        if (slot < CAP / 2) cand64[slot] = ((unsigned long long)x << 32) | (uint32_t)j;
+      }
+    };
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int c = tid + TK_NT * v, i = c >> 3;
+      if (i < nls) {
+        const int j0 = 32 * sample_line(i, nls, nlines) + 4 * (c & 7);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((sv >> (4 * v + e)) & 1u) classify(su[4 * v + e], j0 + e);
+      }
+    }
+    for (int q = 0; q < min(64, (N + 1023) >> 10); ++q)
+      skipm |= (uint64_t)((sampled[q] >> (tid >> 3)) & 1u) << q;
+    scan_row(classify, true, lo);
+    int unused_e0, unused_e1, above, unused_t;
+    block_excl_scan2(nab, 0, &unused_e0, &unused_e1, &above, &unused_t, sh);  // also orders nband and the LDS
+    const int nb_keys = nband;
+    if (above < k && above + nb_keys >= k && nb_keys <= CAP / 2) {
+      // T lies in the band: the remaining passes run over its pairs, from
+      // the first pass whose bits lo and hi do not share (pairs lie in
+      // [lo, hi], so they share those bits too)
+      ncand = nb_keys;
+      krem = k - above;
+      in_lds = mask_mode = true;
+      if ((lo >> 21) == (hi >> 21)) {
+        first_pass = 1;
+        prefix = lo & (0x7ffu << 21);
+        pmask = 0x7ffu << 21;
+        if ((lo >> 10) == (hi >> 10)) {
+          first_pass = 2;
+          prefix = lo & ~0x3ffu;
+          pmask = ~0x3ffu;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  for (int pass = first_pass; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = pass == 2 ? 1024 : 2048;
     for (int b = tid; b < 2048; b += TK_NT) hist[b] = 0;
@@ -456,35 +698,16 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
       for (int c = tid; c < ncand; c += TK_NT)
         count(mask_mode ? (uint32_t)(cand64[c] >> 32) : cand[c], 0);
     } else {
-      scan_row(count);
+      scan_row(count, false, prefix);
     }
     __syncthreads();
-    // thread t owns bins [t*per, (t+1)*per); `above` = elements in higher bins
-    const int per = nb / TK_NT;
-    int mine = 0;
-    for (int b = 0; b < per; ++b) mine += hist[tid * per + b];
-    int excl, unused_e, total, unused_t;
-    block_excl_scan2(mine, 0, &excl, &unused_e, &total, &unused_t, sh);
-    int above = total - excl - mine;
-    if (above < krem && above + mine >= krem) {
-      for (int b = per - 1; b >= 0; --b) {
-        const int bin = tid * per + b;
-        if (above + hist[bin] >= krem) {
-          found[0] = bin;
-          found[1] = above;
-          found[2] = hist[bin];
-          break;
-        }
-        above += hist[bin];
-      }
-    }
-    __syncthreads();
+    radix_find_bin(nb, krem, hist, sh, found);
     prefix |= (uint32_t)found[0] << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     krem -= found[1];
     const int in_bin = found[2];
     __syncthreads();
-    if (pass == 0 && in_bin <= TK_CAP / 2 && N <= 32 * mask_words) {
+    if (!in_lds && pass == 0 && in_bin <= CAP / 2 && N <= 32 * mask_words) {
       // second (and last) read of the row: the keys above T's bin are kept,
       // one bit each; the (score, index) pairs of the bin go to LDS
       for (int wd = tid; wd < mask_words; wd += TK_NT) mask[wd] = 0u;
@@ -495,17 +718,17 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
           atomicOr(&mask[j >> 5], 1u << (j & 31));
         else if ((x & pmask) == prefix)
           cand64[atomicAdd(&sh[0], 1)] = ((unsigned long long)x << 32) | (uint32_t)j;
-      });
+      }, false, prefix);
       __syncthreads();
       ncand = in_bin;
       in_lds = mask_mode = true;
-    } else if (pass == 0 && in_bin <= TK_CAP) {
+    } else if (!in_lds && pass == 0 && in_bin <= CAP) {
       // second read: the scores in T's bin, to LDS (exactly in_bin of them)
       if (tid == 0) sh[0] = 0;
       __syncthreads();
       scan_row([&](uint32_t x, int) {
         if ((x & pmask) == prefix) cand[atomicAdd(&sh[0], 1)] = x;
-      });
+      }, false, prefix);
       __syncthreads();
       ncand = in_bin;
       in_lds = true;
@@ -514,50 +737,83 @@ __global__ __launch_bounds__(TK_NT) void group_topk_kernel(const float* __restri
   const uint32_t T = prefix;
 
   if (mask_mode) {
-    // the bin's winners join the mask: scores above T, and of the scores
+    // the pairs' winners join the mask: scores above T, and of the scores
     // equal to T the krem with the lowest indices
+    int neq = 0;
     for (int c = tid; c < ncand; c += TK_NT) {
       const unsigned long long e = cand64[c];
       const uint32_t x = (uint32_t)(e >> 32);
-      const int j = (int)(uint32_t)e;
-      bool win = x > T;
-      if (x == T) {
-        int rank = 0;
-        for (int c2 = 0; c2 < ncand; ++c2) {
-          const unsigned long long e2 = cand64[c2];
-          rank += ((uint32_t)(e2 >> 32) == T && (int)(uint32_t)e2 < j);
+      if (x > T) atomicOr(&mask[(uint32_t)e >> 5], 1u << ((uint32_t)e & 31));
+      neq += x == T;
+    }
+    int neq_e0, neq_e1, neq_all, neq_t1;
+    block_excl_scan2(neq, 0, &neq_e0, &neq_e1, &neq_all, &neq_t1, sh);
+    // ties: the krem-th smallest index J among the pairs equal to T, as the
+    // krem-th largest of ~j (radix passes over the pairs); krem == neq_all
+    // (the usual single key at T) keeps them all
+    uint32_t jkey = 0;
+    if (krem < neq_all) {
+      uint32_t pre = 0, pm = 0;
+      int r = krem;
+      for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nb = pass == 2 ? 1024 : 2048;
+        for (int b = tid; b < 2048; b += TK_NT) hist[b] = 0;
+        __syncthreads();
+        for (int c = tid; c < ncand; c += TK_NT) {
+          const unsigned long long e = cand64[c];
+          const uint32_t nj = ~(uint32_t)e;
+          if ((uint32_t)(e >> 32) == T && (nj & pm) == pre) atomicAdd(&hist[(nj >> shift) & (nb - 1)], 1);
         }
-        win = rank < krem;
+        __syncthreads();
+        radix_find_bin(nb, r, hist, sh, found);
+        pre |= (uint32_t)found[0] << shift;
+        pm |= (uint32_t)(nb - 1) << shift;
+        r -= found[1];
+        __syncthreads();
       }
-      if (win) atomicOr(&mask[j >> 5], 1u << (j & 31));
+      jkey = pre;
+    }
+    for (int c = tid; c < ncand; c += TK_NT) {
+      const unsigned long long e = cand64[c];
+      if ((uint32_t)(e >> 32) == T && ~(uint32_t)e >= jkey)
+        atomicOr(&mask[(uint32_t)e >> 5], 1u << ((uint32_t)e & 31));
     }
     __syncthreads();
-    // ordered compaction of the mask: thread t owns words [t*wpt, (t+1)*wpt)
+    // ordered compaction of the mask into an LDS window of CAP positions
+    // (the pairs' space, free now), which then goes out with consecutive
+    // stores; one window per CAP kept keys.  Words are taken in rounds of
+    // TK_NT, one per thread, so a run of full words spreads over the lanes.
     const int nwords = (N + 31) / 32;
-    const int wpt = (nwords + TK_NT - 1) / TK_NT;
-    int mine = 0;
-    for (int i = 0; i < wpt; ++i) {
-      const int wd = tid * wpt + i;
-      if (wd < nwords) mine += __popc(mask[wd]);
-    }
-    int excl, unused_e, total, unused_t;
-    block_excl_scan2(mine, 0, &excl, &unused_e, &total, &unused_t, sh);
-    int pos = excl;
-    for (int i = 0; i < wpt; ++i) {
-      const int wd = tid * wpt + i;
-      if (wd >= nwords) break;
-      uint32_t bits = mask[wd];
-      while (bits) {
-        const int j = 32 * wd + __ffs(bits) - 1;
-        bits &= bits - 1;
-        if (pos < k) {
-          if (block == 1)
-            out[pos] = j;
-          else
-            for (int t = 0; t < block; ++t) out[(int64_t)pos * block + t] = j * block + t;
+    int32_t* stage = reinterpret_cast<int32_t*>(cand64);
+    for (int w0 = 0; w0 < k; w0 += CAP) {
+      const int wn = min(CAP, k - w0);
+      int base = 0;  // kept keys in the rounds before
+      for (int r0 = 0; r0 < nwords && base < w0 + wn; r0 += TK_NT) {
+        const int wd = r0 + tid;
+        const uint32_t word = wd < nwords ? mask[wd] : 0u;
+        const int cnt = __popc(word);
+        int ex, unused_e, tot, unused_t;
+        block_excl_scan2(cnt, 0, &ex, &unused_e, &tot, &unused_t, sh);
+        int pos = base + ex;
+        if (pos < w0 + wn && pos + cnt > w0) {
+          uint32_t bits = word;
+          while (bits) {
+            const int j = 32 * wd + __ffs(bits) - 1;
+            bits &= bits - 1;
+            if (pos >= w0 && pos < w0 + wn) stage[pos - w0] = j;
+            ++pos;
+          }
         }
-        ++pos;
+        base += tot;
       }
+      __syncthreads();
+      if (block == 1) {
+        for (int e = tid; e < wn; e += TK_NT) out[w0 + e] = stage[e];
+      } else {
+        for (int e = tid; e < wn * block; e += TK_NT) out[(int64_t)w0 * block + e] = stage[e / block] * block + e % block;
+      }
+      __syncthreads();
     }
     return;
   }
@@ -770,16 +1026,35 @@ hipError_t launch_group_topk(const float* colsum, int ldc, int32_t* idx, int32_t
                              const int64_t* idx_start, int head0, int nheads, int ng, int N, int G, int nq, int block,
                              float keep_mass, hipStream_t s) {
   if (nheads == 0 || ng == 0) return hipSuccess;
-  // the mask path of the top-k holds one bit per key in LDS (rows up to
-  // TK_MASK_KEYS keys); longer rows take the three-read path
+  // the kernel's 16-byte reads at keys j < N need a row stride of at least N
+  // rounded up to 4 keys, and 16-byte aligned rows
+  if (ldc % 4 != 0 || ldc < N) return hipErrorInvalidValue;
+  // the band and mask paths of the top-k hold one bit per key in LDS (rows
+  // up to TK_MASK_KEYS keys); longer rows take the three-read path
   const int mask_words = N <= TK_MASK_KEYS ? (N + 31) / 32 : 0;
   const size_t lds = (size_t)mask_words * 4;
   if (keep_mass > 0.f)
-    hipLaunchKernelGGL(group_topk_kernel<true>, dim3(ng, nheads), dim3(TK_NT), lds, s, colsum, ldc, idx, count, keep,
-                       idx_start, head0, ng, N, G, nq, block, keep_mass, mask_words);
+    hipLaunchKernelGGL((group_topk_kernel<true, TK_CAP, 1>), dim3(ng, nheads), dim3(TK_NT), lds, s, colsum, ldc, idx,
+                       count, keep, idx_start, head0, ng, N, G, nq, block, keep_mass, mask_words, 0);
+  else if (mask_words <= TK_SHORT_WORDS)
+    hipLaunchKernelGGL((group_topk_kernel<false, TK_CAP_SHORT, 6>), dim3(ng, nheads), dim3(TK_NT), lds, s, colsum, ldc,
+                       idx, count, keep, idx_start, head0, ng, N, G, nq, block, keep_mass, mask_words, 0);
   else
-    hipLaunchKernelGGL(group_topk_kernel<false>, dim3(ng, nheads), dim3(TK_NT), lds, s, colsum, ldc, idx, count, keep,
-                       idx_start, head0, ng, N, G, nq, block, keep_mass, mask_words);
+    hipLaunchKernelGGL((group_topk_kernel<false, TK_CAP, 1>), dim3(ng, nheads), dim3(TK_NT), lds, s, colsum, ldc, idx,
+                       count, keep, idx_start, head0, ng, N, G, nq, block, keep_mass, mask_words, 0);
+  return launched(s);
+}
+
+hipError_t launch_topk_rows(const float* scores, int ld, int rows, int n, int k, int32_t* idx, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (ld % 4 != 0 || ld < n || k < 1 || k > n) return hipErrorInvalidValue;
+  const int mask_words = n <= TK_MASK_KEYS ? (n + 31) / 32 : 0;
+  if (mask_words <= TK_SHORT_WORDS)
+    hipLaunchKernelGGL((group_topk_kernel<false, TK_CAP_SHORT, 6>), dim3(rows, 1), dim3(TK_NT), (size_t)mask_words * 4,
+                       s, scores, ld, idx, nullptr, nullptr, nullptr, 0, rows, n, 1, n, 1, 0.f, mask_words, k);
+  else
+    hipLaunchKernelGGL((group_topk_kernel<false, TK_CAP, 1>), dim3(rows, 1), dim3(TK_NT), (size_t)mask_words * 4, s,
+                       scores, ld, idx, nullptr, nullptr, nullptr, 0, rows, n, 1, n, 1, 0.f, mask_words, k);
   return launched(s);
 }
 

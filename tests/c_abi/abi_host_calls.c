@@ -86,6 +86,22 @@ int main(void) {
   d.seq_len = 1000;
   CHECK(mcs_dense_attn(&d, NULL, NULL, NULL, NULL, NULL) == MCS_ERROR_INVALID_VALUE);
   CHECK(mcs_sparse_attn(NULL, NULL, NULL, NULL, NULL, NULL, NULL) == MCS_ERROR_INVALID_VALUE);
+  /* the row top-k validates sizes, strides and buffers before any device call */
+  {
+    float* fake = (float*)(uintptr_t)0x1000;     /* never dereferenced: every call below fails validation */
+    int32_t* fidx = (int32_t*)(uintptr_t)0x2000;
+    CHECK(mcs_topk_rows(fake, 8, 0, 8, 2, fidx, NULL) == MCS_SUCCESS);        /* no rows: nothing to do */
+    CHECK(mcs_topk_rows(NULL, 8, 1, 8, 2, fidx, NULL) == MCS_ERROR_INVALID_VALUE);
+    CHECK(mcs_topk_rows(fake, 8, 1, 8, 2, NULL, NULL) == MCS_ERROR_INVALID_VALUE);
+    CHECK(mcs_topk_rows(fake, 8, 1, 8, 0, fidx, NULL) == MCS_ERROR_INVALID_VALUE);   /* k < 1 */
+    CHECK(mcs_topk_rows(fake, 8, 1, 8, 9, fidx, NULL) == MCS_ERROR_INVALID_VALUE);   /* k > n */
+    CHECK(mcs_topk_rows(fake, 6, 1, 6, 2, fidx, NULL) == MCS_ERROR_INVALID_VALUE);   /* ld not a multiple of 4 */
+    CHECK(mcs_topk_rows(fake, 4, 1, 8, 2, fidx, NULL) == MCS_ERROR_INVALID_VALUE);   /* ld < n */
+    CHECK(mcs_topk_rows(fake, 8, -1, 8, 2, fidx, NULL) == MCS_ERROR_INVALID_VALUE);  /* rows < 0 */
+    CHECK(mcs_topk_rows(fake, 8, 1, 0, 1, fidx, NULL) == MCS_ERROR_INVALID_VALUE);   /* n < 1 */
+    CHECK(mcs_topk_rows((float*)((char*)fake + 4), 8, 1, 8, 2, fidx, NULL) == MCS_ERROR_MISALIGNED);
+    CHECK(mcs_topk_rows(fake, 8, 1, 8, 2, (int32_t*)((char*)fidx + 2), NULL) == MCS_ERROR_MISALIGNED);
+  }
 
   if (failures == 0) printf("C ABI host calls: all checks held\n");
   return failures == 0 ? 0 : 1;

@@ -241,13 +241,16 @@ def test_selection_in_head_chunks_matches_one_pass(hc):
 
 def test_topk_on_rows_with_one_crowded_bin():
     """Rows whose first-pass bin of the k-th score holds more scores than the
-    4096 the top-k copies to LDS, so its last passes run over global memory.
-    With q = 0 every score is equal (the whole row, 16384 scores, in one
-    bin); with |q| ~ 1e-3 the column sums centre on G / N = 2^-8, and the
-    bin [2^-8, 1.25 * 2^-8) holds about half the row (~8000 scores), well
-    above 4096.  Equal scores keep exactly the lowest indices; near-equal
-    ones meet the kept-key rule against the oracle.  (The DiT-shaped rows of
-    the other tests put a few hundred scores in that bin: the LDS path.)"""
+    top-k can copy to LDS (3520 on these 16384-key rows).  With q = 0 every
+    score is equal: the sampled band holds the whole row, far more pairs than
+    fit, so the kernel falls back to its passes over global memory.  With
+    |q| ~ 1e-3 the column sums centre on G / N = 2^-8 and the bin
+    [2^-8, 1.25 * 2^-8) holds about half the row (~8000 scores); the band
+    around the k-th score usually resolves it in LDS, and a row whose band
+    missed would take the global passes.  Equal scores keep exactly the
+    lowest indices; near-equal ones meet the kept-key rule against the
+    oracle.  Every path of the top-k is pinned bit-exactly on caller rows in
+    test_gpu_topk.py."""
     _need_gpu()
     N, d, G, keep = 16384, 64, 64, 300
     sc = scale_for(d)

@@ -73,6 +73,15 @@ struct Geo {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f16x8 as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8, u); }
+// two float32 values rounded to float16 (nearest even), packed
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2 t = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, t);
+}
+
 template <bool B>
 struct Flag {
   static constexpr bool value = B;
@@ -99,8 +108,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr bool SPARSE = (MODE == MODE_REUSE || MODE == MODE_RESINIT);
   // The selection step's outputs (dense output and selection-time sparse
   // output) feed the cached residual, which every reuse step adds back; they
-  // carry the probabilities into the PV product as bf16 hi + lo parts so that
-  // the residual holds ~16-bit probabilities instead of 8-bit ones.
+  // carry the probabilities into the PV product at more than bf16's 8 bits.
+  // With a.v16 (V rounded to float16 once per selection, exact for bf16
+  // values of normal float16 range) the product runs on float16 MFMAs with
+  // P in float16 (11 bits); when V held values beyond float16's range
+  // (*a.v16_bad set) it runs on bf16 with P as hi + lo parts (~16 bits).
   constexpr bool PRECISE_PV = (MODE == MODE_SELECT || MODE == MODE_RESINIT);
   constexpr int STAGE = 2 * GE::TILE;        // K tile + V tile
   static_assert(UPW * NW == GE::NI, "tile loads must split evenly over the waves");
@@ -128,7 +140,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   const size_t hoff = (size_t)h * N * D;
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + hoff;
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + hoff;
-  const uint16_t* vh = static_cast<const uint16_t*>(a.v) + hoff;
+  // the float16 copy of V holds the launch's heads only
+  const bool use16 = PRECISE_PV && a.v16 != nullptr && *a.v16_bad == 0;
+  const uint16_t* vh = use16 ? static_cast<const uint16_t*>(a.v16) + (size_t)(h - a.head0) * N * D
+                             : static_cast<const uint16_t*>(a.v) + hoff;
   const int32_t* permh = a.perm ? a.perm + (size_t)h * N : nullptr;
   // Buffer resources over this head's K and V (N rows of ROWB bytes).
   const int head_bytes = N * GE::ROWB;
@@ -233,7 +248,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto attend_tile = [&](int j, const char* cur, char* nxt, auto masked) {
+    auto attend_tile = [&](int j, const char* cur, char* nxt, auto masked, auto f16) __attribute__((always_inline)) {
+      constexpr bool F16 = PRECISE_PV && decltype(f16)::value;   // P and V as float16
+      constexpr bool HILO = PRECISE_PV && !F16;                  // P as bf16 hi + lo
       wait_vm<0>();
       __syncthreads();
       if (j + 1 < nt) {
@@ -316,7 +333,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       // of the largest term.  The decision is taken per row block from the
       // lanes' maxima.
       bool big[2] = {false, false};
-      if constexpr (PRECISE_PV) {
+      if constexpr (HILO) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           big[rb] = __ballot(lmx[rb] > __builtin_fmaxf(m_run[rb], lref[rb]) - kLoSkip) != 0ull;
@@ -324,7 +341,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
         }
       }
       bf16x8 pf[KC][2];
-      bf16x8 pl[PRECISE_PV ? KC : 1][2];
+      bf16x8 pl[HILO ? KC : 1][2];
+      f16x8 ph[F16 ? KC : 1][2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         float ls = 0.f;
@@ -339,12 +357,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
         l_run[rb] += ls;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
+          if constexpr (F16) {
+            ph[kc][rb] = as_f16x8(make_uint4(pack_f16x2(s[2 * kc][rb][0], s[2 * kc][rb][1]),
+                                             pack_f16x2(s[2 * kc][rb][2], s[2 * kc][rb][3]),
+                                             pack_f16x2(s[2 * kc + 1][rb][0], s[2 * kc + 1][rb][1]),
+                                             pack_f16x2(s[2 * kc + 1][rb][2], s[2 * kc + 1][rb][3])));
+            continue;
+          }
           const uint4 hi = make_uint4(pack_bf16x2(s[2 * kc][rb][0], s[2 * kc][rb][1]),
                                       pack_bf16x2(s[2 * kc][rb][2], s[2 * kc][rb][3]),
                                       pack_bf16x2(s[2 * kc + 1][rb][0], s[2 * kc + 1][rb][1]),
                                       pack_bf16x2(s[2 * kc + 1][rb][2], s[2 * kc + 1][rb][3]));
           pf[kc][rb] = as_bf16x8(hi);
-          if constexpr (PRECISE_PV) {
+          if constexpr (HILO) {
             if (!big[rb]) continue;
             // low part p - bf16(p), so that P = hi + lo to ~16 significant bits
             const uint32_t h4[4] = {hi.x, hi.y, hi.z, hi.w};
@@ -366,13 +391,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 vf = as_bf16x8(
-              make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y));
+          const uint4 vu = make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y);
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kc][rb], oacc[db][rb], 0, 0, 0);
+          for (int rb = 0; rb < 2; ++rb) {
+            if constexpr (F16)
+              oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(vu), ph[kc][rb], oacc[db][rb], 0, 0, 0);
+            else
+              oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vu), pf[kc][rb], oacc[db][rb], 0, 0, 0);
+          }
         }
-      if constexpr (PRECISE_PV) {
+      if constexpr (HILO) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           if (!big[rb]) continue;
@@ -391,23 +419,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     fetch_rows(0);
     if (nt > 0) issue(st0, true);
     fetch_rows(1);
-    {
+    auto run_tiles = [&](auto f16) __attribute__((always_inline)) {
       const Flag<false> full;
       const Flag<true> ragged;
       const int nfull = (nkv % BK) ? nt - 1 : nt;   // tiles that need no masking
       int j = 0;
       for (; j + 1 < nfull; j += 2) {
-        attend_tile(j, st0, st1, full);
-        attend_tile(j + 1, st1, st0, full);
+        attend_tile(j, st0, st1, full, f16);
+        attend_tile(j + 1, st1, st0, full, f16);
       }
-      if (j < nfull) attend_tile(j++, st0, st1, full);
+      if (j < nfull) attend_tile(j++, st0, st1, full, f16);
       if (j < nt) {
         if (j & 1)
-          attend_tile(j, st1, st0, ragged);
+          attend_tile(j, st1, st0, ragged, f16);
         else
-          attend_tile(j, st0, st1, ragged);
+          attend_tile(j, st0, st1, ragged, f16);
       }
-    }
+    };
+    if (PRECISE_PV && use16)
+      run_tiles(Flag<true>());
+    else
+      run_tiles(Flag<false>());
 
     // ---- epilogue ---------------------------------------------------------
 #pragma unroll

@@ -120,13 +120,16 @@ uint64_t colsum_ld(int N) { return align_up((uint64_t)N, 64); }
 uint64_t block_ld(int N) { return align_up((uint64_t)(N + 63) / 64, 64); }
 
 struct WsLayout {
-  uint64_t off_keys, off_proj, off_mean, off_colsum, per_head_colsum, per_head_block, per_head_lse, per_head_odense,
-      fixed;
-  uint64_t per_head() const { return per_head_colsum + per_head_block + per_head_lse + per_head_odense; }
+  uint64_t off_keys, off_proj, off_mean, off_flag, off_colsum, per_head_colsum, per_head_block, per_head_lse,
+      per_head_odense, per_head_v16, fixed;
+  uint64_t per_head() const {
+    return per_head_colsum + per_head_block + per_head_lse + per_head_odense + per_head_v16;
+  }
 };
 
-// keys | projections | query means | key scores [hc][ng][ldc] | block scores [hc][ng][ldb] | row lse [hc][N] |
-// float32 dense output [hc][N][d] (bf16 residual only)
+// keys | projections | query means | float16 overflow flag | key scores [hc][ng][ldc] |
+// block scores [hc][ng][ldb] | row lse [hc][N] | float32 dense output [hc][N][d] (bf16 residual only) |
+// V rounded to float16 [hc][N][d] (bf16 problems)
 WsLayout ws_layout(const mcs_attn_desc* d, int32_t G, bool bf16_residual) {
   const uint64_t H = (uint64_t)d->num_heads, N = (uint64_t)d->seq_len;
   const uint64_t ng = (N + G - 1) / G;
@@ -134,11 +137,13 @@ WsLayout ws_layout(const mcs_attn_desc* d, int32_t G, bool bf16_residual) {
   w.off_keys = 0;
   w.off_proj = align_up(H * N, kAlign);
   w.off_mean = align_up(w.off_proj + (uint64_t)MCS_HASH_BITS * d->head_dim * 8, kAlign);
-  w.off_colsum = align_up(w.off_mean + H * d->head_dim * 8, kAlign);
+  w.off_flag = align_up(w.off_mean + H * d->head_dim * 8, kAlign);
+  w.off_colsum = align_up(w.off_flag + 4, kAlign);
   w.per_head_colsum = ng * colsum_ld((int)N) * 4;
   w.per_head_block = ng * block_ld((int)N) * 4;
   w.per_head_lse = align_up(N * 4, kAlign);
   w.per_head_odense = bf16_residual ? align_up(N * (uint64_t)d->head_dim * 4, kAlign) : 0;
+  w.per_head_v16 = d->dtype == MCS_DTYPE_BF16 ? align_up(N * (uint64_t)d->head_dim * 2, kAlign) : 0;
   w.fixed = w.off_colsum;
   return w;
 }
@@ -405,6 +410,10 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
   float* odense = bf16_res ? at<float>(ws, wl.off_colsum + (uint64_t)hc * (wl.per_head_colsum + wl.per_head_block +
                                                                           wl.per_head_lse))
                            : nullptr;
+  void* v16 = wl.per_head_v16 ? at<void>(ws, wl.off_colsum + (uint64_t)hc * (wl.per_head_colsum + wl.per_head_block +
+                                                                          wl.per_head_lse + wl.per_head_odense))
+                              : nullptr;
+  int* v16_bad = at<int>(ws, wl.off_flag);
   int32_t* perm = at<int32_t>(meta_buf, m.off_perm);
   if (o.grouping == MCS_GROUPING_HASH || o.grouping == MCS_GROUPING_CENTRED_HASH) {
     double* mean = nullptr;
@@ -449,6 +458,14 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
     a.head0 = h0;
     a.nheads = std::min(hc, H - h0);
     a.o = o_dense_out;
+    if (v16) {
+      // the chunk's V in float16 for the selection's P·V products
+      if ((e = mcs::launch_v_to_f16(static_cast<const uint16_t*>(v) + (size_t)h0 * N * D, v16,
+                                    (long long)a.nheads * N * D, v16_bad, s)) != hipSuccess)
+        return hip_fail(e);
+      a.v16 = v16;
+      a.v16_bad = v16_bad;
+    }
     if ((e = launch_attn(d->dtype, mcs::MODE_SELECT, a, s)) != hipSuccess || (e = mark(1)) != hipSuccess)
       return hip_fail(e);
     if (d->dtype == MCS_DTYPE_BF16 && (e = launch_attn(d->dtype, mcs::MODE_SCORE, a, s)) != hipSuccess)

@@ -881,6 +881,29 @@ __global__ void block_scores_kernel(const float* __restrict__ colsum, int ldc, f
   bs[r * ldb + b] = sum;
 }
 
+// V rounded to float16 (nearest even) for the selection's P·V products:
+// eight values per thread and step.  A finite value that rounds to infinity
+// (|v| >= 65520) sets *bad, and the attention kernels then keep to bf16.
+__global__ void v_to_f16_kernel(const uint4* __restrict__ v, uint4* __restrict__ out, long long n8, int* bad) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  bool over = false;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (long long)gridDim.x * blockDim.x) {
+    const uint4 x = v[i];
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xffff0000u);
+      const f16x2 hv = {(_Float16)a, (_Float16)b};
+      over |= (__builtin_isinf((float)hv[0]) && !__builtin_isinf(a)) ||
+              (__builtin_isinf((float)hv[1]) && !__builtin_isinf(b));
+      o[e] = __builtin_bit_cast(uint32_t, hv);
+    }
+    out[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (over) atomicOr(bad, 1);
+}
+
 // Raster-order groups: perm[h][p] = p.
 __global__ void iota_perm_kernel(int32_t* __restrict__ perm, long long total, int N) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long long)gridDim.x * blockDim.x)
@@ -1013,6 +1036,19 @@ hipError_t launch_query_mean(const void* q, int dtype, double* mean, int H, int 
       hipLaunchKernelGGL((query_mean_kernel<float, 128>), dim3(H), dim3(128), 0, s, static_cast<const float*>(q),
                          mean, N);
   }
+  return launched(s);
+}
+
+hipError_t launch_v_to_f16(const void* v, void* out, long long n, int* bad, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  const int zero = 0;
+  hipError_t e = launch_fill_bytes(bad, &zero, sizeof(zero), s);
+  if (e != hipSuccess) return e;
+  const long long n8 = n / 8;
+  const long long blocks = std::min<long long>((n8 + 255) / 256, 4096);
+  hipLaunchKernelGGL(v_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const uint4*>(v),
+                     static_cast<uint4*>(out), n8, bad);
   return launched(s);
 }
 

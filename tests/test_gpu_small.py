@@ -147,6 +147,38 @@ def test_reuse_on_selection_inputs_reproduces_dense():
         assert_close(a[h], orc.dense_attention(q, k, v, sc), "bf16", f"head {h}")
 
 
+def test_selection_with_v_beyond_float16_range():
+    """The selection's P·V products run on float16 with V rounded once per
+    selection; a V holding values beyond float16's range (|v| >= 65520)
+    makes them fall back to bf16 with P as hi + lo parts.  V scaled by 2^16
+    (exact in bf16) overflows float16: the kept keys are unchanged (scores
+    do not involve V), every residual and dense value is finite, and the
+    results are 2^16 times the unscaled ones within the bf16 tolerances; the
+    unscaled ones meet the oracle in the other tests.  A scale of 2^17 gives
+    exactly twice the 2^16 results (the same bf16 path, powers of two)."""
+    _need_gpu()
+    grid, H, d, G = (4, 8, 20), 2, 128, 64
+    p = build_problem(grid, H, d, "bf16", G, [128, 300], 0.0, [1], wid=111)
+    sc = scale_for(d)
+    q, k, v = p.dev[0]
+    out = {}
+    for e in (0, 16, 17):
+        vs = (v.float() * float(2 ** e)).to(torch.bfloat16)
+        meta, od = mcs.select(q, k, vs, G, p.keeps, p.proj(), scale=sc, return_dense=True)
+        torch.cuda.synchronize()
+        out[e] = (meta.idx.clone(), meta.residual.clone(), od.clone())
+    assert torch.equal(out[0][0], out[16][0]) and torch.equal(out[16][0], out[17][0])
+    for e in (16, 17):
+        assert torch.isfinite(out[e][1]).all() and torch.isfinite(out[e][2].float()).all(), e
+    assert torch.equal(out[17][1], 2.0 * out[16][1])
+    assert torch.equal(out[17][2].float(), 2.0 * out[16][2].float())
+    ref_od = to_np(out[0][2]).astype(np.float64)
+    assert_close(to_np(out[16][2]) / 2.0 ** 16, ref_od, "bf16", "dense output, V x 2^16 (bf16 P.V) vs V")
+    r0, r16 = to_np(out[0][1]).astype(np.float64), to_np(out[16][1]) / 2.0 ** 16
+    rel = float(np.linalg.norm(r16 - r0) / np.linalg.norm(ref_od))
+    assert rel <= 5e-3, f"residual, V x 2^16 vs V: relative L2 {rel:.2e} against the dense output's norm"
+
+
 def test_deterministic():
     _need_gpu()
     grid, H, d, G = (4, 8, 20), 2, 64, 128

@@ -111,8 +111,9 @@ def test_workspace_bytes(lib):
     one = lib.mcs_select_workspace_bytes(ctypes.byref(d), 64, 1)
     two = lib.mcs_select_workspace_bytes(ctypes.byref(d), 64, 2)
     # 16 groups x (N rounded up to 64 key scores + 16 block scores rounded up to 64) x float32,
-    # plus the N rows' log-sum-exp (float32, rounded up to 256 bytes)
-    per = 16 * (1024 + 64) * 4 + 4096
+    # plus the N rows' log-sum-exp (float32, rounded up to 256 bytes) and, for bf16 problems,
+    # the head's V rounded to float16 [N][d]
+    per = 16 * (1024 + 64) * 4 + 4096 + 1000 * 64 * 2
     assert two - one == per
     assert lib.mcs_select_workspace_bytes(ctypes.byref(d), 64, 99) == lib.mcs_select_workspace_bytes(
         ctypes.byref(d), 64, 4)

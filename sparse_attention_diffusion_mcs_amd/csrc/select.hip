@@ -493,11 +493,12 @@ __device__ __forceinline__ int topk_mass_count(const uint32_t* __restrict__ row,
 // writes idx + g * kfix.
 template <bool MASS, int CAP, int WAVES>
 __global__ __launch_bounds__(TK_NT, WAVES) void group_topk_kernel(const float* __restrict__ colsum, int ldc,
-                                                           int32_t* __restrict__ idx, int32_t* __restrict__ count,
-                                                           const int32_t* __restrict__ keep,
-                                                           const int64_t* __restrict__ idx_start, int head0, int ng,
-                                                           int N, int G, int nq, int block, float keep_mass,
-                                                           int mask_words, int kfix) {
+                                                                  int32_t* __restrict__ idx,
+                                                                  int32_t* __restrict__ count,
+                                                                  const int32_t* __restrict__ keep,
+                                                                  const int64_t* __restrict__ idx_start, int head0,
+                                                                  int ng, int N, int G, int nq, int block,
+                                                                  float keep_mass, int mask_words, int kfix) {
   __shared__ int hist[2048];
   // candidates: CAP scores, or (band and mask paths) up to CAP / 2
   // (score, index) pairs

@@ -81,8 +81,9 @@ typedef enum mcs_status {
 typedef enum mcs_dtype {
   MCS_DTYPE_FP32 = 0,  /* float32 in and out; float32 arithmetic */
   MCS_DTYPE_BF16 = 1   /* bfloat16 in and out; bf16 matrix products with float32 accumulation (the
-                          selection's P.V products: float16, with V rounded to float16 once per
-                          selection, or bf16 with P in two parts when V exceeds float16's range) */
+                          selection's P.V products: float16, with each head's V rounded to float16
+                          once per selection, scaled by a power of two when it exceeds float16's
+                          range) */
 } mcs_dtype;
 
 /* Shape of one attention layer. */
@@ -234,8 +235,8 @@ mcs_status mcs_meta_layout_ex(const mcs_attn_desc* desc, int32_t group_size, con
  * (1/64 of that) for block-granular selection, the rows' log-sum-exp
  * (float32 [heads_per_chunk][N]) that the dense pass hands to the key-score
  * pass, and for bf16 problems the chunk's V rounded to float16
- * ([heads_per_chunk][N][d], two bytes each) for the selection's P.V
- * products.
+ * ([heads_per_chunk][N][d], two bytes each, and two words per head) for the
+ * selection's P.V products.
  */
 size_t mcs_select_workspace_bytes(const mcs_attn_desc* desc, int32_t group_size, int32_t heads_per_chunk);
 

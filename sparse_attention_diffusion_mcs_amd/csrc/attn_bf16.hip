@@ -1,6 +1,7 @@
 // bf16 attention kernels for gfx950 (MFMA v_mfma_f32_16x16x32_bf16, float32
-// accumulation): dense attention with the per-group key scores of the
-// selection step, and gathered-KV sparse attention of the reuse step.
+// accumulation; the selection passes take their P·V products on
+// v_mfma_f32_16x16x32_f16): dense attention with the per-group key scores of
+// the selection step, and gathered-KV sparse attention of the reuse step.
 //
 // Method: abstract of "MC-Sparse: Deconstructing and Closing the Dense-Sparse
 // Attention Gap in Diffusion Transformers" (exact probabilities drive the
@@ -47,7 +48,6 @@ namespace mcs {
 namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
-constexpr float kLoSkip = 4.0f;        // log2 units: row blocks below 2^-4 of the running max carry P as bf16 only
 constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 constexpr long long kScoreItems = 12288;   // key-score work items to aim for (~16 rounds of resident workgroups)
 
@@ -108,11 +108,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr bool SPARSE = (MODE == MODE_REUSE || MODE == MODE_RESINIT);
   // The selection step's outputs (dense output and selection-time sparse
   // output) feed the cached residual, which every reuse step adds back; they
-  // carry the probabilities into the PV product at more than bf16's 8 bits.
-  // With a.v16 (V rounded to float16 once per selection, exact for bf16
-  // values of normal float16 range) the product runs on float16 MFMAs with
-  // P in float16 (11 bits); when V held values beyond float16's range
-  // (*a.v16_bad set) it runs on bf16 with P as hi + lo parts (~16 bits).
+  // carry the probabilities into the PV product at more than bf16's 8 bits:
+  // the product runs on float16 MFMAs with P in float16 (11 bits) and V from
+  // a.v16, V rounded to float16 once per selection after a per-head scaling
+  // by 2^-a.v16_exp[head] (0 unless the head's V exceeds float16's range),
+  // which the epilogue undoes.
   constexpr bool PRECISE_PV = (MODE == MODE_SELECT || MODE == MODE_RESINIT);
   constexpr int STAGE = 2 * GE::TILE;        // K tile + V tile
   static_assert(UPW * NW == GE::NI, "tile loads must split evenly over the waves");
@@ -141,9 +141,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + hoff;
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + hoff;
   // the float16 copy of V holds the launch's heads only
-  const bool use16 = PRECISE_PV && a.v16 != nullptr && *a.v16_bad == 0;
-  const uint16_t* vh = use16 ? static_cast<const uint16_t*>(a.v16) + (size_t)(h - a.head0) * N * D
-                             : static_cast<const uint16_t*>(a.v) + hoff;
+  const uint16_t* vh = PRECISE_PV ? static_cast<const uint16_t*>(a.v16) + (size_t)(h - a.head0) * N * D
+                                  : static_cast<const uint16_t*>(a.v) + hoff;
   const int32_t* permh = a.perm ? a.perm + (size_t)h * N : nullptr;
   // Buffer resources over this head's K and V (N rows of ROWB bytes).
   const int head_bytes = N * GE::ROWB;
@@ -241,16 +240,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     // ---- pass 1: online-softmax attention over the KV tiles ---------------
     float m_run[2] = {-1e30f, -1e30f};
     float l_run[2] = {0.f, 0.f};
-    float lref[2] = {-1e30f, -1e30f};  // this lane's maximum over the earlier tiles (low-part test)
     f32x4 oacc[DB][2];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto attend_tile = [&](int j, const char* cur, char* nxt, auto masked, auto f16) __attribute__((always_inline)) {
-      constexpr bool F16 = PRECISE_PV && decltype(f16)::value;   // P and V as float16
-      constexpr bool HILO = PRECISE_PV && !F16;                  // P as bf16 hi + lo
+    auto attend_tile = [&](int j, const char* cur, char* nxt, auto masked) {
+      constexpr bool F16 = PRECISE_PV;  // P and V as float16
       wait_vm<0>();
       __syncthreads();
       if (j + 1 < nt) {
@@ -323,25 +320,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
           for (int db = 0; db < DB; ++db) oacc[db][rb] *= alpha;
         }
       }
-      // The low part only matters where probabilities are large: the rounding
-      // error of the output is dominated by its largest terms.  A 16-row
-      // block whose probabilities in this tile all stay below 2^-kLoSkip of a
-      // reference neither forms nor multiplies its low parts.  The reference
-      // is the larger of the lazily kept running max and the lane's own
-      // maximum over the earlier tiles; both are at most the row's true
-      // maximum, so the skipped rounding errors are at most 2^-(9 + kLoSkip)
-      // of the largest term.  The decision is taken per row block from the
-      // lanes' maxima.
-      bool big[2] = {false, false};
-      if constexpr (HILO) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          big[rb] = __ballot(lmx[rb] > __builtin_fmaxf(m_run[rb], lref[rb]) - kLoSkip) != 0ull;
-          lref[rb] = __builtin_fmaxf(lref[rb], lmx[rb]);
-        }
-      }
-      bf16x8 pf[KC][2];
-      bf16x8 pl[HILO ? KC : 1][2];
+      bf16x8 pf[F16 ? 1 : KC][2];
       f16x8 ph[F16 ? KC : 1][2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
@@ -369,20 +348,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
                                       pack_bf16x2(s[2 * kc + 1][rb][0], s[2 * kc + 1][rb][1]),
                                       pack_bf16x2(s[2 * kc + 1][rb][2], s[2 * kc + 1][rb][3]));
           pf[kc][rb] = as_bf16x8(hi);
-          if constexpr (HILO) {
-            if (!big[rb]) continue;
-            // low part p - bf16(p), so that P = hi + lo to ~16 significant bits
-            const uint32_t h4[4] = {hi.x, hi.y, hi.z, hi.w};
-            uint32_t lo[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const f32x4 src = s[2 * kc + (e >> 1)][rb];
-              const float r0 = src[2 * (e & 1)] - __uint_as_float(h4[e] << 16);
-              const float r1 = src[2 * (e & 1) + 1] - __uint_as_float(h4[e] & 0xffff0000u);
-              lo[e] = pack_bf16x2(r0, r1);
-            }
-            pl[kc][rb] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-          }
         }
       }
 
@@ -400,52 +365,36 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
               oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vu), pf[kc][rb], oacc[db][rb], 0, 0, 0);
           }
         }
-      if constexpr (HILO) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          if (!big[rb]) continue;
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const bf16x8 vf = as_bf16x8(
-                  make_uint4(vr[kc][db][0].x, vr[kc][db][0].y, vr[kc][db][1].x, vr[kc][db][1].y));
-              oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[kc][rb], oacc[db][rb], 0, 0, 0);
-            }
-        }
-      }
     };
 
     fetch_rows(0);
     if (nt > 0) issue(st0, true);
     fetch_rows(1);
-    auto run_tiles = [&](auto f16) __attribute__((always_inline)) {
+    {
       const Flag<false> full;
       const Flag<true> ragged;
       const int nfull = (nkv % BK) ? nt - 1 : nt;   // tiles that need no masking
       int j = 0;
       for (; j + 1 < nfull; j += 2) {
-        attend_tile(j, st0, st1, full, f16);
-        attend_tile(j + 1, st1, st0, full, f16);
+        attend_tile(j, st0, st1, full);
+        attend_tile(j + 1, st1, st0, full);
       }
-      if (j < nfull) attend_tile(j++, st0, st1, full, f16);
+      if (j < nfull) attend_tile(j++, st0, st1, full);
       if (j < nt) {
         if (j & 1)
-          attend_tile(j, st1, st0, ragged, f16);
+          attend_tile(j, st1, st0, ragged);
         else
-          attend_tile(j, st0, st1, ragged, f16);
+          attend_tile(j, st0, st1, ragged);
       }
-    };
-    if (PRECISE_PV && use16)
-      run_tiles(Flag<true>());
-    else
-      run_tiles(Flag<false>());
+    }
 
     // ---- epilogue ---------------------------------------------------------
+    // the float16 V of the selection passes was scaled by 2^-vexp
+    const int vexp = PRECISE_PV ? a.v16_exp[h - a.head0] : 0;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const float l = quad_rows_sum(l_run[rb]);
-      const float inv = 1.0f / l;
+      const float inv = PRECISE_PV ? __builtin_ldexpf(1.0f / l, vexp) : 1.0f / l;
       const int r = RPW * w + 16 * rb + lr;
       const int p = row0 + r;
       if constexpr (MODE == MODE_SELECT) {

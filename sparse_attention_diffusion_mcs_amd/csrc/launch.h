@@ -19,8 +19,9 @@ struct AttnArgs {
   const void* q;
   const void* k;
   const void* v;
-  const void* v16;           // SELECT/RESINIT: V rounded to float16, [nheads][N][d] of the launch's heads, or null
-  const int* v16_bad;        // set (non-zero) when the rounding overflowed: the float16 copy is not used
+  const void* v16;           // SELECT/RESINIT (bf16): V * 2^-v16_exp[head] rounded to float16, [nheads][N][d] of
+                             // the launch's heads
+  const int* v16_exp;        // SELECT/RESINIT (bf16): per launch head, the power of two V was scaled down by
   void* o;                   // PLAIN/REUSE: output; SELECT: optional dense output (original order)
   void* residual;            // [H][N][d], sorted-position rows: float32, or bf16 when residual_bf16
   int residual_bf16;         // REUSE/RESINIT: the residual region holds bf16
@@ -55,9 +56,12 @@ hipError_t launch_attn_f32(int mode, const AttnArgs& a, hipStream_t s);
 hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, const double* mean, uint8_t* keys, int H,
                             int N, int D, hipStream_t s);
 hipError_t launch_query_mean(const void* q, int dtype, double* mean, int H, int N, int D, hipStream_t s);
-// bf16 V (n values, n a multiple of 8, 16-byte aligned) rounded to float16
-// into out; *bad is cleared first and set when a finite value overflows.
-hipError_t launch_v_to_f16(const void* v, void* out, long long n, int* bad, hipStream_t s);
+// The bf16 V of nheads heads (per_head values each, a multiple of 8, 16-byte
+// aligned) rounded to float16 into out, each head scaled by 2^-vexp[head]:
+// 0, or the smallest power of two that brings the head's largest finite
+// magnitude within float16's range.  hmax (nheads words) is scratch.
+hipError_t launch_v_to_f16(const void* v, void* out, int nheads, long long per_head, uint32_t* hmax, int* vexp,
+                           hipStream_t s);
 hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hipStream_t s);
 // Writes each group's kept keys (idx) and their number (count[h][g]); with
 // keep_mass > 0 the number comes from the retained-mass target (groups of G

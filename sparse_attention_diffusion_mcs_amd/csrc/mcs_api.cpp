@@ -120,14 +120,14 @@ uint64_t colsum_ld(int N) { return align_up((uint64_t)N, 64); }
 uint64_t block_ld(int N) { return align_up((uint64_t)(N + 63) / 64, 64); }
 
 struct WsLayout {
-  uint64_t off_keys, off_proj, off_mean, off_flag, off_colsum, per_head_colsum, per_head_block, per_head_lse,
+  uint64_t off_keys, off_proj, off_mean, off_vscale, off_colsum, per_head_colsum, per_head_block, per_head_lse,
       per_head_odense, per_head_v16, fixed;
   uint64_t per_head() const {
     return per_head_colsum + per_head_block + per_head_lse + per_head_odense + per_head_v16;
   }
 };
 
-// keys | projections | query means | float16 overflow flag | key scores [hc][ng][ldc] |
+// keys | projections | query means | V's per-head magnitude and float16 scale [2][H] | key scores [hc][ng][ldc] |
 // block scores [hc][ng][ldb] | row lse [hc][N] | float32 dense output [hc][N][d] (bf16 residual only) |
 // V rounded to float16 [hc][N][d] (bf16 problems)
 WsLayout ws_layout(const mcs_attn_desc* d, int32_t G, bool bf16_residual) {
@@ -137,8 +137,8 @@ WsLayout ws_layout(const mcs_attn_desc* d, int32_t G, bool bf16_residual) {
   w.off_keys = 0;
   w.off_proj = align_up(H * N, kAlign);
   w.off_mean = align_up(w.off_proj + (uint64_t)MCS_HASH_BITS * d->head_dim * 8, kAlign);
-  w.off_flag = align_up(w.off_mean + H * d->head_dim * 8, kAlign);
-  w.off_colsum = align_up(w.off_flag + 4, kAlign);
+  w.off_vscale = align_up(w.off_mean + H * d->head_dim * 8, kAlign);
+  w.off_colsum = align_up(w.off_vscale + 2 * H * 4, kAlign);
   w.per_head_colsum = ng * colsum_ld((int)N) * 4;
   w.per_head_block = ng * block_ld((int)N) * 4;
   w.per_head_lse = align_up(N * 4, kAlign);
@@ -413,7 +413,8 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
   void* v16 = wl.per_head_v16 ? at<void>(ws, wl.off_colsum + (uint64_t)hc * (wl.per_head_colsum + wl.per_head_block +
                                                                           wl.per_head_lse + wl.per_head_odense))
                               : nullptr;
-  int* v16_bad = at<int>(ws, wl.off_flag);
+  uint32_t* v16_max = at<uint32_t>(ws, wl.off_vscale);
+  int* v16_exp = at<int>(ws, wl.off_vscale + (uint64_t)H * 4);
   int32_t* perm = at<int32_t>(meta_buf, m.off_perm);
   if (o.grouping == MCS_GROUPING_HASH || o.grouping == MCS_GROUPING_CENTRED_HASH) {
     double* mean = nullptr;
@@ -460,11 +461,11 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
     a.o = o_dense_out;
     if (v16) {
       // the chunk's V in float16 for the selection's P·V products
-      if ((e = mcs::launch_v_to_f16(static_cast<const uint16_t*>(v) + (size_t)h0 * N * D, v16,
-                                    (long long)a.nheads * N * D, v16_bad, s)) != hipSuccess)
+      if ((e = mcs::launch_v_to_f16(static_cast<const uint16_t*>(v) + (size_t)h0 * N * D, v16, a.nheads,
+                                    (long long)N * D, v16_max, v16_exp, s)) != hipSuccess)
         return hip_fail(e);
       a.v16 = v16;
-      a.v16_bad = v16_bad;
+      a.v16_exp = v16_exp;
     }
     if ((e = launch_attn(d->dtype, mcs::MODE_SELECT, a, s)) != hipSuccess || (e = mark(1)) != hipSuccess)
       return hip_fail(e);

@@ -882,27 +882,56 @@ __global__ void block_scores_kernel(const float* __restrict__ colsum, int ldc, f
   bs[r * ldb + b] = sum;
 }
 
-// V rounded to float16 (nearest even) for the selection's P·V products:
-// eight values per thread and step.  A finite value that rounds to infinity
-// (|v| >= 65520) sets *bad, and the attention kernels then keep to bf16.
-__global__ void v_to_f16_kernel(const uint4* __restrict__ v, uint4* __restrict__ out, long long n8, int* bad) {
+// V rounded to float16 (nearest even) for the selection's P·V products, one
+// head per blockIdx.y, eight values per thread and step, scaled by 2^-e
+// (e = 0 in the first pass).  The first pass also records the head's
+// largest magnitude as a bit pattern (non-negative floats order like
+// unsigned integers; infinities and NaNs lie above every finite value).
+__device__ __forceinline__ uint4 v_f16_chunk(uint4 x, int e, uint32_t* amax) {
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  bool over = false;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (long long)gridDim.x * blockDim.x) {
-    const uint4 x = v[i];
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-    uint32_t o[4];
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xffff0000u);
-      const f16x2 hv = {(_Float16)a, (_Float16)b};
-      over |= (__builtin_isinf((float)hv[0]) && !__builtin_isinf(a)) ||
-              (__builtin_isinf((float)hv[1]) && !__builtin_isinf(b));
-      o[e] = __builtin_bit_cast(uint32_t, hv);
-    }
-    out[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  for (int k = 0; k < 4; ++k) {
+    *amax = max(*amax, max((w[k] << 16) & 0x7fffffffu, w[k] & 0x7fff0000u));
+    const float a = __builtin_ldexpf(__uint_as_float(w[k] << 16), -e);
+    const float b = __builtin_ldexpf(__uint_as_float(w[k] & 0xffff0000u), -e);
+    const f16x2 hv = {(_Float16)a, (_Float16)b};
+    o[k] = __builtin_bit_cast(uint32_t, hv);
   }
-  if (over) atomicOr(bad, 1);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__global__ __launch_bounds__(256) void v_to_f16_kernel(const uint4* __restrict__ v, uint4* __restrict__ out,
+                                                       long long per8, uint32_t* __restrict__ hmax) {
+  const size_t base = (size_t)blockIdx.y * per8;
+  uint32_t amax = 0;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < per8; i += (long long)gridDim.x * blockDim.x)
+    out[base + i] = v_f16_chunk(v[base + i], 0, &amax);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(&hmax[blockIdx.y], amax);
+}
+
+// The second pass: e = the smallest power of two that brings the head's
+// largest finite magnitude below 65520 (where float16 rounding overflows),
+// 0 when it is already below or V is not finite; heads with e > 0 are
+// rounded again.  vexp[head] = e for the attention kernels' epilogues.
+__global__ __launch_bounds__(256) void v_f16_rescale_kernel(const uint4* __restrict__ v, uint4* __restrict__ out,
+                                                            long long per8, const uint32_t* __restrict__ hmax,
+                                                            int* __restrict__ vexp) {
+  const uint32_t m = hmax[blockIdx.y];
+  int e = 0;
+  if (m >= 0x477ff000u && m < 0x7f800000u) {  // 65520 <= max < infinity
+    const float mx = __uint_as_float(m);
+    while (__builtin_ldexpf(mx, -e) >= 65520.f) ++e;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) vexp[blockIdx.y] = e;
+  if (e == 0) return;
+  const size_t base = (size_t)blockIdx.y * per8;
+  uint32_t unused = 0;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < per8; i += (long long)gridDim.x * blockDim.x)
+    out[base + i] = v_f16_chunk(v[base + i], e, &unused);
 }
 
 // Raster-order groups: perm[h][p] = p.
@@ -1040,16 +1069,20 @@ hipError_t launch_query_mean(const void* q, int dtype, double* mean, int H, int 
   return launched(s);
 }
 
-hipError_t launch_v_to_f16(const void* v, void* out, long long n, int* bad, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  if (n % 8) return hipErrorInvalidValue;
-  const int zero = 0;
-  hipError_t e = launch_fill_bytes(bad, &zero, sizeof(zero), s);
+hipError_t launch_v_to_f16(const void* v, void* out, int nheads, long long per_head, uint32_t* hmax, int* vexp,
+                           hipStream_t s) {
+  if (nheads == 0 || per_head == 0) return hipSuccess;
+  if (per_head % 8) return hipErrorInvalidValue;
+  hipError_t e = launch_zero_floats(reinterpret_cast<float*>(hmax), nheads, s);
   if (e != hipSuccess) return e;
-  const long long n8 = n / 8;
-  const long long blocks = std::min<long long>((n8 + 255) / 256, 4096);
-  hipLaunchKernelGGL(v_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const uint4*>(v),
-                     static_cast<uint4*>(out), n8, bad);
+  const long long per8 = per_head / 8;
+  const long long bx = std::max<long long>(1, std::min<long long>((per8 + 255) / 256, (2048 + nheads - 1) / nheads));
+  const dim3 grid((unsigned)bx, (unsigned)nheads);
+  hipLaunchKernelGGL(v_to_f16_kernel, grid, dim3(256), 0, s, static_cast<const uint4*>(v), static_cast<uint4*>(out),
+                     per8, hmax);
+  if ((e = launched(s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(v_f16_rescale_kernel, grid, dim3(256), 0, s, static_cast<const uint4*>(v),
+                     static_cast<uint4*>(out), per8, static_cast<const uint32_t*>(hmax), vexp);
   return launched(s);
 }
 

@@ -148,14 +148,15 @@ def test_reuse_on_selection_inputs_reproduces_dense():
 
 
 def test_selection_with_v_beyond_float16_range():
-    """The selection's P·V products run on float16 with V rounded once per
-    selection; a V holding values beyond float16's range (|v| >= 65520)
-    makes them fall back to bf16 with P as hi + lo parts.  V scaled by 2^16
-    (exact in bf16) overflows float16: the kept keys are unchanged (scores
-    do not involve V), every residual and dense value is finite, and the
-    results are 2^16 times the unscaled ones within the bf16 tolerances; the
-    unscaled ones meet the oracle in the other tests.  A scale of 2^17 gives
-    exactly twice the 2^16 results (the same bf16 path, powers of two)."""
+    """The selection's P·V products run on float16, with each head's V rounded
+    once per selection and scaled down by a power of two when its largest
+    magnitude would round to infinity (>= 65520); the epilogue scales back.
+    V scaled by 2^16 (exact in bf16) takes that path: the kept keys are
+    unchanged (scores do not involve V), every residual and dense value is
+    finite, and the results are 2^16 times the unscaled ones within the
+    bf16 tolerances (the unscaled ones meet the oracle in the other tests).
+    A scale of 2^17 rounds to the same float16 values with one more power of
+    two: exactly twice the 2^16 results."""
     _need_gpu()
     grid, H, d, G = (4, 8, 20), 2, 128, 64
     p = build_problem(grid, H, d, "bf16", G, [128, 300], 0.0, [1], wid=111)

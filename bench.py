@@ -582,7 +582,7 @@ def traffic_summary(fetch_db, write_db, out, grouping):
         others[label] = {"kernel": name, "fetch_bytes": int(round(fk * 1024 * fs)),
                          "write_bytes": int(round(wk * 1024 * ws)), "algorithmic_bytes": int(alg),
                          "launches_averaged": nk}
-    cmd = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c} -o pmc -- python3 bench.py --steps 1 --warmup 0 "
+    cmd = ("rocprofv3 --pmc {c} -d {d} -o {o} -- python3 bench.py --steps 1 --warmup 0 "
            "--no-cpu-baseline --copy-probe --no-zcurve --no-cold-cache" +
            ("" if grouping == "hash" else " --grouping " + grouping))
     res = {
@@ -595,7 +595,8 @@ def traffic_summary(fetch_db, write_db, out, grouping):
         "fetch_bytes": int(round(f_reuse * 1024 * fs)), "write_bytes": int(round(w_reuse * 1024 * ws)),
         "launches_averaged": min(n1, n2), "compulsory_bytes": compulsory,
         "selection_kernels": others,
-        "commands": [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE"),
+        "commands": [cmd.format(c="FETCH_SIZE", **profiler_out(fetch_db)),
+                     cmd.format(c="WRITE_SIZE", **profiler_out(write_db)),
                      f"python3 bench.py --traffic-summary {fetch_db} {write_db} {out} {grouping}"],
         "note": "FETCH_SIZE counts L2 misses served by the fabric (MALL or HBM); each counter is scaled by what it "
                 "reads for a plain 1 GiB device copy (--copy-probe). Compulsory = one read of Q, K, V, residual, "
@@ -616,6 +617,13 @@ COUNTER_PASSES = [
     "TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
 ]
 REUSE_KERNEL = "attn_bf16_kernel<128, 2, 2, 32>"
+
+
+def profiler_out(db):
+    """The -d directory and -o name of the rocprofv3 run that wrote `db`
+    (<dir>/<name>_results.db)."""
+    name = os.path.basename(db)
+    return {"d": os.path.dirname(db) or ".", "o": name[:-len("_results.db")] if name.endswith("_results.db") else name}
 
 
 def counter_summary(out, *args):
@@ -677,14 +685,14 @@ def counter_summary(out, *args):
         ("LDS bank-conflict cycles / LDS active cycles",
          vals.get("SQ_LDS_BANK_CONFLICT", float("nan")) / vals.get("SQ_LDS_IDX_ACTIVE", float("nan"))),
     ]
-    cmd = ("rocprofv3 --pmc {c} -d gpurun_out/cnt_{i} -o cnt -- python3 bench.py --steps 1 --warmup 0 "
+    cmd = ("rocprofv3 --pmc {c} -d {d} -o {o} -- python3 bench.py --steps 1 --warmup 0 "
            "--no-cpu-baseline --no-zcurve --no-cold-cache")
     what = "reuse launch" if kernel == REUSE_KERNEL else "launch"
     src = ATTN_SRC if "attn_bf16" in kernel else SELECT_SRC
     lines = [f"# Counters of the workload-2 {what} (`{kernel}`)", "",
              f"Source hash of `{os.path.basename(src)}`: `{src_hash(src)}`. Mean over the launch's dispatches in each pass; "
              f"median dispatch time under counter collection {dur * 1e3:.3f} ms.", "", "Commands:", ""]
-    lines += [f"- `{cmd.format(c=c, i=i + 1)}`" for i, c in enumerate(COUNTER_PASSES)]
+    lines += [f"- `{cmd.format(c=c, **profiler_out(db))}`" for c, db in zip(COUNTER_PASSES, dbs)]
     sel = "" if kernel == REUSE_KERNEL else f' --kernel "{kernel}"'
     lines += [f"- `python3 bench.py --counter-summary {out} {' '.join(dbs)}{sel}`", "",
               "| derived | value |", "|---|---|"]

@@ -908,9 +908,13 @@ __global__ __launch_bounds__(256) void v_to_f16_kernel(const uint4* __restrict__
   uint32_t amax = 0;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < per8; i += (long long)gridDim.x * blockDim.x)
     out[base + i] = v_f16_chunk(v[base + i], 0, &amax);
+  // one atomic per workgroup: the wave maxima meet in LDS first
+  __shared__ uint32_t wmax[4];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(&hmax[blockIdx.y], amax);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(&hmax[blockIdx.y], max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
 }
 
 // The second pass: e = the smallest power of two that brings the head's
@@ -1076,7 +1080,8 @@ hipError_t launch_v_to_f16(const void* v, void* out, int nheads, long long per_h
   hipError_t e = launch_zero_floats(reinterpret_cast<float*>(hmax), nheads, s);
   if (e != hipSuccess) return e;
   const long long per8 = per_head / 8;
-  const long long bx = std::max<long long>(1, std::min<long long>((per8 + 255) / 256, (2048 + nheads - 1) / nheads));
+  // about 4096 workgroups over all heads, a few 16-byte chunks per thread
+  const long long bx = std::max<long long>(1, std::min<long long>((per8 + 255) / 256, (4096 + nheads - 1) / nheads));
   const dim3 grid((unsigned)bx, (unsigned)nheads);
   hipLaunchKernelGGL(v_to_f16_kernel, grid, dim3(256), 0, s, static_cast<const uint4*>(v), static_cast<uint4*>(out),
                      per8, hmax);

@@ -36,95 +36,130 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return
 // projection is exact in float64 and one fused multiply-add per term gives
 // the same sum.
 //
-// A workgroup hashes tiles of HT consecutive tokens (rows of the flattened
-// [H*N] queries), tile blockIdx.x, then every gridDim.x-th tile after it.  A
-// tile's rows are copied with 16-byte loads that consecutive threads issue
-// for consecutive addresses; the loads of the next tile go out into
-// registers before the current tile is hashed, so the copy overlaps the
-// float64 arithmetic.  Each thread sums its own row from LDS in dimension
-// order, 8 dimensions per 16-byte LDS read.  The LDS rows are padded by 16
-// bytes: the row stride in 4-byte banks is then odd in units of four banks,
-// so the 16-byte reads of 32 lanes of different rows fall into distinct bank
-// groups.  The projections are read with uniform addresses (scalar loads).
-constexpr int HT = 128;
-constexpr int HASH_BLOCKS_PER_CU = 4;
+// A workgroup of two waves hashes tiles of HR consecutive tokens (rows of the
+// flattened [H*N] queries), tile blockIdx.x, then every gridDim.x-th tile
+// after it.  Lane r of wave w sums row r of the tile against projections
+// 4w .. 4w + 3, in dimension order.  The projection values are then the
+// same across the wave and come from scalar loads into SGPRs, batch by batch
+// (BD dimensions of four projections): batch m + 1 is loaded while batch m
+// is summed.  Scalar loads return out of order, so the wait for a batch
+// covers every load in flight, and it comes before the next batch's loads
+// are issued; an opaque zero added to each batch's base address keeps the
+// compiler from merging the batches' loads or hoisting them out of the tile
+// loop (1024 values do not fit in SGPRs).  A 64-row tile keeps the LDS per
+// workgroup small enough for four waves per SIMD.  A tile's rows are copied
+// with 16-byte buffer loads that consecutive threads issue for consecutive
+// addresses, one tile ahead, so the copy overlaps the arithmetic; the
+// buffer's range check returns zeros past the last row, so the loads need no
+// branches.  The LDS rows are padded by 16 bytes: the row stride in 4-byte
+// banks is then odd in units of four banks, so the 16-byte reads of 32 lanes
+// of different rows fall into distinct bank groups.  Each wave leaves its
+// four key bits in LDS, and the key bytes are written after the barrier
+// that ends the tile.
+constexpr int HT = 128;  // threads per workgroup: two waves
+constexpr int HR = 64;   // rows per tile
+constexpr int HASH_BLOCKS_PER_CU = 8;
 
 template <typename T, int D, bool CENTRED>
 __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, const double* __restrict__ proj,
                                                         const double* __restrict__ mean, uint8_t* __restrict__ keys,
                                                         long long total, int N) {
-  constexpr int ROWB = D * (int)sizeof(T);   // bytes per query row
-  constexpr int STRIDE = ROWB + 16;          // padded LDS row
-  constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
-  constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
-  constexpr int LPT = CPR;                   // 16-byte loads per thread per tile (HT rows * CPR chunks / HT)
-  __shared__ __attribute__((aligned(16))) unsigned char rows[HT * STRIDE];
-  const long long tiles = (total + HT - 1) / HT;
+  constexpr int ROWB = D * (int)sizeof(T);  // bytes per query row
+  constexpr int STRIDE = ROWB + 16;         // padded LDS row
+  constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
+  constexpr int LPT = HR * CPR / HT;        // 16-byte loads per thread per tile
+  constexpr int BD = 4;                     // dimensions per batch
+  constexpr int NBAT = D / BD;
+  constexpr int BPC = EPC / BD;             // batches per chunk
+  static_assert(EPC % BD == 0 && D % EPC == 0, "batches must tile the chunks");
+  __shared__ __attribute__((aligned(16))) unsigned char rows[HR * STRIDE];
+  __shared__ uint8_t part[2][HR];
+  const long long tiles = (total + HR - 1) / HR;
   const unsigned char* base = reinterpret_cast<const unsigned char*>(q);
-  // chunk e = threadIdx.x + HT * l of a tile: row e / CPR, chunk e % CPR;
-  // chunks past the last row of a ragged last tile load nothing (zeros)
+  const int r = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+
+  // chunk e = threadIdx.x + HT * l of tile t: row e / CPR, chunk e % CPR
+  auto load_tile = [&](uint4* buf, long long t) __attribute__((always_inline)) {
+    const long long start = t * (long long)(HR * ROWB);
+    const long long left = total * (long long)ROWB - start;
+    const int nbytes = left <= 0 ? 0 : (int)min(left, (long long)(HR * ROWB));
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (left > 0 ? start : 0)), (short)0, nbytes, 0x00020000);
+#pragma unroll
+    for (int l = 0; l < LPT; ++l) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (threadIdx.x + HT * l), 0, 0);
+      buf[l] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  };
+  // the 4 * BD values of batch m: projections 4w .. 4w + 3, dimensions BD m ..
+  auto load_batch = [&](double* p, int m) __attribute__((always_inline)) {
+    int opaque = 0;
+    asm volatile("" : "+s"(opaque));
+    const double* pm = proj + opaque + 4 * w * D + BD * m;
+#pragma unroll
+    for (int t = 0; t < 4 * BD; ++t) p[t] = pm[(t / BD) * D + t % BD];
+  };
+
   uint4 buf[LPT];
   long long tile = blockIdx.x;
-  if (tile < tiles) {
-    const int lim = (int)min((long long)HT, total - tile * HT) * CPR;
-#pragma unroll
-    for (int l = 0; l < LPT; ++l) {
-      const int e = threadIdx.x + HT * l;
-      buf[l] = e < lim ? *reinterpret_cast<const uint4*>(base + (size_t)tile * HT * ROWB + 16 * (size_t)e)
-                       : make_uint4(0, 0, 0, 0);
-    }
-  }
+  load_tile(buf, tile);
   for (; tile < tiles; tile += gridDim.x) {
-    const long long t0 = tile * HT;
-    const int nrows = (int)min((long long)HT, total - t0);
+    const long long t0 = tile * HR;
+    const int nrows = (int)min((long long)HR, total - t0);
 #pragma unroll
     for (int l = 0; l < LPT; ++l) {
       const int e = threadIdx.x + HT * l;
-      if (e < nrows * CPR) *reinterpret_cast<uint4*>(rows + (e / CPR) * STRIDE + 16 * (e % CPR)) = buf[l];
+      *reinterpret_cast<uint4*>(rows + (e / CPR) * STRIDE + 16 * (e % CPR)) = buf[l];
     }
     __syncthreads();
-    const long long nxt = tile + gridDim.x;
-    if (nxt < tiles) {
-      const int lim = (int)min((long long)HT, total - nxt * HT) * CPR;
+    load_tile(buf, tile + gridDim.x);
+    const long long i = t0 + min(r, nrows - 1);
+    const double* mu = CENTRED ? mean + (i / N) * D : nullptr;
+    const unsigned char* xr = rows + r * STRIDE;
+    double acc[4] = {0, 0, 0, 0};
+    double pr[2][4 * BD];
+    double xv[EPC];
+    uint4 u = *reinterpret_cast<const uint4*>(xr);
+    load_batch(pr[0], 0);
 #pragma unroll
-      for (int l = 0; l < LPT; ++l) {
-        const int e = threadIdx.x + HT * l;
-        buf[l] = e < lim ? *reinterpret_cast<const uint4*>(base + (size_t)nxt * HT * ROWB + 16 * (size_t)e)
-                         : make_uint4(0, 0, 0, 0);
-      }
-    }
-    const int r = threadIdx.x;
-    if (r < nrows) {
-      const long long i = t0 + r;
-      const double* mu = CENTRED ? mean + (i / N) * D : nullptr;
-      double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int c = 0; c < CPR; ++c) {
-        const uint4 u = *reinterpret_cast<const uint4*>(rows + r * STRIDE + 16 * c);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int m = 0; m < NBAT; ++m) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): batch m and the row's chunk m / BPC
+      __builtin_amdgcn_sched_barrier(0);
+      if (m % BPC == 0) {
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
-          double x;
           if constexpr (sizeof(T) == 2)
-            x = (double)bf16_to_f32((uint16_t)(w[e / 2] >> (16 * (e % 2))));
+            xv[e] = (double)bf16_to_f32((uint16_t)(wd[e / 2] >> (16 * (e % 2))));
           else
-            x = (double)__uint_as_float(w[e]);
-          const int dim = c * EPC + e;
-          if constexpr (CENTRED) {
-            const double xc = x - mu[dim];
+            xv[e] = (double)__uint_as_float(wd[e]);
+        }
+        if (m + BPC < NBAT) u = *reinterpret_cast<const uint4*>(xr + 16 * (m / BPC + 1));
+      }
+      if (m + 1 < NBAT) load_batch(pr[(m + 1) & 1], m + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int b = 0; b < 8; ++b) acc[b] = __dadd_rn(acc[b], __dmul_rn(xc, proj[b * D + dim]));
-          } else {
+      for (int d = 0; d < BD; ++d) {
+        const int dim = BD * m + d;
+        const double x = xv[dim % EPC];
+        if constexpr (CENTRED) {
+          const double xc = x - mu[dim];
 #pragma unroll
-            for (int b = 0; b < 8; ++b) acc[b] = __fma_rn(x, proj[b * D + dim], acc[b]);
-          }
+          for (int b = 0; b < 4; ++b) acc[b] = __dadd_rn(acc[b], __dmul_rn(xc, pr[m & 1][b * BD + d]));
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[b] = __fma_rn(x, pr[m & 1][b * BD + d], acc[b]);
         }
       }
-      uint32_t key = 0;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) key |= (acc[b] > 0.0 ? 1u : 0u) << b;
-      keys[i] = (uint8_t)key;
     }
-    __syncthreads();  // the rows are rewritten by the next tile
+    uint32_t bits = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bits |= (acc[b] > 0.0 ? 1u : 0u) << (4 * w + b);
+    part[w][r] = (uint8_t)bits;
+    __syncthreads();  // the rows are rewritten by the next tile; both halves of each key are in
+    if (threadIdx.x < nrows) keys[t0 + threadIdx.x] = (uint8_t)(part[0][threadIdx.x] | part[1][threadIdx.x]);
   }
 }
 
@@ -1006,7 +1041,7 @@ void hash_launch(const void* q, const double* proj, const double* mean, uint8_t*
                  hipStream_t s) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const long long tiles = (total + HT - 1) / HT;
+  const long long tiles = (total + HR - 1) / HR;
   const dim3 grid((unsigned)std::min<long long>(tiles, (long long)std::max(cus, 1) * HASH_BLOCKS_PER_CU));
   if (mean)
     hipLaunchKernelGGL((hash_keys_kernel<T, D, true>), grid, dim3(HT), 0, s, static_cast<const T*>(q), proj, mean,

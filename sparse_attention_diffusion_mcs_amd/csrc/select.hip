@@ -47,7 +47,8 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return
 // are issued; an opaque zero added to each batch's base address keeps the
 // compiler from merging the batches' loads or hoisting them out of the tile
 // loop (1024 values do not fit in SGPRs).  A 64-row tile keeps the LDS per
-// workgroup small enough for four waves per SIMD.  A tile's rows are copied
+// workgroup (17.5 KB at d = 128 in bf16) small enough for nine workgroups,
+// 18 waves, per CU.  A tile's rows are copied
 // with 16-byte buffer loads that consecutive threads issue for consecutive
 // addresses, one tile ahead, so the copy overlaps the arithmetic; the
 // buffer's range check returns zeros past the last row, so the loads need no
@@ -58,7 +59,7 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return
 // that ends the tile.
 constexpr int HT = 128;  // threads per workgroup: two waves
 constexpr int HR = 64;   // rows per tile
-constexpr int HASH_BLOCKS_PER_CU = 8;
+constexpr int HASH_BLOCKS_PER_CU = 9;
 
 template <typename T, int D, bool CENTRED>
 __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, const double* __restrict__ proj,

@@ -7,7 +7,9 @@ per-group top-k, selection-time sparse pass and residual) on the step-0
 inputs, followed by every reuse step on that step's drifted inputs.  All
 inputs are generated (seeded, synthetic) and resident in device memory before
 the timed region.  The library's own dense attention is timed on the same
-inputs as the speedup baseline.
+inputs as the speedup baseline.  Workload 6 is the joint attention of an
+MM-DiT block: workload 2's video tokens followed by 226 text tokens in one
+sequence.
 
 Prints one JSON line: `value` is the mean reuse-step time in ms (lower is
 better), with the speedup over dense, the selection time, the amortised time
@@ -60,7 +62,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from mcs_inputs import WORKLOADS, hash_projections, head_base, head_step, position_embedding  # noqa: E402
+from mcs_inputs import WORKLOADS, hash_projections, head_base, head_step, token_embedding  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
@@ -79,7 +81,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5, help="timed denoising segments")
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6])
     ap.add_argument("--keep", type=float, default=None, help="override the keep fraction")
     ap.add_argument("--group", type=int, default=None, help="override the group size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -118,14 +120,15 @@ def describe(w, keeps):
     ks = sorted(set(int(k) for k in keeps))
     kdesc = str(ks[0]) if len(ks) == 1 else "/".join(map(str, ks))
     T, Y, X = w.grid
-    return (f"{w.name}: H={w.heads}, N={w.seq_len} ({T}x{Y}x{X}), d={w.head_dim}, {w.dtype}, G={w.group}, "
+    toks = f"{T}x{Y}x{X}" + (f" + {w.text} text" if w.text else "")
+    return (f"{w.name}: H={w.heads}, N={w.seq_len} ({toks}), d={w.head_dim}, {w.dtype}, G={w.group}, "
             f"k={kdesc} per group, select once + {w.reuse_steps} reuse steps, drift {w.drift}*t")
 
 
 def generate(w, steps, threads, seed=0):
     """Device tensors per step: {t: (q, k, v)} in [H, N, d] bf16."""
     import torch
-    pos = position_embedding(w.grid, w.head_dim)
+    pos = token_embedding(w.grid, w.head_dim, w.text, seed, w.wid)
     H, N, d = w.heads, w.seq_len, w.head_dim
     bases = [None] * H
 
@@ -170,7 +173,7 @@ def cpu_baseline(w, keeps, T, scale, n_groups, seed=0):
     extra = rng.choice(np.arange(2, ng - 1), size=max(0, min(n_groups, ng) - len(set(fixed))), replace=False)
     groups = sorted(set(fixed) | set(int(x) for x in extra))
     tsteps = sorted({1, max(1, T // 2), T})
-    pos = position_embedding(w.grid, d)
+    pos = token_embedding(w.grid, d, w.text, seed, w.wid)
     proj = hash_projections(seed, w.wid, d)
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])

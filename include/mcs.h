@@ -318,7 +318,9 @@ typedef struct mcs_select_options {
                         multiples of 64 (else MCS_ERROR_UNSUPPORTED_SHAPE) */
   int32_t residual;  /* 1: cache O_dense - O_sparse (MC-Sparse); 0: cache zeros, so reuse returns the
                         sparse output renormalised over the kept keys alone */
-  int32_t grid_t, grid_y, grid_x;  /* MCS_GROUPING_MORTON: the latent grid, each in [1, 1024], product N;
+  int32_t grid_t, grid_y, grid_x;  /* MCS_GROUPING_MORTON: the latent grid, each in [1, 1024], product at
+                                      most N; tokens from the product on (the text tokens of a joint
+                                      video + text sequence) follow the grid's tokens in index order;
                                       0 for every other grouping */
   /* Extensions of the method (zero selects the method as read):
      residual_dtype  MCS_DTYPE_FP32 or, for bf16 problems, MCS_DTYPE_BF16: the cached residual

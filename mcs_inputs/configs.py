@@ -2,7 +2,9 @@
 
 Workload 1 is the tiny fp32 case an exact CPU implementation finishes in
 seconds; 2 and 3 are single video-DiT attention layers; 4 is a 3D-asset DiT
-layer with a per-head keep budget; 5 is a full denoising-loop sweep.  The
+layer with a per-head keep budget; 5 is a full denoising-loop sweep; 6 is the
+joint attention of an MM-DiT block, workload 2's video tokens followed by text
+tokens in one sequence.  The
 pages name the two model families (a video DiT and a 3D asset generator) but
 none of their shapes, so the shapes here are DiT-typical stand-ins.
 """
@@ -43,10 +45,11 @@ class Workload:
     reselect: int = 0             # re-selection interval (0 = select once)
     keep_override: int | None = None
     sweep: dict = field(default_factory=dict)
+    text: int = 0                 # text tokens after the grid tokens (joint attention)
 
     @property
     def seq_len(self) -> int:
-        return int(np.prod(self.grid))
+        return int(np.prod(self.grid)) + self.text
 
     @property
     def num_groups(self) -> int:
@@ -79,6 +82,8 @@ WORKLOADS = {
     5: Workload(5, "denoising-loop sweep, 40 heads, 21x30x52", (21, 30, 52), 40, 128, "bf16", 64, (0.10,), 9,
                 0.02, reselect=10,
                 sweep={"keep": (0.02, 0.05, 0.10, 0.25, 1.0), "group": (64, 128), "steps": 30}),
+    6: Workload(6, "joint video+text DiT layer, 24 heads, 16x30x52 + 226 text", (16, 30, 52), 24, 128, "bf16", 64,
+                (0.10,), 10, 0.02, text=226),
 }
 
 

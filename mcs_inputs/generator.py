@@ -19,6 +19,11 @@ seeded by SeedSequence([seed, workload_id, stream, head, step])):
 * per head h: W_h = orthogonal factor of a QR of a Gaussian d x d matrix with
   the signs fixed so that diag(R) > 0;
   Q = 3 P W_h + 0.5 E_Q,  K = 3 P W_h + 0.5 E_K,  V = E_V;
+* joint video + text sequences (the joint attention of MM-DiT blocks, whose
+  text tokens are appended to the latent tokens): L text tokens follow the
+  N_v grid tokens, each with an embedding T_j = sqrt(d/2) * u_j / |u_j|,
+  u_j a Gaussian vector (stream 9, shared by all heads), in place of P;
+  they enter Q, K and V exactly as grid tokens do;
 * step t > 0: X_t = X_0 + delta * t * E_t with E_t freshly drawn per step,
   per tensor and per head (not a random walk);
 * the float32 master is rounded to bfloat16 (round to nearest even) for the
@@ -32,6 +37,7 @@ import numpy as np
 STREAM_W, STREAM_EQ, STREAM_EK, STREAM_EV = 0, 1, 2, 3
 STREAM_DQ, STREAM_DK, STREAM_DV = 4, 5, 6
 STREAM_PROJ, STREAM_KEEP = 7, 8
+STREAM_TEXT = 9
 
 _DRIFT_STREAMS = (STREAM_DQ, STREAM_DK, STREAM_DV)
 
@@ -61,6 +67,24 @@ def position_embedding(grid, d: int) -> np.ndarray:
         parts.append(np.sin(ang))
         parts.append(np.cos(ang))
     return np.concatenate(parts, axis=1).astype(np.float32)
+
+
+def text_embedding(seed: int, workload_id: int, n_text: int, d: int) -> np.ndarray:
+    """Embeddings of n_text text tokens, float32 [n_text, d], each of squared
+    norm d/2 (that of every grid token's position embedding) in a Gaussian
+    random direction."""
+    u = _normal(rng(seed, workload_id, STREAM_TEXT), (n_text, d)).astype(np.float64)
+    u *= np.sqrt(d / 2.0) / np.maximum(np.linalg.norm(u, axis=1, keepdims=True), 1e-300)
+    return u.astype(np.float32)
+
+
+def token_embedding(grid, d: int, n_text: int = 0, seed: int = 0, workload_id: int = 0) -> np.ndarray:
+    """Embedding of every token of a sequence: the grid tokens in raster order
+    (position_embedding), then n_text text tokens (text_embedding)."""
+    pos = position_embedding(grid, d)
+    if n_text <= 0:
+        return pos
+    return np.concatenate([pos, text_embedding(seed, workload_id, n_text, d)], axis=0)
 
 
 def head_rotation(seed: int, workload_id: int, head: int, d: int) -> np.ndarray:

@@ -143,12 +143,18 @@ def morton_code(t: np.ndarray, y: np.ndarray, x: np.ndarray) -> np.ndarray:
     return code
 
 
-def morton_permutation(grid) -> np.ndarray:
+def morton_permutation(grid, n: int | None = None) -> np.ndarray:
     """Tokens of a raster-ordered (T, Y, X) grid (token = (t * Y + y) * X + x)
-    sorted by their Z-curve code."""
-    tt, yy, xx = np.meshgrid(*(np.arange(n) for n in grid), indexing="ij")
+    sorted by their Z-curve code; the tokens from T*Y*X to n - 1 (the text
+    tokens of a joint video + text sequence) follow in index order."""
+    tt, yy, xx = np.meshgrid(*(np.arange(m) for m in grid), indexing="ij")
     code = morton_code(tt.ravel(), yy.ravel(), xx.ravel())
-    return np.argsort(code, kind="stable").astype(np.int32)
+    grid_perm = np.argsort(code, kind="stable").astype(np.int32)
+    n_grid = grid_perm.size
+    n = n_grid if n is None else n
+    if n < n_grid:
+        raise ValueError("the grid holds more tokens than the sequence")
+    return np.concatenate([grid_perm, np.arange(n_grid, n, dtype=np.int32)])
 
 
 def group_ranges(n: int, group: int):
@@ -367,10 +373,10 @@ def select_head(q, k, v, proj, group, keep, scale, groups=None, grouping="hash",
         keys = np.zeros(n, dtype=np.uint8)
         perm = raster_permutation(n)
     elif grouping == "morton":
-        if grid is None or int(np.prod(grid)) != n:
+        if grid is None or int(np.prod(grid)) > n:
             raise ValueError("morton grouping needs the (T, Y, X) grid of the tokens")
         keys = np.zeros(n, dtype=np.uint8)
-        perm = morton_permutation(grid)
+        perm = morton_permutation(grid, n)
     else:
         raise ValueError(f"unknown grouping {grouping!r}")
     ranges = group_ranges(n, group)

@@ -363,7 +363,8 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
   if (o.grouping == MCS_GROUPING_MORTON) {
     for (int g : {o.grid_t, o.grid_y, o.grid_x})
       if (g < 1 || g > 1024) return MCS_ERROR_INVALID_VALUE;
-    if ((int64_t)o.grid_t * o.grid_y * o.grid_x != d->seq_len) return MCS_ERROR_INVALID_VALUE;
+    // tokens past the grid (text tokens of a joint sequence) follow it in order
+    if ((int64_t)o.grid_t * o.grid_y * o.grid_x > d->seq_len) return MCS_ERROR_INVALID_VALUE;
   } else if (o.grid_t != 0 || o.grid_y != 0 || o.grid_x != 0) {
     return MCS_ERROR_INVALID_VALUE;
   }

@@ -993,6 +993,10 @@ __device__ __forceinline__ long long clipped(int lo, int len, int size) {
 __global__ void morton_perm_kernel(int32_t* __restrict__ perm, int H, int N, int T, int Y, int X) {
   const int tok = blockIdx.x * blockDim.x + threadIdx.x;
   if (tok >= N) return;
+  if (tok >= T * Y * X) {  // past the grid: the trailing tokens keep their order
+    for (int h = 0; h < H; ++h) perm[(size_t)h * N + tok] = tok;
+    return;
+  }
   const int x = tok % X, y = (tok / X) % Y, t = tok / (X * Y);
   const int size[3] = {X, Y, T}, coord[3] = {x, y, t};
   int lo[3] = {0, 0, 0}, len[3] = {1024, 1024, 1024};

@@ -382,6 +382,9 @@ def check_morton_groups(impl):
     last = {c: i for i, c in enumerate(cell.tolist())}
     for c in first:
         assert last[c] - first[c] + 1 == int(np.sum(cell == c)), "a 2x2x2 cell is split"
+    # a joint sequence: the 5 tokens past a 1 x 2 x 4 grid keep their order after it
+    assert impl.morton_permutation((1, 2, 4), 13).tolist() == [0, 1, 4, 5, 2, 3, 6, 7, 8, 9, 10, 11, 12]
+    assert impl.morton_permutation((1, 2, 4), 8).tolist() == [0, 1, 4, 5, 2, 3, 6, 7]
 
 
 def check_no_residual(impl, seed=15):

@@ -28,7 +28,7 @@ import numpy as np
 import torch
 
 import oracle.mcs_oracle as orc
-from mcs_inputs import hash_projections, head_base, head_step, position_embedding
+from mcs_inputs import hash_projections, head_base, head_step, token_embedding
 
 THREADS = min(16, os.cpu_count() or 8)
 GAP = 1e-6
@@ -53,10 +53,11 @@ class Problem:
     wid: int = 100
     heads_np: dict = field(default_factory=dict)   # (head, step) -> (q, k, v) float32
     dev: dict = field(default_factory=dict)        # step -> (q, k, v) device tensors
+    text: int = 0                # text tokens after the grid tokens (a joint sequence)
 
     @property
     def N(self):
-        return int(np.prod(self.grid))
+        return int(np.prod(self.grid)) + self.text
 
     @property
     def ng(self):
@@ -70,12 +71,13 @@ class Problem:
         return hash_projections(self.seed, self.wid, self.d)
 
 
-def build_problem(grid, H, d, dtype, G, keeps, drift, steps, seed=0, wid=100, keep_heads=None) -> Problem:
+def build_problem(grid, H, d, dtype, G, keeps, drift, steps, seed=0, wid=100, keep_heads=None, text=0) -> Problem:
     """Generates step 0 and the listed reuse steps for every head, uploads
     them, and keeps the float32 host copies of the heads in keep_heads (all
-    heads if None) for the oracle."""
-    p = Problem(tuple(grid), H, d, dtype, G, np.asarray(keeps, np.int32), drift, list(steps), seed, wid)
-    pos = position_embedding(grid, d)
+    heads if None) for the oracle.  `text` text tokens follow the grid's
+    tokens (a joint video + text sequence)."""
+    p = Problem(tuple(grid), H, d, dtype, G, np.asarray(keeps, np.int32), drift, list(steps), seed, wid, text=text)
+    pos = token_embedding(grid, d, text, seed, wid)
     bf = dtype == "bf16"
     bases = [None] * H
 

@@ -4,7 +4,7 @@ import numpy as np
 import torch
 
 from mcs_inputs import (WORKLOADS, bf16_bits, hash_projections, head_base, head_rotation, head_step,
-                        keep_count, position_embedding, round_bf16)
+                        keep_count, position_embedding, round_bf16, text_embedding, token_embedding)
 
 
 def test_position_embedding_norm_and_origin():
@@ -68,4 +68,19 @@ def test_workload_sizes():
     assert WORKLOADS[1].seq_len == 1024 and WORKLOADS[2].seq_len == 24960
     assert WORKLOADS[3].seq_len == 75600 and WORKLOADS[3].num_groups == 1182
     assert WORKLOADS[4].seq_len == 32768 and WORKLOADS[5].seq_len == 32760
+    w6 = WORKLOADS[6]
+    assert w6.seq_len == 24960 + 226 and w6.num_groups == 394 and w6.keeps()[0] == 2496
     assert hash_projections(0, 1, 64).shape == (8, 64)
+
+
+def test_text_tokens_follow_the_grid():
+    """Joint sequences: the grid tokens' position embeddings, then text
+    embeddings of the same squared norm d/2, seeded, independent of the grid."""
+    for d in (64, 128):
+        e = token_embedding((2, 3, 4), d, 7, seed=3, workload_id=6)
+        assert e.shape == (31, d)
+        assert np.array_equal(e[:24], position_embedding((2, 3, 4), d))
+        assert np.array_equal(e[24:], text_embedding(3, 6, 7, d))
+        assert np.allclose((e[24:].astype(np.float64) ** 2).sum(1), d / 2, rtol=1e-6)
+        assert not np.array_equal(text_embedding(3, 6, 7, d), text_embedding(4, 6, 7, d))
+    assert np.array_equal(token_embedding((2, 3, 4), 64), position_embedding((2, 3, 4), 64))

@@ -180,7 +180,7 @@ def test_select_ex_options_validation(lib):
     assert call(O(0, 1, 2)) == L.MCS_ERROR_INVALID_VALUE          # residual flag not 0 / 1
     assert call(O(0, 1, 1, 2, 8, 8)) == L.MCS_ERROR_INVALID_VALUE   # grid given to a non-grid grouping
     assert call(O(3, 1, 1)) == L.MCS_ERROR_INVALID_VALUE          # Z-curve without a grid
-    assert call(O(3, 1, 1, 2, 8, 9)) == L.MCS_ERROR_INVALID_VALUE   # grid does not hold N tokens
+    assert call(O(3, 1, 1, 2, 8, 9)) == L.MCS_ERROR_INVALID_VALUE   # grid holds more than N tokens
     assert call(O(3, 1, 1, 1, 2, 2048)) == L.MCS_ERROR_INVALID_VALUE  # a dimension above 1024
     odd, op = _i32([64, 100])
     assert call(O(0, 64, 1), keep_p=op) == L.MCS_ERROR_UNSUPPORTED_SHAPE   # keep not whole blocks

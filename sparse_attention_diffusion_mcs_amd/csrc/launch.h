@@ -52,9 +52,13 @@ hipError_t launch_attn_bf16(int mode, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(int mode, const AttnArgs& a, hipStream_t s);
 
 // selection helpers (select.hip)
-// mean: per-head query means (float64 [H][D]) for the centred hash, or null
-hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, const double* mean, uint8_t* keys, int H,
-                            int N, int D, hipStream_t s);
+// proj: the projections as float64 [8][D], then as float32 [8][D], then the
+// float32 coefficient of each projection's decision threshold [8];
+// mean: per-head query means (float64 [H][D]) for the centred hash, or null;
+// undecided: H*N bytes of scratch (the key bits the float32 pass leaves to
+// the float64 one)
+hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, const double* mean, uint8_t* keys,
+                            uint8_t* undecided, int H, int N, int D, hipStream_t s);
 hipError_t launch_query_mean(const void* q, int dtype, double* mean, int H, int N, int D, hipStream_t s);
 // The bf16 V of nheads heads (per_head values each, a multiple of 8, 16-byte
 // aligned) rounded to float16 into out, each head scaled by 2^-vexp[head]:

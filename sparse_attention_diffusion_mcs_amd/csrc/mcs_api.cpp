@@ -119,15 +119,49 @@ uint64_t colsum_ld(int N) { return align_up((uint64_t)N, 64); }
 // Leading dimension of the 64-key block scores of one score row.
 uint64_t block_ld(int N) { return align_up((uint64_t)(N + 63) / 64, 64); }
 
+// Hash projections in the workspace: float64 [8][d], float32 [8][d], then the
+// float32 coefficient of each projection's decision threshold (see
+// hash_tables).
+uint64_t hash_table_bytes(int d) { return (uint64_t)MCS_HASH_BITS * d * 12 + MCS_HASH_BITS * 4; }
+
+// The projection tables of the hash kernel.  A float32 sum S32 of d terms
+// decides the sign of the float64 sum the key is defined by whenever |S32|
+// exceeds (1 + 2^-8) (gamma_d(2^-24) + gamma_d(2^-53)) |r_b| |q| (plus terms
+// for underflow); gamma_n(u) = n u / (1 - n u) bounds the error of a
+// recursive sum of n rounded terms relative to the sum of their magnitudes,
+// which Cauchy-Schwarz bounds by |r_b| |q|.  The coefficient before |q| is
+// computed in float64 and rounded up to float32.
+std::vector<uint8_t> hash_tables(const float* proj, int d) {
+  std::vector<uint8_t> out(hash_table_bytes(d));
+  double* p64 = reinterpret_cast<double*>(out.data());
+  float* p32 = reinterpret_cast<float*>(out.data() + (size_t)MCS_HASH_BITS * d * 8);
+  float* coef = p32 + (size_t)MCS_HASH_BITS * d;
+  const double g32 = d * 0x1p-24 / (1.0 - d * 0x1p-24), g64 = d * 0x1p-53 / (1.0 - d * 0x1p-53);
+  for (int b = 0; b < MCS_HASH_BITS; ++b) {
+    double n2 = 0.0;
+    for (int c = 0; c < d; ++c) {
+      const float r = proj[(size_t)b * d + c];
+      p64[(size_t)b * d + c] = (double)r;
+      p32[(size_t)b * d + c] = r;
+      n2 += (double)r * (double)r;
+    }
+    const double cb = (1.0 + 0x1p-8) * (g32 + g64) * std::sqrt(n2);
+    float c32 = (float)cb;
+    if ((double)c32 < cb) c32 = std::nextafter(c32, INFINITY);
+    coef[b] = c32;
+  }
+  return out;
+}
+
 struct WsLayout {
-  uint64_t off_keys, off_proj, off_mean, off_vscale, off_colsum, per_head_colsum, per_head_block, per_head_lse,
+  uint64_t off_keys, off_undecided, off_proj, off_mean, off_vscale, off_colsum, per_head_colsum, per_head_block, per_head_lse,
       per_head_odense, per_head_v16, fixed;
   uint64_t per_head() const {
     return per_head_colsum + per_head_block + per_head_lse + per_head_odense + per_head_v16;
   }
 };
 
-// keys | projections | query means | V's per-head magnitude and float16 scale [2][H] | key scores [hc][ng][ldc] |
+// keys | undecided key bits | projections | query means | V's per-head magnitude and float16 scale [2][H] | key scores [hc][ng][ldc] |
 // block scores [hc][ng][ldb] | row lse [hc][N] | float32 dense output [hc][N][d] (bf16 residual only) |
 // V rounded to float16 [hc][N][d] (bf16 problems)
 WsLayout ws_layout(const mcs_attn_desc* d, int32_t G, bool bf16_residual) {
@@ -135,8 +169,9 @@ WsLayout ws_layout(const mcs_attn_desc* d, int32_t G, bool bf16_residual) {
   const uint64_t ng = (N + G - 1) / G;
   WsLayout w;
   w.off_keys = 0;
-  w.off_proj = align_up(H * N, kAlign);
-  w.off_mean = align_up(w.off_proj + (uint64_t)MCS_HASH_BITS * d->head_dim * 8, kAlign);
+  w.off_undecided = align_up(H * N, kAlign);
+  w.off_proj = align_up(w.off_undecided + H * N, kAlign);
+  w.off_mean = align_up(w.off_proj + hash_table_bytes(d->head_dim), kAlign);
   w.off_vscale = align_up(w.off_mean + H * d->head_dim * 8, kAlign);
   w.off_colsum = align_up(w.off_vscale + 2 * H * 4, kAlign);
   w.per_head_colsum = ng * colsum_ld((int)N) * 4;
@@ -400,8 +435,7 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   if ((st = upload_meta_tables(&m, keep, s)) != MCS_SUCCESS) return st;
-  std::vector<double> proj64((size_t)MCS_HASH_BITS * D);
-  for (size_t i = 0; i < proj64.size(); ++i) proj64[i] = (double)proj[i];
+  const std::vector<uint8_t> ptab = hash_tables(proj, D);
   hipError_t e;
   double* dproj = at<double>(ws, wl.off_proj);
   uint8_t* keys = at<uint8_t>(ws, wl.off_keys);
@@ -423,8 +457,10 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
       mean = at<double>(ws, wl.off_mean);
       if ((e = mcs::launch_query_mean(q, d->dtype, mean, H, N, D, s)) != hipSuccess) return hip_fail(e);
     }
-    if ((e = mcs::launch_fill_bytes(dproj, proj64.data(), proj64.size() * 8, s)) != hipSuccess) return hip_fail(e);
-    if ((e = mcs::launch_hash_keys(q, d->dtype, dproj, mean, keys, H, N, D, s)) != hipSuccess) return hip_fail(e);
+    if ((e = mcs::launch_fill_bytes(dproj, ptab.data(), ptab.size(), s)) != hipSuccess) return hip_fail(e);
+    if ((e = mcs::launch_hash_keys(q, d->dtype, dproj, mean, keys, at<uint8_t>(ws, wl.off_undecided), H, N, D, s)) !=
+        hipSuccess)
+      return hip_fail(e);
     if ((e = mcs::launch_perm_sort(keys, perm, H, N, s)) != hipSuccess) return hip_fail(e);
   } else if (o.grouping == MCS_GROUPING_MORTON) {
     if ((e = mcs::launch_morton_perm(perm, H, N, o.grid_t, o.grid_y, o.grid_x, s)) != hipSuccess) return hip_fail(e);

@@ -29,12 +29,29 @@ __device__ __forceinline__ float load_elem<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
+// The key bit of token i and projection b is [S > 0] for S = q_i . r_b
+// accumulated in float64 in dimension order, one fused multiply-add per term
+// (every product of a bf16/float32 value and a float32 projection is exact in
+// float64).  The kernel first forms S32, the same sum in float32.  With
+// A = sum_c |q_ic r_bc| <= |q_i| |r_b| (Cauchy-Schwarz), the two sums of D
+// rounded terms are within gamma_D(u) A of the exact sum (the standard bound
+// of recursive summation, u = 2^-24 and 2^-53), the float32 one also within
+// an absolute D * 2^-126 when results underflow.  So whenever
+//   |S32| > (1 + 2^-8) (gamma_D(2^-24) + gamma_D(2^-53)) |r_b| sqrt(|q_i|^2 + 2^-100) + 2^-100
+// (the factor 1 + 2^-8 covers the rounding of this threshold, computed in
+// float32 from the float32 |q_i|^2, whose own error is at most gamma_D(2^-24)
+// relative plus the underflow the 2^-100 term absorbs; the coefficient per
+// projection comes from the host, rounded up), the exact sum has the sign of S32 and a magnitude above
+// the float64 sum's error, and the float64 sum has the same sign: the bit is
+// decided.  The bits left undecided (|S32| below the threshold, or not
+// finite) are marked per token, and a second kernel recomputes their sums in
+// float64 exactly as defined (hash_fixup_kernel); on Gaussian projections
+// about one token in a thousand has such a bit.
+//
 // With CENTRED the queries are first centred on their head's mean (`mean`,
 // float64 [H][D]); each product and each addition is then rounded on its own
 // (__dmul_rn, __dadd_rn), because the centred values no longer multiply
-// exactly.  Without it every product of a bf16/float32 value and a float32
-// projection is exact in float64 and one fused multiply-add per term gives
-// the same sum.
+// exactly, and the sums are taken in float64 only.
 //
 // A workgroup of two waves hashes tiles of HR consecutive tokens (rows of the
 // flattened [H*N] queries), tile blockIdx.x, then every gridDim.x-th tile
@@ -46,7 +63,7 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return
 // covers every load in flight, and it comes before the next batch's loads
 // are issued; an opaque zero added to each batch's base address keeps the
 // compiler from merging the batches' loads or hoisting them out of the tile
-// loop (1024 values do not fit in SGPRs).  A 64-row tile keeps the LDS per
+// loop (the projections do not fit in SGPRs).  A 64-row tile keeps the LDS per
 // workgroup (17.5 KB at d = 128 in bf16) small enough for nine workgroups,
 // 18 waves, per CU.  A tile's rows are copied
 // with 16-byte buffer loads that consecutive threads issue for consecutive
@@ -60,11 +77,14 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return
 constexpr int HT = 128;  // threads per workgroup: two waves
 constexpr int HR = 64;   // rows per tile
 constexpr int HASH_BLOCKS_PER_CU = 9;
+constexpr int kHashBits = 8;  // projections: two waves of four
 
 template <typename T, int D, bool CENTRED>
 __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, const double* __restrict__ proj,
+                                                        const float* __restrict__ proj32,
+                                                        const float* __restrict__ coef,
                                                         const double* __restrict__ mean, uint8_t* __restrict__ keys,
-                                                        long long total, int N) {
+                                                        uint8_t* __restrict__ undecided_out, long long total, int N) {
   constexpr int ROWB = D * (int)sizeof(T);  // bytes per query row
   constexpr int STRIDE = ROWB + 16;         // padded LDS row
   constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
@@ -76,6 +96,7 @@ __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, 
   static_assert(EPC % BD == 0 && D % EPC == 0, "batches must tile the chunks");
   __shared__ __attribute__((aligned(16))) unsigned char rows[HR * STRIDE];
   __shared__ uint8_t part[2][HR];
+  __shared__ uint8_t part_und[2][HR];
   const long long tiles = (total + HR - 1) / HR;
   const unsigned char* base = reinterpret_cast<const unsigned char*>(q);
   const int r = threadIdx.x & 63;
@@ -102,6 +123,21 @@ __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, 
 #pragma unroll
     for (int t = 0; t < 4 * BD; ++t) p[t] = pm[(t / BD) * D + t % BD];
   };
+  // float32 path: the 4 * BD values of batch m, as load_batch
+  auto load_batch32 = [&](float* p, int m) __attribute__((always_inline)) {
+    int opaque = 0;
+    asm volatile("" : "+s"(opaque));
+    const float* pm = proj32 + opaque + 4 * w * D + BD * m;
+#pragma unroll
+    for (int t = 0; t < 4 * BD; ++t) p[t] = pm[(t / BD) * D + t % BD];
+  };
+  // element e of the 16-byte chunk held in wd
+  auto elem = [&](const uint32_t* wd, int e) __attribute__((always_inline)) -> float {
+    if constexpr (sizeof(T) == 2)
+      return __uint_as_float(e % 2 ? (wd[e / 2] & 0xffff0000u) : (wd[e / 2] << 16));
+    else
+      return __uint_as_float(wd[e]);
+  };
 
   uint4 buf[LPT];
   long long tile = blockIdx.x;
@@ -116,9 +152,49 @@ __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, 
     }
     __syncthreads();
     load_tile(buf, tile + gridDim.x);
-    const long long i = t0 + min(r, nrows - 1);
-    const double* mu = CENTRED ? mean + (i / N) * D : nullptr;
     const unsigned char* xr = rows + r * STRIDE;
+    uint32_t bits = 0, undecided = 0;
+    if constexpr (!CENTRED) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      float nrm = 0.f;
+      float pr[2][4 * BD];
+      uint32_t wd[4];
+      uint4 u = *reinterpret_cast<const uint4*>(xr);
+      load_batch32(pr[0], 0);
+#pragma unroll
+      for (int m = 0; m < NBAT; ++m) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): batch m and the row's chunk m / BPC
+        __builtin_amdgcn_sched_barrier(0);
+        if (m % BPC == 0) {
+          wd[0] = u.x, wd[1] = u.y, wd[2] = u.z, wd[3] = u.w;
+          if (m + BPC < NBAT) u = *reinterpret_cast<const uint4*>(xr + 16 * (m / BPC + 1));
+        }
+        if (m + 1 < NBAT) load_batch32(pr[(m + 1) & 1], m + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < BD; ++d) {
+          const float x = elem(wd, (BD * m + d) % EPC);
+          nrm = fmaf(x, x, nrm);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[b] = fmaf(x, pr[m & 1][b * BD + d], acc[b]);
+        }
+        // all five sums advance batch by batch (otherwise the compiler may
+        // run the projections one after the other over the whole row, with
+        // every element of the row held in registers)
+        asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(nrm));
+      }
+      const float xn = __builtin_sqrtf(nrm + 0x1p-100f);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float a = __builtin_fabsf(acc[b]);
+        if (a > fmaf(coef[4 * w + b], xn, 0x1p-100f) && a <= 3.40282347e38f)
+          bits |= (acc[b] > 0.f ? 1u : 0u) << (4 * w + b);
+        else
+          undecided |= 1u << (4 * w + b);
+      }
+    } else {
+    const long long i = t0 + min(r, nrows - 1);
+    const double* mu = mean + (i / N) * D;
     double acc[4] = {0, 0, 0, 0};
     double pr[2][4 * BD];
     double xv[EPC];
@@ -144,24 +220,66 @@ __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, 
 #pragma unroll
       for (int d = 0; d < BD; ++d) {
         const int dim = BD * m + d;
-        const double x = xv[dim % EPC];
-        if constexpr (CENTRED) {
-          const double xc = x - mu[dim];
+        const double xc = xv[dim % EPC] - mu[dim];
 #pragma unroll
-          for (int b = 0; b < 4; ++b) acc[b] = __dadd_rn(acc[b], __dmul_rn(xc, pr[m & 1][b * BD + d]));
-        } else {
-#pragma unroll
-          for (int b = 0; b < 4; ++b) acc[b] = __fma_rn(x, pr[m & 1][b * BD + d], acc[b]);
-        }
+        for (int b = 0; b < 4; ++b) acc[b] = __dadd_rn(acc[b], __dmul_rn(xc, pr[m & 1][b * BD + d]));
       }
     }
-    uint32_t bits = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) bits |= (acc[b] > 0.0 ? 1u : 0u) << (4 * w + b);
+    }
     part[w][r] = (uint8_t)bits;
+    if constexpr (!CENTRED) part_und[w][r] = (uint8_t)undecided;
     __syncthreads();  // the rows are rewritten by the next tile; both halves of each key are in
-    if (threadIdx.x < nrows) keys[t0 + threadIdx.x] = (uint8_t)(part[0][threadIdx.x] | part[1][threadIdx.x]);
+    if (threadIdx.x < nrows) {
+      keys[t0 + threadIdx.x] = (uint8_t)(part[0][threadIdx.x] | part[1][threadIdx.x]);
+      if constexpr (!CENTRED)
+        undecided_out[t0 + threadIdx.x] = (uint8_t)(part_und[0][threadIdx.x] | part_und[1][threadIdx.x]);
+    }
   }
+}
+
+// The undecided key bits of the float32 pass: one thread per token.  A
+// workgroup with any such token stages the float64 projections in LDS; each
+// of its tokens with undecided bits loads its query row into registers and
+// forms each such bit's float64 sum in dimension order, one fused
+// multiply-add per term, as the key is defined.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void hash_fixup_kernel(const T* __restrict__ q, const double* __restrict__ proj,
+                                                         const uint8_t* __restrict__ undecided,
+                                                         uint8_t* __restrict__ keys, long long total) {
+  __shared__ double pl[kHashBits * D];
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte load
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t und = i < total ? undecided[i] : 0u;
+  if (!__syncthreads_or(und != 0u)) return;  // uniform across the workgroup
+  for (int t = threadIdx.x; t < kHashBits * D; t += blockDim.x) pl[t] = proj[t];
+  __syncthreads();
+  if (und == 0u) return;
+  uint4 row[D / EPC];
+  const uint4* src = reinterpret_cast<const uint4*>(q + i * D);
+#pragma unroll
+  for (int c = 0; c < D / EPC; ++c) row[c] = src[c];
+  uint32_t key = keys[i];
+  for (int b = 0; b < kHashBits; ++b) {
+    if (!((und >> b) & 1u)) continue;
+    double acc = 0.0;
+#pragma unroll
+    for (int c = 0; c < D / EPC; ++c) {
+      uint32_t wd[4] = {row[c].x, row[c].y, row[c].z, row[c].w};
+      // converted per projection: hoisted out of the loop over b, the row's
+      // float64 values would take four times the registers
+      asm volatile("" : "+v"(wd[0]), "+v"(wd[1]), "+v"(wd[2]), "+v"(wd[3]));
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const float x = sizeof(T) == 2 ? __uint_as_float(e % 2 ? (wd[e / 2] & 0xffff0000u) : (wd[e / 2] << 16))
+                                       : __uint_as_float(wd[e]);
+        acc = __fma_rn((double)x, pl[b * D + EPC * c + e], acc);
+      }
+    }
+    key = (key & ~(1u << b)) | ((acc > 0.0 ? 1u : 0u) << b);
+  }
+  keys[i] = (uint8_t)key;
 }
 
 // Per-dimension mean of each head's queries: one thread per (head, dim),
@@ -1042,18 +1160,23 @@ __global__ void fill_words_kernel(uint32_t* dst, FillPayload p, int n) {
 
 namespace {
 template <typename T, int D>
-void hash_launch(const void* q, const double* proj, const double* mean, uint8_t* keys, long long total, int N,
-                 hipStream_t s) {
+void hash_launch(const void* q, const double* proj, const double* mean, uint8_t* keys, uint8_t* undecided,
+                 long long total, int N, hipStream_t s) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const long long tiles = (total + HR - 1) / HR;
   const dim3 grid((unsigned)std::min<long long>(tiles, (long long)std::max(cus, 1) * HASH_BLOCKS_PER_CU));
-  if (mean)
-    hipLaunchKernelGGL((hash_keys_kernel<T, D, true>), grid, dim3(HT), 0, s, static_cast<const T*>(q), proj, mean,
-                       keys, total, N);
-  else
+  const float* proj32 = reinterpret_cast<const float*>(proj + kHashBits * D);
+  const float* coef = proj32 + kHashBits * D;
+  if (mean) {
+    hipLaunchKernelGGL((hash_keys_kernel<T, D, true>), grid, dim3(HT), 0, s, static_cast<const T*>(q), proj, proj32,
+                       coef, mean, keys, undecided, total, N);
+  } else {
     hipLaunchKernelGGL((hash_keys_kernel<T, D, false>), grid, dim3(HT), 0, s, static_cast<const T*>(q), proj,
-                       mean, keys, total, N);
+                       proj32, coef, mean, keys, undecided, total, N);
+    hipLaunchKernelGGL((hash_fixup_kernel<T, D>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const T*>(q), proj, undecided, keys, total);
+  }
 }
 // Sort key of each group's launch order: floor(m * 256 / N) for its median
 // kept key m (entry count/2 of the ascending list), one thread per group.
@@ -1075,20 +1198,20 @@ __global__ __launch_bounds__(256) void group_bucket_kernel(const int32_t* __rest
 
 }  // namespace
 
-hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, const double* mean, uint8_t* keys, int H,
-                            int N, int D, hipStream_t s) {
+hipError_t launch_hash_keys(const void* q, int dtype, const double* proj, const double* mean, uint8_t* keys,
+                            uint8_t* undecided, int H, int N, int D, hipStream_t s) {
   const long long total = (long long)H * N;
   if (total == 0) return hipSuccess;
   if (dtype == 1) {
     if (D == 64)
-      hash_launch<uint16_t, 64>(q, proj, mean, keys, total, N, s);
+      hash_launch<uint16_t, 64>(q, proj, mean, keys, undecided, total, N, s);
     else
-      hash_launch<uint16_t, 128>(q, proj, mean, keys, total, N, s);
+      hash_launch<uint16_t, 128>(q, proj, mean, keys, undecided, total, N, s);
   } else {
     if (D == 64)
-      hash_launch<float, 64>(q, proj, mean, keys, total, N, s);
+      hash_launch<float, 64>(q, proj, mean, keys, undecided, total, N, s);
     else
-      hash_launch<float, 128>(q, proj, mean, keys, total, N, s);
+      hash_launch<float, 128>(q, proj, mean, keys, undecided, total, N, s);
   }
   return launched(s);
 }

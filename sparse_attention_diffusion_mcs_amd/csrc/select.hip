@@ -239,47 +239,78 @@ __global__ __launch_bounds__(HT) void hash_keys_kernel(const T* __restrict__ q, 
   }
 }
 
-// The undecided key bits of the float32 pass: one thread per token.  A
-// workgroup with any such token stages the float64 projections in LDS; each
-// of its tokens with undecided bits loads its query row into registers and
-// forms each such bit's float64 sum in dimension order, one fused
-// multiply-add per term, as the key is defined.
+// The undecided key bits of the float32 pass.  A workgroup stages the
+// float64 projections in LDS, then each wave walks runs of 256 tokens (four
+// flag bytes per lane); the tokens with undecided bits are taken eight at a
+// time, lane 8j + b forming bit b of the j-th such token as its float64 sum
+// in dimension order, one fused multiply-add per term, as the key is
+// defined; lane 8j then writes that token's corrected key.
+constexpr int FIXUP_BLOCKS = 512;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void hash_fixup_kernel(const T* __restrict__ q, const double* __restrict__ proj,
                                                          const uint8_t* __restrict__ undecided,
                                                          uint8_t* __restrict__ keys, long long total) {
-  __shared__ double pl[kHashBits * D];
   constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte load
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const uint32_t und = i < total ? undecided[i] : 0u;
-  if (!__syncthreads_or(und != 0u)) return;  // uniform across the workgroup
+  __shared__ double pl[kHashBits * D];
   for (int t = threadIdx.x; t < kHashBits * D; t += blockDim.x) pl[t] = proj[t];
   __syncthreads();
-  if (und == 0u) return;
-  uint4 row[D / EPC];
-  const uint4* src = reinterpret_cast<const uint4*>(q + i * D);
-#pragma unroll
-  for (int c = 0; c < D / EPC; ++c) row[c] = src[c];
-  uint32_t key = keys[i];
-  for (int b = 0; b < kHashBits; ++b) {
-    if (!((und >> b) & 1u)) continue;
-    double acc = 0.0;
-#pragma unroll
-    for (int c = 0; c < D / EPC; ++c) {
-      uint32_t wd[4] = {row[c].x, row[c].y, row[c].z, row[c].w};
-      // converted per projection: hoisted out of the loop over b, the row's
-      // float64 values would take four times the registers
-      asm volatile("" : "+v"(wd[0]), "+v"(wd[1]), "+v"(wd[2]), "+v"(wd[3]));
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const float x = sizeof(T) == 2 ? __uint_as_float(e % 2 ? (wd[e / 2] & 0xffff0000u) : (wd[e / 2] << 16))
-                                       : __uint_as_float(wd[e]);
-        acc = __fma_rn((double)x, pl[b * D + EPC * c + e], acc);
-      }
+  const int lane = threadIdx.x & 63;
+  const long long nwaves = (long long)gridDim.x * (blockDim.x >> 6);
+  const long long wid = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  for (long long base = wid * 256; base < total; base += nwaves * 256) {
+    const long long i0 = base + 4 * lane;
+    uint32_t f4 = 0;
+    if (i0 + 4 <= total) {
+      f4 = *reinterpret_cast<const uint32_t*>(undecided + i0);  // the flags start 256-byte aligned
+    } else {
+      for (int j = 0; j < 4 && i0 + j < total; ++j) f4 |= (uint32_t)undecided[i0 + j] << (8 * j);
     }
-    key = (key & ~(1u << b)) | ((acc > 0.0 ? 1u : 0u) << b);
+    // tokens (4 per lane) with undecided bits, in order
+    uint64_t lanes = __ballot(f4 != 0u);
+    uint32_t mine = f4;  // this lane's flags, consumed token by token
+    while (lanes) {
+      // gather up to eight tokens: slot j of the round is token tok[j]
+      long long tok = -1;
+      uint32_t fl = 0;
+      int filled = 0;
+      while (lanes && filled < 8) {
+        const int src = __builtin_ctzll(lanes);
+        const uint32_t fsrc = (uint32_t)__shfl((int)mine, src);
+        const int j = __builtin_ctz(fsrc) / 8;  // first token of that lane with flags
+        const uint32_t fj = (fsrc >> (8 * j)) & 0xffu;
+        if (lane / 8 == filled) {
+          tok = base + 4 * src + j;
+          fl = fj;
+        }
+        if (lane == src) mine &= ~(0xffu << (8 * j));
+        const uint32_t rest = fsrc & ~(0xffu << (8 * j));
+        if (rest == 0u) lanes &= lanes - 1;
+        ++filled;
+      }
+      const int b = lane & 7;
+      bool pos = false;
+      if (tok >= 0 && ((fl >> b) & 1u)) {
+        const uint4* src = reinterpret_cast<const uint4*>(q + tok * D);
+        uint4 row[D / EPC];
+#pragma unroll
+        for (int c = 0; c < D / EPC; ++c) row[c] = src[c];
+        double acc = 0.0;
+#pragma unroll
+        for (int c = 0; c < D / EPC; ++c) {
+          const uint32_t wd[4] = {row[c].x, row[c].y, row[c].z, row[c].w};
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            const float x = sizeof(T) == 2 ? __uint_as_float(e % 2 ? (wd[e / 2] & 0xffff0000u) : (wd[e / 2] << 16))
+                                           : __uint_as_float(wd[e]);
+            acc = __fma_rn((double)x, pl[b * D + EPC * c + e], acc);
+          }
+        }
+        pos = acc > 0.0;
+      }
+      const uint32_t set = (uint32_t)(__ballot(pos) >> (lane & ~7)) & 0xffu;
+      if (b == 0 && tok >= 0) keys[tok] = (uint8_t)((keys[tok] & ~fl) | (set & fl));
+    }
   }
-  keys[i] = (uint8_t)key;
 }
 
 // Per-dimension mean of each head's queries: one thread per (head, dim),
@@ -301,66 +332,115 @@ __global__ __launch_bounds__(D) void query_mean_kernel(const T* __restrict__ q, 
   mean[(size_t)h * D + c] = sum / (double)N;
 }
 
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  // DPP: shifts by 1, 2, 4, 8 within each row of 16 lanes (a lane whose
+  // source lies before its row adds 0), then lane 15 of rows 0 and 2 is added
+  // to rows 1 and 3, and lane 31 to rows 2 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // ---------------------------------------------------------- stable sort ----
 // One workgroup per head.  A 256-bin histogram gives each key's first
-// position; tokens are then placed tile by tile in token order, with the rank
-// among equal keys inside a wave found by ballots over the 8 key bits and
-// across the waves of a tile by an ordered prefix over per-wave counts, so the
-// result is the stable order.
+// position (an exclusive scan by four waves); tokens are then placed tile by
+// tile in token order, SORT_KPT runs of 64 tokens per wave and tile, so that
+// a tile's key loads go out together.  Wave w of a tile takes the contiguous
+// tokens t0 + 64 (SORT_KPT w + s) + lane, run s after run s - 1: the rank
+// among equal keys inside a run comes from ballots over the 8 key bits,
+// offset by the wave's running count of that key (cnt[w][key], advanced by
+// the run's lowest lane), and across the waves by an ordered prefix over the
+// per-wave counts, so the result is the stable order.
 constexpr int SORT_NT = 1024;
 constexpr int SORT_NW = SORT_NT / 64;
+constexpr int SORT_KPT = 8;  // runs of 64 tokens per wave and tile
 
 __global__ __launch_bounds__(SORT_NT) void perm_sort_kernel(const uint8_t* __restrict__ keys,
                                                             int32_t* __restrict__ perm, int N) {
   __shared__ int hist[256];
   __shared__ int base[256];
   __shared__ int cnt[SORT_NW][256];
+  __shared__ int wsum[4];
   const int h = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const uint8_t* kh = keys + (size_t)h * N;
   int32_t* ph = perm + (size_t)h * N;
 
   if (tid < 256) hist[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < N; i += SORT_NT) atomicAdd(&hist[kh[i]], 1);
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int b = 0; b < 256; ++b) {
-      base[b] = run;
-      run += hist[b];
+  // eight key loads in flight per thread, then their counts: not one round
+  // trip per key
+  for (int i0 = tid; i0 < N; i0 += SORT_NT * SORT_KPT) {
+    int k[SORT_KPT];
+#pragma unroll
+    for (int j = 0; j < SORT_KPT; ++j) {
+      const int i = i0 + j * SORT_NT;
+      k[j] = i < N ? kh[i] : -1;
     }
+#pragma unroll
+    for (int j = 0; j < SORT_KPT; ++j)
+      if (k[j] >= 0) atomicAdd(&hist[k[j]], 1);
+  }
+  __syncthreads();
+  int hv = 0, hinc = 0;
+  if (tid < 256) {
+    hv = hist[tid];
+    hinc = wave_incl_scan(hv);
+    if (lane == 63) wsum[w] = hinc;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int off = 0;
+    for (int ww = 0; ww < w; ++ww) off += wsum[ww];
+    base[tid] = off + hinc - hv;
   }
   __syncthreads();
 
   const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int t0 = 0; t0 < N; t0 += SORT_NT) {
+  constexpr int TILE = SORT_NT * SORT_KPT;
+  for (int t0 = 0; t0 < N; t0 += TILE) {
     for (int e = tid; e < SORT_NW * 256; e += SORT_NT) (&cnt[0][0])[e] = 0;
-    __syncthreads();
-    const int i = t0 + tid;
-    const bool valid = i < N;
-    const int key = valid ? kh[i] : 0;
-    unsigned long long same = __ballot(valid);
+    int key[SORT_KPT];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool bit = (key >> b) & 1;
-      const unsigned long long bb = __ballot(valid && bit);
-      same &= bit ? bb : ~bb;
+    for (int r = 0; r < SORT_KPT; ++r) {
+      const int i = t0 + 64 * (SORT_KPT * w + r) + lane;
+      key[r] = i < N ? kh[i] : -1;
     }
-    const int rank = __popcll(same & lt_mask);
-    const bool leader = valid && (same >> lane) == 1ull;
-    if (leader) cnt[w][key] = __popcll(same);
+    __syncthreads();
+    int rank[SORT_KPT];
+#pragma unroll
+    for (int r = 0; r < SORT_KPT; ++r) {
+      const bool valid = key[r] >= 0;
+      unsigned long long same = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const bool bit = (key[r] >> b) & 1;
+        const unsigned long long bb = __ballot(valid && bit);
+        same &= bit ? bb : ~bb;
+      }
+      // every lane of a key reads the wave's count before its lowest lane
+      // advances it (one wave: the read instruction precedes the write)
+      const int before = valid ? cnt[w][key[r]] : 0;
+      rank[r] = before + __popcll(same & lt_mask);
+      if (valid && (same & lt_mask) == 0ull) cnt[w][key[r]] = before + __popcll(same);
+    }
     __syncthreads();
     if (tid < 256) {
-      int r = base[tid];
+      int run = base[tid];
       for (int ww = 0; ww < SORT_NW; ++ww) {
         const int c = cnt[ww][tid];
-        cnt[ww][tid] = r;
-        r += c;
+        cnt[ww][tid] = run;
+        run += c;
       }
-      base[tid] = r;
+      base[tid] = run;
     }
     __syncthreads();
-    if (valid) ph[cnt[w][key] + rank] = i;
+#pragma unroll
+    for (int r = 0; r < SORT_KPT; ++r)
+      if (key[r] >= 0) ph[cnt[w][key[r]] + rank[r]] = t0 + 64 * (SORT_KPT * w + r) + lane;
     __syncthreads();
   }
 }
@@ -404,18 +484,6 @@ constexpr int TK_SHORT_WORDS = 1074;
 constexpr int TK_MASK_KEYS = 1 << 17;  // longest row of the mask path (16 KB of LDS)
 constexpr int TK_SAMPLE_LINES = 128;   // 32-key lines of the band's sample (16 keys per thread)
 
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  // DPP: shifts by 1, 2, 4, 8 within each row of 16 lanes (a lane whose
-  // source lies before its row adds 0), then lane 15 of rows 0 and 2 is added
-  // to rows 1 and 3, and lane 31 to rows 2 and 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
 
 // Exclusive block scan of two counters; returns the totals through *ta/*tb.
 __device__ __forceinline__ void block_excl_scan2(int a, int b, int* ea, int* eb, int* ta, int* tb, int* sh) {
@@ -1174,8 +1242,9 @@ void hash_launch(const void* q, const double* proj, const double* mean, uint8_t*
   } else {
     hipLaunchKernelGGL((hash_keys_kernel<T, D, false>), grid, dim3(HT), 0, s, static_cast<const T*>(q), proj,
                        proj32, coef, mean, keys, undecided, total, N);
-    hipLaunchKernelGGL((hash_fixup_kernel<T, D>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       static_cast<const T*>(q), proj, undecided, keys, total);
+    const long long fblocks = std::min<long long>(FIXUP_BLOCKS, (total + 1023) / 1024);
+    hipLaunchKernelGGL((hash_fixup_kernel<T, D>), dim3((unsigned)fblocks), dim3(256), 0, s, static_cast<const T*>(q),
+                       proj, undecided, keys, total);
   }
 }
 // Sort key of each group's launch order: floor(m * 256 / N) for its median

@@ -66,7 +66,10 @@ hipError_t launch_query_mean(const void* q, int dtype, double* mean, int H, int 
 // magnitude within float16's range.  hmax (nheads words) is scratch.
 hipError_t launch_v_to_f16(const void* v, void* out, int nheads, long long per_head, uint32_t* hmax, int* vexp,
                            hipStream_t s);
-hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hipStream_t s);
+// Stable sort of each head's token keys; counts: H * 256 * sort_chunks(N)
+// int32 of scratch
+int sort_chunks(int N);
+hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int32_t* counts, int H, int N, hipStream_t s);
 // Writes each group's kept keys (idx) and their number (count[h][g]); with
 // keep_mass > 0 the number comes from the retained-mass target (groups of G
 // of the nq queries), else it is keep[h] / block blocks.

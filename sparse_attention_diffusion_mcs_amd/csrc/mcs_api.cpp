@@ -154,14 +154,14 @@ std::vector<uint8_t> hash_tables(const float* proj, int d) {
 }
 
 struct WsLayout {
-  uint64_t off_keys, off_undecided, off_proj, off_mean, off_vscale, off_colsum, per_head_colsum, per_head_block, per_head_lse,
+  uint64_t off_keys, off_undecided, off_sortcnt, off_proj, off_mean, off_vscale, off_colsum, per_head_colsum, per_head_block, per_head_lse,
       per_head_odense, per_head_v16, fixed;
   uint64_t per_head() const {
     return per_head_colsum + per_head_block + per_head_lse + per_head_odense + per_head_v16;
   }
 };
 
-// keys | undecided key bits | projections | query means | V's per-head magnitude and float16 scale [2][H] | key scores [hc][ng][ldc] |
+// keys | undecided key bits | sort counts [H][256][chunks] | projections | query means | V's per-head magnitude and float16 scale [2][H] | key scores [hc][ng][ldc] |
 // block scores [hc][ng][ldb] | row lse [hc][N] | float32 dense output [hc][N][d] (bf16 residual only) |
 // V rounded to float16 [hc][N][d] (bf16 problems)
 WsLayout ws_layout(const mcs_attn_desc* d, int32_t G, bool bf16_residual) {
@@ -170,7 +170,8 @@ WsLayout ws_layout(const mcs_attn_desc* d, int32_t G, bool bf16_residual) {
   WsLayout w;
   w.off_keys = 0;
   w.off_undecided = align_up(H * N, kAlign);
-  w.off_proj = align_up(w.off_undecided + H * N, kAlign);
+  w.off_sortcnt = align_up(w.off_undecided + H * N, kAlign);
+  w.off_proj = align_up(w.off_sortcnt + H * 256 * (uint64_t)mcs::sort_chunks((int)N) * 4, kAlign);
   w.off_mean = align_up(w.off_proj + hash_table_bytes(d->head_dim), kAlign);
   w.off_vscale = align_up(w.off_mean + H * d->head_dim * 8, kAlign);
   w.off_colsum = align_up(w.off_vscale + 2 * H * 4, kAlign);
@@ -461,7 +462,8 @@ mcs_status select_impl(const mcs_attn_desc* d, const void* q, const void* k, con
     if ((e = mcs::launch_hash_keys(q, d->dtype, dproj, mean, keys, at<uint8_t>(ws, wl.off_undecided), H, N, D, s)) !=
         hipSuccess)
       return hip_fail(e);
-    if ((e = mcs::launch_perm_sort(keys, perm, H, N, s)) != hipSuccess) return hip_fail(e);
+    if ((e = mcs::launch_perm_sort(keys, perm, at<int32_t>(ws, wl.off_sortcnt), H, N, s)) != hipSuccess)
+      return hip_fail(e);
   } else if (o.grouping == MCS_GROUPING_MORTON) {
     if ((e = mcs::launch_morton_perm(perm, H, N, o.grid_t, o.grid_y, o.grid_x, s)) != hipSuccess) return hip_fail(e);
   } else if ((e = mcs::launch_iota_perm(perm, H, N, s)) != hipSuccess) {

@@ -445,6 +445,106 @@ __global__ __launch_bounds__(SORT_NT) void perm_sort_kernel(const uint8_t* __res
   }
 }
 
+// The token sort over several workgroups per head.  The head's tokens are
+// cut into chunks of CSORT_CHUNK; sort_hist_kernel counts each chunk's keys
+// (counts[h][key][chunk]); sort_scan_kernel turns the counts in place into
+// each (key, chunk)'s first sorted position: the keys in order, and for each
+// key the chunks in token order; sort_scatter_kernel places a chunk's tokens
+// from those positions with the ranks of perm_sort_kernel's tile, so that
+// equal keys keep their token order across and within the chunks.
+constexpr int CSORT_NT = 1024;
+constexpr int CSORT_KPT = 4;  // runs of 64 tokens per wave: 4096-token chunks
+constexpr int CSORT_CHUNK = CSORT_NT * CSORT_KPT;
+
+__global__ __launch_bounds__(CSORT_NT) void sort_hist_kernel(const uint8_t* __restrict__ keys,
+                                                             int32_t* __restrict__ counts, int N, int nch) {
+  __shared__ int hist[256];
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const uint8_t* kh = keys + (size_t)h * N;
+  if (tid < 256) hist[tid] = 0;
+  __syncthreads();
+  int k[CSORT_KPT];
+#pragma unroll
+  for (int r = 0; r < CSORT_KPT; ++r) {
+    const int i = c * CSORT_CHUNK + r * CSORT_NT + tid;
+    k[r] = i < N ? kh[i] : -1;
+  }
+#pragma unroll
+  for (int r = 0; r < CSORT_KPT; ++r)
+    if (k[r] >= 0) atomicAdd(&hist[k[r]], 1);
+  __syncthreads();
+  if (tid < 256) counts[((size_t)h * 256 + tid) * nch + c] = hist[tid];
+}
+
+__global__ __launch_bounds__(256) void sort_scan_kernel(int32_t* __restrict__ counts, int nch) {
+  __shared__ int wsum[4];
+  const int h = blockIdx.x, b = threadIdx.x, w = b >> 6, lane = b & 63;
+  int32_t* row = counts + ((size_t)h * 256 + b) * nch;
+  int total = 0;
+  for (int c = 0; c < nch; ++c) total += row[c];
+  const int inc = wave_incl_scan(total);
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  int run = inc - total;
+  for (int ww = 0; ww < w; ++ww) run += wsum[ww];
+  for (int c = 0; c < nch; ++c) {
+    const int v = row[c];
+    row[c] = run;
+    run += v;
+  }
+}
+
+__global__ __launch_bounds__(CSORT_NT) void sort_scatter_kernel(const uint8_t* __restrict__ keys,
+                                                                const int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ perm, int N, int nch) {
+  __shared__ int base[256];
+  __shared__ int cnt[SORT_NW][256];
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const uint8_t* kh = keys + (size_t)h * N;
+  int32_t* ph = perm + (size_t)h * N;
+  const int t0 = c * CSORT_CHUNK;
+  for (int e = tid; e < SORT_NW * 256; e += CSORT_NT) (&cnt[0][0])[e] = 0;
+  if (tid < 256) base[tid] = offsets[((size_t)h * 256 + tid) * nch + c];
+  int key[CSORT_KPT];
+#pragma unroll
+  for (int r = 0; r < CSORT_KPT; ++r) {
+    const int i = t0 + 64 * (CSORT_KPT * w + r) + lane;
+    key[r] = i < N ? kh[i] : -1;
+  }
+  __syncthreads();
+  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rank[CSORT_KPT];
+#pragma unroll
+  for (int r = 0; r < CSORT_KPT; ++r) {
+    const bool valid = key[r] >= 0;
+    unsigned long long same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (key[r] >> b) & 1;
+      const unsigned long long bb = __ballot(valid && bit);
+      same &= bit ? bb : ~bb;
+    }
+    // every lane of a key reads the wave's count before its lowest lane
+    // advances it (one wave: the read instruction precedes the write)
+    const int before = valid ? cnt[w][key[r]] : 0;
+    rank[r] = before + __popcll(same & lt_mask);
+    if (valid && (same & lt_mask) == 0ull) cnt[w][key[r]] = before + __popcll(same);
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int run = base[tid];
+    for (int ww = 0; ww < SORT_NW; ++ww) {
+      const int n = cnt[ww][tid];
+      cnt[ww][tid] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < CSORT_KPT; ++r)
+    if (key[r] >= 0) ph[cnt[w][key[r]] + rank[r]] = t0 + 64 * (CSORT_KPT * w + r) + lane;
+}
+
 // ---------------------------------------------------------------- top-k ----
 // One workgroup per (head, group) score row.  Scores are non-negative floats,
 // so their bit patterns order like the values, and the k-th largest pattern T
@@ -1323,9 +1423,18 @@ hipError_t launch_v_to_f16(const void* v, void* out, int nheads, long long per_h
   return launched(s);
 }
 
-hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int H, int N, hipStream_t s) {
+int sort_chunks(int N) { return (N + CSORT_CHUNK - 1) / CSORT_CHUNK; }
+
+hipError_t launch_perm_sort(const uint8_t* keys, int32_t* perm, int32_t* counts, int H, int N, hipStream_t s) {
   if (H == 0 || N == 0) return hipSuccess;
-  hipLaunchKernelGGL(perm_sort_kernel, dim3(H), dim3(SORT_NT), 0, s, keys, perm, N);
+  const int nch = sort_chunks(N);
+  hipLaunchKernelGGL(sort_hist_kernel, dim3((unsigned)nch, (unsigned)H), dim3(CSORT_NT), 0, s, keys, counts, N, nch);
+  hipError_t e = launched(s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sort_scan_kernel, dim3((unsigned)H), dim3(256), 0, s, counts, nch);
+  if ((e = launched(s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(sort_scatter_kernel, dim3((unsigned)nch, (unsigned)H), dim3(CSORT_NT), 0, s, keys, counts, perm,
+                     N, nch);
   return launched(s);
 }
 

@@ -1228,8 +1228,17 @@ __global__ __launch_bounds__(256) void v_to_f16_kernel(const uint4* __restrict__
                                                        long long per8, uint32_t* __restrict__ hmax) {
   const size_t base = (size_t)blockIdx.y * per8;
   uint32_t amax = 0;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < per8; i += (long long)gridDim.x * blockDim.x)
-    out[base + i] = v_f16_chunk(v[base + i], 0, &amax);
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  // four 16-byte loads in flight per thread, then their conversions
+  for (; i + 3 * stride < per8; i += 4 * stride) {
+    uint4 a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = v[base + i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) out[base + i + u * stride] = v_f16_chunk(a[u], 0, &amax);
+  }
+  for (; i < per8; i += stride) out[base + i] = v_f16_chunk(v[base + i], 0, &amax);
   // one atomic per workgroup: the wave maxima meet in LDS first
   __shared__ uint32_t wmax[4];
 #pragma unroll

@@ -154,16 +154,17 @@ std::vector<uint8_t> hash_tables(const float* proj, int d) {
 }
 
 struct WsLayout {
-  uint64_t off_keys, off_undecided, off_sortcnt, off_proj, off_mean, off_vscale, off_colsum, per_head_colsum, per_head_block, per_head_lse,
-      per_head_odense, per_head_v16, fixed;
+  uint64_t off_keys, off_undecided, off_sortcnt, off_proj, off_mean, off_vscale, off_colsum, per_head_colsum,
+      per_head_block, per_head_lse, per_head_odense, per_head_v16, fixed;
   uint64_t per_head() const {
     return per_head_colsum + per_head_block + per_head_lse + per_head_odense + per_head_v16;
   }
 };
 
-// keys | undecided key bits | sort counts [H][256][chunks] | projections | query means | V's per-head magnitude and float16 scale [2][H] | key scores [hc][ng][ldc] |
-// block scores [hc][ng][ldb] | row lse [hc][N] | float32 dense output [hc][N][d] (bf16 residual only) |
-// V rounded to float16 [hc][N][d] (bf16 problems)
+// keys | undecided key bits | sort counts [H][256][chunks] | projections | query means |
+// V's per-head magnitude and float16 scale [2][H] | key scores [hc][ng][ldc] | block scores [hc][ng][ldb] |
+// row lse [hc][N] | float32 dense output [hc][N][d] (bf16 residual only) | V rounded to float16 [hc][N][d]
+// (bf16 problems)
 WsLayout ws_layout(const mcs_attn_desc* d, int32_t G, bool bf16_residual) {
   const uint64_t H = (uint64_t)d->num_heads, N = (uint64_t)d->seq_len;
   const uint64_t ng = (N + G - 1) / G;

@@ -236,7 +236,11 @@ mcs_status mcs_meta_layout_ex(const mcs_attn_desc* desc, int32_t group_size, con
  * (float32 [heads_per_chunk][N]) that the dense pass hands to the key-score
  * pass, and for bf16 problems the chunk's V rounded to float16
  * ([heads_per_chunk][N][d], two bytes each, and two words per head) for the
- * selection's P.V products.
+ * selection's P.V products.  A fixed part holds the grouping's scratch: one
+ * key byte and one byte of undecided key bits per token (the hash decides
+ * most bits in float32 and recomputes the rest in float64), the stable
+ * sort's per-chunk key counts (1 KB per head per 4096 tokens), and the
+ * projection tables.
  */
 size_t mcs_select_workspace_bytes(const mcs_attn_desc* desc, int32_t group_size, int32_t heads_per_chunk);
 

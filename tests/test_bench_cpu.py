@@ -112,3 +112,12 @@ def test_trace_summary_tables(tmp_path):
     text = out.read_text()
     assert "| `void mcs::attn_bf16_kernel<128, 2, 2, 32>(mcs::AttnArgs)` | 10 | 9500.0 | 950.0 | 42.50 |" in text
     assert "| 120 | 0 | 112 | 32768 | 1198080 | 128 |" in text and "command: `CMD`" in text
+
+
+def test_joint_workload_description():
+    """Workload 6 names its text tokens and its full sequence length."""
+    b = _bench()
+    from mcs_inputs import workload
+    w = workload(6)
+    text = b.describe(w, w.keeps())
+    assert "16x30x52 + 226 text" in text and "N=25186" in text and "k=2496" in text
